@@ -1,0 +1,244 @@
+"""MI355X (gfx950) DSV dynamic block-sparse attention.
+
+A thin Python binding over the C ABI of ``libdsv.so`` (declared in
+``include/dsv.h``).  It only marshals arguments: torch tensors provide device
+memory and the current HIP stream; every step of the computation runs in the
+library's HIP kernels.  There is no fallback: if the library is missing, or the
+tensors are not on a GPU, the calls raise.
+
+Entry points (same names as the C ABI):
+  predict(q, k, wq, wk, ...)          -> block_scores [B, H, N/Bq, N/Bk] float32
+  select_topk(block_scores, topk)     -> block_idx    [B, H, N/Bq, k]    int32
+  sparse_attn_fwd(q, k, v, idx, ...)  -> (o, lse)
+  sparse_attn_bwd(q, k, v, o, do, lse, idx, ...) -> (dq, dk, dv)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsv.so")
+
+DSV_F32, DSV_BF16 = 0, 1
+STATUS = {0: "DSV_OK", 1: "DSV_ERR_INVALID_ARGUMENT", 2: "DSV_ERR_UNSUPPORTED", 3: "DSV_ERR_WORKSPACE_TOO_SMALL",
+          4: "DSV_ERR_HIP"}
+
+EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_select_topk", "dsv_sparse_attn_fwd_workspace_size",
+            "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd_workspace_size", "dsv_sparse_attn_bwd", "dsv_status_string",
+            "dsv_last_error", "dsv_version")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``dsv_problem`` in include/dsv.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float), ("pred_scale", ctypes.c_float)]
+
+
+class DSVError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdsv.so (once) and declare the C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m dynamic_sparse_attention_dsv_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, V, S = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "dsv_predict_workspace_size": (S, [P]),
+        "dsv_predict": (ctypes.c_int, [P, V, V, V, V, V, S, V, V]),
+        "dsv_select_topk": (ctypes.c_int, [P, V, V, V]),
+        "dsv_sparse_attn_fwd_workspace_size": (S, [P]),
+        "dsv_sparse_attn_fwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, S, V]),
+        "dsv_sparse_attn_bwd_workspace_size": (S, [P]),
+        "dsv_sparse_attn_bwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, V, V, V, S, V]),
+        "dsv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "dsv_last_error": (ctypes.c_char_p, []),
+        "dsv_version": (ctypes.c_int32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DSVError(status, where, load_library().dsv_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSV_BF16
+    if t.dtype == torch.float32:
+        return DSV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise RuntimeError("dsv kernels need GPU tensors (no CPU path exists)")
+    for t in ts:
+        if t.device != dev:
+            raise RuntimeError("all tensors must be on the same device")
+    return dev
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def make_problem(q: torch.Tensor, *, q_block: int, kv_block: int, topk: int = 1, rank: int = 0,
+                 sm_scale: Optional[float] = None, pred_scale: Optional[float] = None) -> Problem:
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    b, h, n, d = q.shape
+    return Problem(b, h, n, d, q_block, kv_block, topk, rank, _dtype_code(q),
+                   0.0 if sm_scale is None else float(sm_scale), 0.0 if pred_scale is None else float(pred_scale))
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _workspace(nbytes: int, dev: torch.device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def predict_workspace_size(prob: Problem) -> int:
+    return int(load_library().dsv_predict_workspace_size(ctypes.byref(prob)))
+
+
+def predict(q, k, wq, wk, *, q_block: int, kv_block: int = 64, pred_scale: Optional[float] = None,
+            workspace: Optional[torch.Tensor] = None, return_projections: bool = False):
+    """Predicted attention mass per (query block, KV block): [B, H, N/Bq, N/Bk] float32."""
+    lib = load_library()
+    dev = _dev(q, k, wq, wk)
+    _contig(q, k, wq, wk)
+    b, h, n, d = q.shape
+    if k.shape != q.shape or wq.shape != wk.shape or wq.shape[:2] != (h, d):
+        raise ValueError("shape mismatch: q, k [B,H,N,d]; wq, wk [H,d,r]")
+    if not (q.dtype == k.dtype == wq.dtype == wk.dtype):
+        raise TypeError("q, k, wq, wk must share one dtype")
+    r = wq.shape[2]
+    prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=1, rank=r, pred_scale=pred_scale)
+    ws = _workspace(int(lib.dsv_predict_workspace_size(ctypes.byref(prob))), dev, workspace)
+    scores = torch.empty((b, h, n // q_block, n // kv_block), dtype=torch.float32, device=dev)
+    _check(lib.dsv_predict(ctypes.byref(prob), _p(q), _p(k), _p(wq), _p(wk), _p(ws), ws.numel() * ws.element_size(),
+                           _p(scores), _stream(dev)), "dsv_predict")
+    if return_projections:
+        esz = q.element_size()
+        lr = b * h * n * r * esz
+        off_k = (lr + 255) // 256 * 256
+        flat = ws.view(torch.uint8)
+        qlr = flat[:lr].view(q.dtype).view(b, h, n, r)
+        klr = flat[off_k:off_k + lr].view(q.dtype).view(b, h, n, r)
+        return scores, qlr, klr
+    return scores
+
+
+def select_topk(scores: torch.Tensor, topk: int, *, q_block: int, kv_block: int = 64,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The top-k KV blocks of every query block, ascending, ties to the smaller index."""
+    lib = load_library()
+    dev = _dev(scores)
+    _contig(scores)
+    if scores.dtype != torch.float32 or scores.dim() != 4:
+        raise TypeError("scores must be float32 [B, H, N/Bq, N/Bk]")
+    b, h, nqb, nkb = scores.shape
+    n = nkb * kv_block
+    if nqb * q_block != n:
+        raise ValueError("scores shape does not match the block sizes")
+    prob = Problem(b, h, n, 64, q_block, kv_block, topk, 1, DSV_F32, 0.0, 0.0)
+    idx = out if out is not None else torch.empty((b, h, nqb, topk), dtype=torch.int32, device=dev)
+    _check(lib.dsv_select_topk(ctypes.byref(prob), _p(scores), _p(idx), _stream(dev)), "dsv_select_topk")
+    return idx
+
+
+def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_scale: Optional[float] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Softmax attention over the selected KV blocks only -> (o [B,H,N,d], lse [B,H,N] float32)."""
+    lib = load_library()
+    dev = _dev(q, k, v, block_idx)
+    _contig(q, k, v, block_idx)
+    if not (q.shape == k.shape == v.shape) or block_idx.dtype != torch.int32:
+        raise ValueError("q, k, v must share a shape; block_idx must be int32")
+    b, h, n, d = q.shape
+    prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1], sm_scale=sm_scale)
+    if tuple(block_idx.shape) != (b, h, n // q_block, prob.topk):
+        raise ValueError("block_idx must be [B, H, N/Bq, k]")
+    ws = _workspace(int(lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(prob))), dev, workspace)
+    o = torch.empty_like(q)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dsv_sparse_attn_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(block_idx), _p(o), _p(lse), _p(ws),
+                                   nbytes, _stream(dev)), "dsv_sparse_attn_fwd")
+    return o, lse
+
+
+def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block: int = 64,
+                    sm_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of the sparse attention."""
+    lib = load_library()
+    dev = _dev(q, k, v, o, dout, lse, block_idx)
+    _contig(q, k, v, o, dout, lse, block_idx)
+    b, h, n, d = q.shape
+    prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1], sm_scale=sm_scale)
+    ws = _workspace(int(lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(prob))), dev, workspace)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib.dsv_sparse_attn_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(o), _p(dout), _p(lse), _p(block_idx),
+                                   _p(dq), _p(dk), _p(dv), _p(ws), ws.numel() * ws.element_size(), _stream(dev)),
+           "dsv_sparse_attn_bwd")
+    return dq, dk, dv
+
+
+class DSVAttention(torch.autograd.Function):
+    """predict -> select -> sparse forward; the backward is the sparse backward.
+
+    No gradient flows to the predictor weights or the selection.
+    """
+
+    @staticmethod
+    def forward(ctx, q, k, v, wq, wk, q_block: int, kv_block: int, topk: int, sm_scale=None, pred_scale=None):
+        scores = predict(q, k, wq, wk, q_block=q_block, kv_block=kv_block, pred_scale=pred_scale)
+        idx = select_topk(scores, topk, q_block=q_block, kv_block=kv_block)
+        o, lse = sparse_attn_fwd(q, k, v, idx, q_block=q_block, kv_block=kv_block, sm_scale=sm_scale)
+        ctx.save_for_backward(q, k, v, o, lse, idx)
+        ctx.cfg = (q_block, kv_block, sm_scale)
+        ctx.mark_non_differentiable(idx)
+        return o, idx
+
+    @staticmethod
+    def backward(ctx, do, _didx):
+        q, k, v, o, lse, idx = ctx.saved_tensors
+        qb, kb, sm = ctx.cfg
+        dq, dk, dv = sparse_attn_bwd(q, k, v, o, do.contiguous(), lse, idx, q_block=qb, kv_block=kb, sm_scale=sm)
+        return dq, dk, dv, None, None, None, None, None, None, None

@@ -1,0 +1,619 @@
+// Block-sparse attention backward, plus the small helper kernels of the path
+// (layout transposes, the D = rowsum(dO o O) preprocess, and the transpose of
+// the block lists from "query block -> KV blocks" to "KV block -> query blocks").
+//
+// Method: the DSV pages ("DSV: Exploiting Dynamic Sparsity to Accelerate
+// Large-Scale Video DiT Training", gist.science/de technical summary §2.A,
+// stage 2, and gist.science/es §2.A, fase 2) train the video DiT with the
+// sparse attention, so its gradients are needed.  For every selected (qb, kb)
+// pair, with P = exp(S - lse) the forward's probabilities:
+//   dV_kb += P^T dO_qb,  dP = dO_qb V_kb^T,  dS = P o (dP - D),  D = rowsum(dO o O),
+//   dK_kb += sm_scale dS^T Q_qb,  dQ_qb += sm_scale dS K_kb.
+//
+// gfx950 design (bf16):
+//  * dK/dV: one workgroup per KV block walks the list of query blocks that
+//    selected it (the transposed lists), 32 query rows at a time, with dK and dV
+//    accumulated in registers -- no atomics, deterministic;
+//  * dQ: one workgroup per query block walks its own k blocks (recomputing P and
+//    dP), accumulating dQ in registers -- again no atomics;
+//  * every GEMM is a v_mfma 32x32x16 bf16 whose operands come from LDS tiles in
+//    the layout the operand needs; operands that contract over the query (or
+//    key) index read transposed copies of Q, dO and K made once per call.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace dsv {
+
+// ---------------------------------------------------------------- transpose [BH, N, D] -> [BH, D, N]
+
+template <int D>
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
+                                                             uint16_t* __restrict__ out, int n) {
+  constexpr int TS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t t[64 * TS];
+  const int bh = blockIdx.y, r0 = blockIdx.x * 64;
+  const uint16_t* src = in + ((size_t)bh * n + r0) * D;
+  for (int ch = threadIdx.x; ch < 64 * D / 8; ch += 256) {
+    const int row = ch / (D / 8), c8 = ch % (D / 8);
+    st16(&t[row * TS + c8 * 8], ld16(src + (size_t)row * D + c8 * 8));
+  }
+  __syncthreads();
+  uint16_t* dst = out + (size_t)bh * D * n + r0;
+  for (int ch = threadIdx.x; ch < D * 8; ch += 256) {
+    const int d = ch / 8, c8 = ch % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)t[(c8 * 8 + 2 * e) * TS + d] | ((uint32_t)t[(c8 * 8 + 2 * e + 1) * TS + d] << 16);
+    st16(dst + (size_t)d * n + c8 * 8, u32x4{w[0], w[1], w[2], w[3]});
+  }
+}
+
+// ---------------------------------------------------------------- D = rowsum(dO o O), lse2 = lse * log2(e)
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(const uint16_t* __restrict__ o,
+                                                           const uint16_t* __restrict__ dout,
+                                                           const float* __restrict__ lse, float* __restrict__ dvec,
+                                                           float* __restrict__ lse2, int rows) {
+  constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int row = t / LPR, c = t % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = ld16(o + (size_t)row * D + c * 8), b = ld16(dout + (size_t)row * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
+      acc = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && c == 0) {
+    dvec[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
+}
+
+__global__ void bwd_pre_f32_kernel(const float* __restrict__ o, const float* __restrict__ dout,
+                                   float* __restrict__ dvec, int rows, int d) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  float acc = 0.f;
+  for (int c = 0; c < d; ++c) acc = fmaf(o[(size_t)row * d + c], dout[(size_t)row * d + c], acc);
+  dvec[row] = acc;
+}
+
+// ---------------------------------------------------------------- block lists: CSR (per query block) -> CSC
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void csc_mark_kernel(const int32_t* __restrict__ idx, uint32_t* __restrict__ bitmap, int nqb, int nkb,
+                                int topk, int words, size_t total) {
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const size_t row = t / topk;  // bh * nqb + qb
+  const int qb = (int)(row % nqb);
+  const size_t bh = row / nqb;
+  const int kb = idx[t];
+  if ((unsigned)kb >= (unsigned)nkb) return;  // out-of-range index: ignored
+  atomicOr(&bitmap[(bh * nkb + kb) * words + qb / 32], 1u << (qb % 32));
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// one wave per (bh, kb): number of query blocks that selected kb
+__global__ __launch_bounds__(256) void csc_count_kernel(const uint32_t* __restrict__ bitmap,
+                                                        int32_t* __restrict__ counts, int cols, int words) {
+  const int col = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (col >= cols) return;
+  const int lane = threadIdx.x & 63;
+  int c = 0;
+  for (int w = lane; w < words; w += 64) c += __popc(bitmap[(size_t)col * words + w]);
+  c = wave_sum_i(c);
+  if (lane == 0) counts[col] = c;
+}
+
+// one workgroup of 1024 threads per bh: exclusive scan of counts[nkb] -> col_ptr[nkb + 1]
+__global__ __launch_bounds__(1024) void csc_scan_kernel(const int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ col_ptr, int nkb) {
+  __shared__ int32_t part[1024];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int per = (nkb + 1023) / 1024;
+  const int32_t* c = counts + (size_t)bh * nkb;
+  int32_t* cp = col_ptr + (size_t)bh * (nkb + 1);
+  int s = 0;
+  for (int i = 0; i < per; ++i) {
+    const int j = tid * per + i;
+    if (j < nkb) s += c[j];
+  }
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;  // exclusive prefix of this thread's segment
+  for (int i = 0; i < per; ++i) {
+    const int j = tid * per + i;
+    if (j < nkb) {
+      cp[j] = run;
+      run += c[j];
+    }
+  }
+  if (tid == 1023) cp[nkb] = part[1023];
+}
+
+// one wave per (bh, kb): write the query blocks that selected kb, ascending
+__global__ __launch_bounds__(256) void csc_emit_kernel(const uint32_t* __restrict__ bitmap,
+                                                       const int32_t* __restrict__ col_ptr,
+                                                       int32_t* __restrict__ rows, int cols, int nkb, int words,
+                                                       int nnz_per_bh) {
+  const int col = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (col >= cols) return;
+  const int lane = threadIdx.x & 63;
+  const int bh = col / nkb, kb = col % nkb;
+  int32_t* out = rows + (size_t)bh * nnz_per_bh + col_ptr[(size_t)bh * (nkb + 1) + kb];
+  int base = 0;
+  for (int w0 = 0; w0 < words; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t bits = w < words ? bitmap[(size_t)col * words + w] : 0u;
+    const int pc = __popc(bits);
+    // exclusive prefix of pc over lanes
+    int incl = pc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    int pos = base + incl - pc;
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      out[pos++] = w * 32 + b;
+      bits &= bits - 1;
+    }
+    base += __shfl(incl, 63);
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV (bf16, MFMA)
+
+template <int D, int BQ>
+__global__ __launch_bounds__(128) void attn_bwd_dkdv_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ dot,
+    const float* __restrict__ lse2, const float* __restrict__ dvec, const int32_t* __restrict__ col_ptr,
+    const int32_t* __restrict__ rows, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int n, int nnz_per_bh,
+    int nwg, float c /* sm_scale*log2e */, float sm_scale) {
+  constexpr int RS = D + 8;   // row-major chunk tiles [32][D]
+  constexpr int TS = 32 + 8;  // transposed chunk tiles [D][32]
+  constexpr int RCH = 32 * D / 8, TCH = D * 4;  // 16-byte chunks per tile
+  constexpr int CH = 2 * (RCH + TCH) / 128;
+  constexpr int SUBS = BQ / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[2][32 * RS];  // dO rows
+  __shared__ __attribute__((aligned(16))) uint16_t Qts[2][D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ots[2][D * TS];  // dO^T
+  __shared__ __attribute__((aligned(16))) float Ls[2][32];
+  __shared__ __attribute__((aligned(16))) float Dsh[2][32];
+
+  const int nkb = n / 64;
+  const int id = xcd_remap(blockIdx.x, nwg);
+  const int bh = id / nkb, kb = id % nkb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, c32 = lane & 31;
+  const size_t head = (size_t)bh * n * D;
+  const int key = kb * 64 + wave * 32 + c32;  // this lane's key (column of S)
+
+  const int32_t* cp = col_ptr + (size_t)bh * (nkb + 1);
+  const int start = cp[kb], cnt = cp[kb + 1] - start;
+  const int32_t* list = rows + (size_t)bh * nnz_per_bh + start;
+
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) { dka[dt] = f32x16{}; dva[dt] = f32x16{}; }
+
+  if (cnt > 0) {
+    // K^T and V^T as B operands: lane holds its key, 8 consecutive d per chunk
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      kf[dc] = as_bf16x8(ld16(k + head + (size_t)key * D + dc * 16 + g * 8));
+      vf[dc] = as_bf16x8(ld16(v + head + (size_t)key * D + dc * 16 + g * 8));
+    }
+    const int nch = cnt * SUBS;
+    auto q0_of = [&](int j) { return list[j / SUBS] * BQ + (j % SUBS) * 32; };
+    auto gsrc = [&](int q0, int ch) -> const uint16_t* {
+      const int tsel = ch / (RCH + TCH) ;  // 0: Q family, 1: dO family
+      int r = ch % (RCH + TCH);
+      if (r < RCH) return (tsel ? dout : q) + head + (size_t)(q0 + r / (D / 8)) * D + (r % (D / 8)) * 8;
+      r -= RCH;
+      return (tsel ? dot : qt) + head + (size_t)(r / 4) * n + q0 + (r % 4) * 8;
+    };
+    auto ldst = [&](int buf, int ch) -> uint16_t* {
+      const int tsel = ch / (RCH + TCH);
+      int r = ch % (RCH + TCH);
+      if (r < RCH) return &(tsel ? Os : Qs)[buf][(r / (D / 8)) * RS + (r % (D / 8)) * 8];
+      r -= RCH;
+      return &(tsel ? Ots : Qts)[buf][(r / 4) * TS + (r % 4) * 8];
+    };
+    u32x4 stage[CH];
+    u32x4 small = {};
+    auto load_small = [&](int q0) {  // threads 0..15: lse2 (8 chunks) and D (8 chunks)
+      if (threadIdx.x < 16) {
+        const float* s = (threadIdx.x < 8 ? lse2 : dvec) + (size_t)bh * n + q0 + (threadIdx.x % 8) * 4;
+        small = ld16(s);
+      }
+    };
+    auto store_small = [&](int buf) {
+      if (threadIdx.x < 16) st16(&(threadIdx.x < 8 ? Ls : Dsh)[buf][(threadIdx.x % 8) * 4], small);
+    };
+    {
+      const int q0 = q0_of(0);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(q0, threadIdx.x + i * 128));
+      load_small(q0);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) st16(ldst(0, threadIdx.x + i * 128), stage[i]);
+      store_small(0);
+    }
+    __syncthreads();
+    const int arow = sigma(c32);
+    for (int j = 0; j < nch; ++j) {
+      const int buf = j & 1;
+      if (j + 1 < nch) {
+        const int q0 = q0_of(j + 1);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(q0, threadIdx.x + i * 128));
+        load_small(q0);
+      }
+      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys (A rows in sigma order)
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const uint16_t* qa = &Qs[buf][arow * RS + g * 8];
+      const uint16_t* oa = &Os[buf][arow * RS + g * 8];
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) {
+        s = mfma32(as_bf16x8(ld16(qa + dc * 16)), kf[dc], s);
+        dp = mfma32(as_bf16x8(ld16(oa + dc * 16)), vf[dc], dp);
+      }
+      // register v holds query (v/8)*16 + g*8 + v%8 of the chunk
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int qi = (vv >> 3) * 16 + g * 8 + (vv & 7);
+        const float p = fast_exp2(fmaf(s[vv], c, -Ls[buf][qi]));
+        s[vv] = p;
+        dp[vv] = p * (dp[vv] - Dsh[buf][qi]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int b0 = cc * 8;
+        const bf16x8 pa = cvt8(s[b0], s[b0 + 1], s[b0 + 2], s[b0 + 3], s[b0 + 4], s[b0 + 5], s[b0 + 6], s[b0 + 7]);
+        const bf16x8 da = cvt8(dp[b0], dp[b0 + 1], dp[b0 + 2], dp[b0 + 3], dp[b0 + 4], dp[b0 + 5], dp[b0 + 6],
+                               dp[b0 + 7]);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          dva[dt] = mfma32(pa, as_bf16x8(ld16(&Ots[buf][(dt * 32 + c32) * TS + cc * 16 + g * 8])), dva[dt]);
+          dka[dt] = mfma32(da, as_bf16x8(ld16(&Qts[buf][(dt * 32 + c32) * TS + cc * 16 + g * 8])), dka[dt]);
+        }
+      }
+      if (j + 1 < nch) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) st16(ldst(buf ^ 1, threadIdx.x + i * 128), stage[i]);
+        store_small(buf ^ 1);
+      }
+      __syncthreads();
+    }
+  }
+  // D layout of dK/dV tiles: lane holds d = dt*32 + c32; register v holds key (v/4)*8 + g*4 + v%4
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) {
+      const int kr = kb * 64 + wave * 32 + (vv >> 2) * 8 + g * 4 + (vv & 3);
+      const size_t off = head + (size_t)kr * D + dt * 32 + c32;
+      dk[off] = f32_to_bf16(dka[dt][vv] * sm_scale);
+      dv[off] = f32_to_bf16(dva[dt][vv]);
+    }
+}
+
+// ---------------------------------------------------------------- dQ (bf16, MFMA)
+
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2) void attn_bwd_dq_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kt,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ dvec, const int32_t* __restrict__ idx, uint16_t* __restrict__ dq, int n, int topk,
+    int nwg, float c, float sm_scale) {
+  constexpr int THREADS = BQ * 2;
+  constexpr int RS = D + 8, TS = 64 + 8;
+  constexpr int RCH = 64 * D / 8, TCH = D * 8;
+  constexpr int CH = (2 * RCH + TCH) / THREADS;
+  static_assert((2 * RCH + TCH) % THREADS == 0, "staging must divide evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Kts[2][D * TS];
+
+  const int nqb = n / BQ;
+  const int id = xcd_remap(blockIdx.x, nwg);
+  const int bh = id / nqb, qb = id % nqb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, c32 = lane & 31;
+  const size_t head = (size_t)bh * n * D;
+  const int32_t* blocks = idx + ((size_t)bh * nqb + qb) * topk;
+  const int qrow = qb * BQ + wave * 32 + c32;
+  const int nkb = n / 64;
+  auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };  // clamp out-of-range indices
+
+  auto gsrc = [&](int blk, int ch) -> const uint16_t* {
+    if (ch < 2 * RCH) {
+      const int r = ch % RCH;
+      return (ch < RCH ? k : v) + head + (size_t)(blk * 64 + r / (D / 8)) * D + (r % (D / 8)) * 8;
+    }
+    const int r = ch - 2 * RCH;
+    return kt + head + (size_t)(r / 8) * n + blk * 64 + (r % 8) * 8;
+  };
+  auto ldst = [&](int buf, int ch) -> uint16_t* {
+    if (ch < 2 * RCH) {
+      const int r = ch % RCH;
+      return &(ch < RCH ? Ks : Vs)[buf][(r / (D / 8)) * RS + (r % (D / 8)) * 8];
+    }
+    const int r = ch - 2 * RCH;
+    return &Kts[buf][(r / 8) * TS + (r % 8) * 8];
+  };
+
+  bf16x8 qf[D / 16], of[D / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) {
+    qf[dc] = as_bf16x8(ld16(q + head + (size_t)qrow * D + dc * 16 + g * 8));
+    of[dc] = as_bf16x8(ld16(dout + head + (size_t)qrow * D + dc * 16 + g * 8));
+  }
+  const float my_lse2 = lse2[(size_t)bh * n + qrow];
+  const float my_d = dvec[(size_t)bh * n + qrow];
+
+  u32x4 stage[CH];
+  {
+    const int blk = blk_at(0);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(blk, threadIdx.x + i * THREADS));
+#pragma unroll
+    for (int i = 0; i < CH; ++i) st16(ldst(0, threadIdx.x + i * THREADS), stage[i]);
+  }
+  __syncthreads();
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  const int arow = sigma(c32);
+  for (int j = 0; j < topk; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < topk) {
+      const int blk = blk_at(j + 1);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(blk, threadIdx.x + i * THREADS));
+    }
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x16{};
+      dp[t] = f32x16{};
+      const uint16_t* ka = &Ks[buf][(t * 32 + arow) * RS + g * 8];
+      const uint16_t* va = &Vs[buf][(t * 32 + arow) * RS + g * 8];
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) {
+        s[t] = mfma32(as_bf16x8(ld16(ka + dc * 16)), qf[dc], s[t]);
+        dp[t] = mfma32(as_bf16x8(ld16(va + dc * 16)), of[dc], dp[t]);
+      }
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const float p = fast_exp2(fmaf(s[t][vv], c, -my_lse2));
+        dp[t][vv] = p * (dp[t][vv] - my_d);
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const f32x16& st = dp[cc >> 1];
+      const int b0 = (cc & 1) * 8;
+      const bf16x8 db = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
+                             st[b0 + 7]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        acc[dt] = mfma32(as_bf16x8(ld16(&Kts[buf][(dt * 32 + c32) * TS + cc * 16 + g * 8])), db, acc[dt]);
+    }
+    if (j + 1 < topk) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) st16(ldst(buf ^ 1, threadIdx.x + i * THREADS), stage[i]);
+    }
+    __syncthreads();
+  }
+  uint16_t* out = dq + head + (size_t)qrow * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      const int d0 = dt * 32 + vq * 8 + g * 4;
+      u32x2 pk = {pack_bf16x2(acc[dt][vq * 4] * sm_scale, acc[dt][vq * 4 + 1] * sm_scale),
+                  pack_bf16x2(acc[dt][vq * 4 + 2] * sm_scale, acc[dt][vq * 4 + 3] * sm_scale)};
+      *reinterpret_cast<u32x2*>(out + d0) = pk;
+    }
+}
+
+// ---------------------------------------------------------------- f32 path (plain VALU)
+
+__global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                       const float* __restrict__ v, const float* __restrict__ dout,
+                                       const float* __restrict__ lse, const float* __restrict__ dvec,
+                                       const int32_t* __restrict__ idx, float* __restrict__ dq, int n, int d, int bq,
+                                       int bk, int topk, float scale) {
+  // one thread per query row and output column c: grid (ceil(n*d/256), BH)
+  const int bh = blockIdx.y;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (size_t)n * d) return;
+  const int i = (int)(t / d), col = (int)(t % d);
+  const size_t head = (size_t)bh * n * d;
+  const float* qi = q + head + (size_t)i * d;
+  const float* gi = dout + head + (size_t)i * d;
+  const float li = lse[(size_t)bh * n + i], di = dvec[(size_t)bh * n + i];
+  const int32_t* blocks = idx + ((size_t)bh * (n / bq) + i / bq) * topk;
+  float acc = 0.f;
+  for (int jb = 0; jb < topk; ++jb) {
+    const int kb = min(max(blocks[jb], 0), n / bk - 1);  // clamp out-of-range indices
+    for (int j = kb * bk; j < (kb + 1) * bk; ++j) {
+      const float* kj = k + head + (size_t)j * d;
+      const float* vj = v + head + (size_t)j * d;
+      float s = 0.f, dp = 0.f;
+      for (int cc = 0; cc < d; ++cc) {
+        s = fmaf(qi[cc], kj[cc], s);
+        dp = fmaf(gi[cc], vj[cc], dp);
+      }
+      const float p = expf(s * scale - li);
+      acc = fmaf(p * (dp - di), kj[col], acc);
+    }
+  }
+  dq[head + (size_t)i * d + col] = acc * scale;
+}
+
+__global__ void attn_bwd_dkdv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                         const float* __restrict__ v, const float* __restrict__ dout,
+                                         const float* __restrict__ lse, const float* __restrict__ dvec,
+                                         const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ rows,
+                                         float* __restrict__ dk, float* __restrict__ dv, int n, int d, int bq, int bk,
+                                         int nnz_per_bh, float scale) {
+  // one thread per key row and output column: grid (ceil(n*d/256), BH)
+  const int bh = blockIdx.y;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (size_t)n * d) return;
+  const int j = (int)(t / d), col = (int)(t % d);
+  const int nkb = n / bk, kb = j / bk;
+  const size_t head = (size_t)bh * n * d;
+  const float* kj = k + head + (size_t)j * d;
+  const float* vj = v + head + (size_t)j * d;
+  const int32_t* cp = col_ptr + (size_t)bh * (nkb + 1);
+  const int32_t* list = rows + (size_t)bh * nnz_per_bh;
+  float ak = 0.f, av = 0.f;
+  for (int e = cp[kb]; e < cp[kb + 1]; ++e) {
+    const int qb = list[e];
+    for (int i = qb * bq; i < (qb + 1) * bq; ++i) {
+      const float* qi = q + head + (size_t)i * d;
+      const float* gi = dout + head + (size_t)i * d;
+      float s = 0.f, dp = 0.f;
+      for (int cc = 0; cc < d; ++cc) {
+        s = fmaf(qi[cc], kj[cc], s);
+        dp = fmaf(gi[cc], vj[cc], dp);
+      }
+      const float p = expf(s * scale - lse[(size_t)bh * n + i]);
+      av = fmaf(p, gi[col], av);
+      ak = fmaf(p * (dp - dvec[(size_t)bh * n + i]), qi[col], ak);
+    }
+  }
+  dk[head + (size_t)j * d + col] = ak * scale;
+  dv[head + (size_t)j * d + col] = av;
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_transpose_bf16(const uint16_t* in, uint16_t* out, int bh, int n, int d, hipStream_t st) {
+  dim3 grid(n / 64, bh);
+  if (d == 64) hipLaunchKernelGGL(transpose_bf16_kernel<64>, grid, dim3(256), 0, st, in, out, n);
+  else if (d == 128) hipLaunchKernelGGL(transpose_bf16_kernel<128>, grid, dim3(256), 0, st, in, out, n);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* dout, const float* lse, float* dvec, float* lse2,
+                               int rows, int d, hipStream_t st) {
+  const int lanes = rows * (d / 8);
+  dim3 grid((lanes + 255) / 256);
+  if (d == 64) hipLaunchKernelGGL(bwd_pre_bf16_kernel<64>, grid, dim3(256), 0, st, o, dout, lse, dvec, lse2, rows);
+  else if (d == 128)
+    hipLaunchKernelGGL(bwd_pre_bf16_kernel<128>, grid, dim3(256), 0, st, o, dout, lse, dvec, lse2, rows);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre_f32(const float* o, const float* dout, float* dvec, int rows, int d, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_pre_f32_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, o, dout, dvec, rows, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_csc(const int32_t* idx, uint32_t* bitmap, int32_t* counts, int32_t* col_ptr, int32_t* rows,
+                      int bh, int nqb, int nkb, int topk, hipStream_t st) {
+  const int words = (nqb + 31) / 32;
+  const size_t nbits = (size_t)bh * nkb * words;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<size_t>((nbits + 255) / 256, 65535)), dim3(256), 0,
+                     st, bitmap, nbits, 0u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t total = (size_t)bh * nqb * topk;
+  hipLaunchKernelGGL(csc_mark_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, idx, bitmap, nqb,
+                     nkb, topk, words, total);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int cols = bh * nkb;
+  hipLaunchKernelGGL(csc_count_kernel, dim3((cols + 3) / 4), dim3(256), 0, st, bitmap, counts, cols, words);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(csc_scan_kernel, dim3(bh), dim3(1024), 0, st, counts, col_ptr, nkb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(csc_emit_kernel, dim3((cols + 3) / 4), dim3(256), 0, st, bitmap, col_ptr, rows, cols, nkb,
+                     words, nqb * topk);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* qt, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* dout, const uint16_t* dot, const float* lse2, const float* dvec,
+                                const int32_t* col_ptr, const int32_t* rows, uint16_t* dk, uint16_t* dv, int bh,
+                                int n, int d, int bq, int topk, float sm_scale, hipStream_t st) {
+  const int nwg = bh * (n / 64);
+  const int nnz = (n / bq) * topk;
+  const float c = sm_scale * kLog2e;
+#define DKDV(D_, BQ_)                                                                                      \
+  if (d == D_ && bq == BQ_) {                                                                              \
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(128), 0, st, q, qt, k, v, dout, \
+                       dot, lse2, dvec, col_ptr, rows, dk, dv, n, nnz, nwg, c, sm_scale);                  \
+    return hipGetLastError();                                                                              \
+  }
+  DKDV(64, 64) DKDV(64, 128) DKDV(128, 64) DKDV(128, 128)
+#undef DKDV
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* kt, const uint16_t* v,
+                              const uint16_t* dout, const float* lse2, const float* dvec, const int32_t* idx,
+                              uint16_t* dq, int bh, int n, int d, int bq, int topk, float sm_scale, hipStream_t st) {
+  const int nwg = bh * (n / bq);
+  const float c = sm_scale * kLog2e;
+#define DQ(D_, BQ_)                                                                                         \
+  if (d == D_ && bq == BQ_) {                                                                               \
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, kt, v, dout, \
+                       lse2, dvec, idx, dq, n, topk, nwg, c, sm_scale);                                     \
+    return hipGetLastError();                                                                               \
+  }
+  DQ(64, 64) DQ(64, 128) DQ(128, 64) DQ(128, 128)
+#undef DQ
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dout, const float* lse,
+                          const float* dvec, const int32_t* idx, const int32_t* col_ptr, const int32_t* rows,
+                          float* dq, float* dk, float* dv, int bh, int n, int d, int bq, int bk, int topk,
+                          float sm_scale, hipStream_t st) {
+  dim3 grid((unsigned)(((size_t)n * d + 255) / 256), bh);
+  hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, grid, dim3(256), 0, st, q, k, v, dout, lse, dvec, idx, dq, n, d, bq, bk,
+                     topk, sm_scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, grid, dim3(256), 0, st, q, k, v, dout, lse, dvec, col_ptr, rows, dk,
+                     dv, n, d, bq, bk, (n / bq) * topk, sm_scale);
+  return hipGetLastError();
+}
+
+}  // namespace dsv

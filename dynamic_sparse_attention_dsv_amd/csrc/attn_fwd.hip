@@ -1,0 +1,224 @@
+// Block-sparse attention forward.
+//
+// Method: the DSV pages ("DSV: Exploiting Dynamic Sparsity to Accelerate
+// Large-Scale Video DiT Training", gist.science/es technical summary §3 and
+// gist.science/de §2.A stage 2) run exact attention over the selected critical
+// KV only.  For query block qb with selected blocks J:
+//   O_i = softmax_J(sm_scale q_i K_J^T) V_J,  lse_i = log sum_{j in J} exp(sm_scale q_i.k_j).
+//
+// gfx950 design (bf16, d in {64,128}, Bq in {64,128}, Bk = 64):
+//  * one workgroup per (b, h, qb), Bq/32 waves, each wave owns 32 query rows;
+//    workgroup ids are remapped so that one XCD works on one head at a time;
+//  * Q stays in registers as the B operand of S^T = K Q^T (v_mfma 32x32x16);
+//  * each selected KV block is gathered into LDS (K row-major, V^T from a
+//    transposed copy of V) with double buffering: the next block's global loads
+//    are in flight while the current block is computed;
+//  * S^T's D layout puts one query per lane, so the online-softmax row max and
+//    row sum are lane-local plus one exchange with lane ^ 32; K rows are loaded
+//    in the sigma order so that P^T feeds O^T += V^T P^T directly from registers.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dsv {
+
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse, int n, int topk,
+    int nwg, float c /* sm_scale * log2(e) */) {
+  constexpr int THREADS = BQ * 2;  // (BQ / 32) waves of 64
+  constexpr int KS = D + 8;        // padded row (elements) of the K tile
+  constexpr int VS = 64 + 8;       // padded row of the V^T tile
+  constexpr int KCH = 64 * D / 8;  // 16-byte chunks of the K tile
+  constexpr int CH = (KCH + D * 8) / THREADS;
+  static_assert((KCH + D * 8) % THREADS == 0, "staging must divide evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VS];
+
+  const int nqb = n / BQ;
+  const int id = xcd_remap(blockIdx.x, nwg);
+  const int bh = id / nqb, qb = id % nqb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, c32 = lane & 31;
+  const size_t head = (size_t)bh * n * D;
+  const int32_t* blocks = idx + ((size_t)bh * nqb + qb) * topk;
+  const int nkb = n / 64;
+  // out-of-range block indices are clamped: wrong results, but no access outside the tensors
+  auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };
+
+  // staging helpers: chunk ch -> (global source, LDS destination)
+  auto gsrc = [&](int blk, int ch) -> const uint16_t* {
+    if (ch < KCH) return k + head + (size_t)(blk * 64 + ch / (D / 8)) * D + (ch % (D / 8)) * 8;
+    const int c2 = ch - KCH;
+    return vt + head + (size_t)(c2 / 8) * n + blk * 64 + (c2 % 8) * 8;
+  };
+  auto ldst = [&](int buf, int ch) -> uint16_t* {
+    if (ch < KCH) return &Ks[buf][(ch / (D / 8)) * KS + (ch % (D / 8)) * 8];
+    const int c2 = ch - KCH;
+    return &Vs[buf][(c2 / 8) * VS + (c2 % 8) * 8];
+  };
+
+  // Q^T as the B operand: lane holds its query row, 8 consecutive d per 16-wide chunk
+  const int qrow = qb * BQ + wave * 32 + c32;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) qf[dc] = as_bf16x8(ld16(q + head + (size_t)qrow * D + dc * 16 + g * 8));
+
+  u32x4 stage[CH];
+  {
+    const int blk = blk_at(0);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(blk, threadIdx.x + i * THREADS));
+#pragma unroll
+    for (int i = 0; i < CH; ++i) st16(ldst(0, threadIdx.x + i * THREADS), stage[i]);
+  }
+  __syncthreads();
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int arow = sigma(c32);
+
+  for (int j = 0; j < topk; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < topk) {
+      const int blk = blk_at(j + 1);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(blk, threadIdx.x + i * THREADS));
+    }
+    // S^T = K Q^T: two 32-key tiles, rows loaded in sigma order
+    f32x16 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x16{};
+      const uint16_t* kr = &Ks[buf][(t * 32 + arow) * KS + g * 8];
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) s[t] = mfma32(as_bf16x8(ld16(kr + dc * 16)), qf[dc], s[t]);
+    }
+    // online softmax (log2 domain); lane owns one query, 32 of the block's 64 keys
+    float mx = s[0][0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[1][v]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s[t][v] = fast_exp2(fmaf(s[t][v], c, -m_new));
+        psum += s[t][v];
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    // O^T += V^T P^T: P^T chunk cc = registers (cc%2)*8.. of tile cc/2
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const f32x16& st = s[cc >> 1];
+      const int b0 = (cc & 1) * 8;
+      const bf16x8 pb = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
+                             st[b0 + 7]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        oacc[dt] = mfma32(as_bf16x8(ld16(&Vs[buf][(dt * 32 + c32) * VS + cc * 16 + g * 8])), pb, oacc[dt]);
+    }
+    if (j + 1 < topk) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) st16(ldst(buf ^ 1, threadIdx.x + i * THREADS), stage[i]);
+    }
+    __syncthreads();
+  }
+
+  const float l = l_run + xor32(l_run);
+  const float inv = 1.f / l;
+  uint16_t* orow = o + head + (size_t)qrow * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      const int d0 = dt * 32 + vq * 8 + g * 4;
+      u32x2 pk = {pack_bf16x2(oacc[dt][vq * 4] * inv, oacc[dt][vq * 4 + 1] * inv),
+                  pack_bf16x2(oacc[dt][vq * 4 + 2] * inv, oacc[dt][vq * 4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + d0) = pk;
+    }
+  if (g == 0) lse[(size_t)bh * n + qrow] = (m_run + fast_log2(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------- f32 path (plain VALU)
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                          const float* __restrict__ v,
+                                                          const int32_t* __restrict__ idx, float* __restrict__ o,
+                                                          float* __restrict__ lse, int n, int d, int bq, int bk,
+                                                          int topk, float scale) {
+  // one thread per query row; grid (ceil(n/64), BH)
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= n) return;
+  const size_t head = (size_t)bh * n * d;
+  const float* qi = q + head + (size_t)i * d;
+  float qv[D], acc[D];
+  for (int c = 0; c < d; ++c) { qv[c] = qi[c]; acc[c] = 0.f; }
+  const int32_t* blocks = idx + ((size_t)bh * (n / bq) + i / bq) * topk;
+  float m = -INFINITY, l = 0.f;
+  for (int jb = 0; jb < topk; ++jb) {
+    const int kb = min(max(blocks[jb], 0), n / bk - 1);  // clamp out-of-range indices
+    for (int j = kb * bk; j < (kb + 1) * bk; ++j) {
+      const float* kj = k + head + (size_t)j * d;
+      float s = 0.f;
+      for (int c = 0; c < d; ++c) s = fmaf(qv[c], kj[c], s);
+      s *= scale;
+      const float mn = fmaxf(m, s);
+      const float a = expf(m - mn), p = expf(s - mn);
+      l = l * a + p;
+      const float* vj = v + head + (size_t)j * d;
+      for (int c = 0; c < d; ++c) acc[c] = fmaf(p, vj[c], acc[c] * a);
+      m = mn;
+    }
+  }
+  float* oi = o + head + (size_t)i * d;
+  for (int c = 0; c < d; ++c) oi[c] = acc[c] / l;
+  lse[(size_t)bh * n + i] = m + logf(l);
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt, const int32_t* idx,
+                                uint16_t* o, float* lse, int bh, int n, int d, int bq, int topk, float sm_scale,
+                                hipStream_t st) {
+  const int nwg = bh * (n / bq);
+  const float c = sm_scale * kLog2e;
+#define FWD(D_, BQ_)                                                                                      \
+  if (d == D_ && bq == BQ_) {                                                                             \
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, vt, idx, o, \
+                       lse, n, topk, nwg, c);                                                             \
+    return hipGetLastError();                                                                             \
+  }
+  FWD(64, 64) FWD(64, 128) FWD(128, 64) FWD(128, 128)
+#undef FWD
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* idx, float* o,
+                               float* lse, int bh, int n, int d, int bq, int bk, int topk, float sm_scale,
+                               hipStream_t st) {
+  dim3 grid((n + 63) / 64, bh);
+#define FF(D_)                                                                                            \
+  if (d <= D_) {                                                                                          \
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D_>), grid, dim3(64), 0, st, q, k, v, idx, o, lse, n, d, bq, bk, \
+                       topk, sm_scale);                                                                   \
+    return hipGetLastError();                                                                             \
+  }
+  FF(32) FF(64) FF(128)
+#undef FF
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsv

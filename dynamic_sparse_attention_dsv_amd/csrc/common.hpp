@@ -1,0 +1,96 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels: bf16 conversion, MFMA
+// fragment types, wave-level exchange, and the problem description passed to
+// kernels.
+//
+// MFMA fragment conventions used throughout (verified on the device with an
+// in-bounds layout check against a host matmul):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds row (l % 32), 8 consecutive k starting at (l / 32) * 8
+//     B: lane l holds col (l % 32), 8 consecutive k starting at (l / 32) * 8
+//     D: lane l holds col (l % 32); register v holds row (v/4)*8 + (l/32)*4 + v%4
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] * B[32x16]
+//     A: lane l holds row (l % 16), 8 consecutive k starting at (l / 16) * 8
+//     B: lane l holds col (l % 16), same k
+//     D: lane l holds col (l % 16); register v holds row (l/16)*4 + v
+//
+// Row permutation "sigma" (swap bits 2 and 3 of a row index inside a 32-row
+// tile).  If the A operand's row r is loaded from source row sigma(r), then in
+// the 32x32 D layout lane group g = l/32, register v corresponds to source row
+//   (v / 8) * 16 + g * 8 + (v % 8),
+// which is exactly the k layout of a B (or A) operand: registers 0..7 of a lane
+// form the operand for source rows [0, 16), registers 8..15 for [16, 32).  This
+// lets a softmax tile computed by one MFMA feed the next MFMA straight from
+// registers, with no LDS round trip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bfloat16 bits, round to nearest even (NaN -> quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Eight floats -> one bf16 MFMA operand (hardware round-to-nearest-even).
+__device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                       float a6, float a7) {
+  f32x8 f = {a0, a1, a2, a3, a4, a5, a6, a7};
+  return __builtin_convertvector(f, bf16x8);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Value held by lane (l ^ 32).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// sigma: swap bits 2 and 3 of a row index (see the header comment).
+__device__ __forceinline__ int sigma(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Map a workgroup id so that consecutive logical ids run on the same XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8); with this
+// remap XCD x processes the contiguous logical range [x*per, (x+1)*per), so the
+// work sharing one head's K/V tiles shares that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  const int per = n / 8;
+  if (per == 0 || id >= per * 8) return id;
+  return (id % 8) * per + id / 8;
+}
+
+}  // namespace dsv

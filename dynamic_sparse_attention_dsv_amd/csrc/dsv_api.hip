@@ -1,0 +1,336 @@
+// C ABI of libdsv: argument validation, workspace carving and launch sequencing.
+// The declarations and the contract of every entry point are in include/dsv.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsv.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+dsv_status fail(dsv_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+constexpr size_t kWsAlign = 256;
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+struct Prob {
+  int b, h, n, d, bq, bk, k, r, dtype;
+  float sm, ps;
+  int bh() const { return b * h; }
+  int nqb() const { return n / bq; }
+  int nkb() const { return n / bk; }
+  size_t esize() const { return dtype == DSV_BF16 ? 2 : 4; }
+  size_t tensor_elems() const { return (size_t)b * h * n * d; }
+};
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Common checks; `need_rank` for the predictor, `need_k` for selection and attention.
+dsv_status to_prob(const dsv_problem* p, Prob& o, bool need_rank) {
+  if (!p) return fail(DSV_ERR_INVALID_ARGUMENT, "problem pointer is NULL");
+  o = Prob{p->batch, p->heads, p->seq_len, p->head_dim, p->q_block, p->kv_block, p->topk, p->rank, p->dtype,
+           p->sm_scale, p->pred_scale};
+  char buf[256];
+  if (o.b < 1 || o.h < 1 || o.n < 1 || o.d < 1 || o.bq < 1 || o.bk < 1) {
+    snprintf(buf, sizeof buf, "sizes must be positive (B=%d H=%d N=%d d=%d Bq=%d Bk=%d)", o.b, o.h, o.n, o.d, o.bq,
+             o.bk);
+    return fail(DSV_ERR_INVALID_ARGUMENT, buf);
+  }
+  if (o.n % o.bq || o.n % o.bk || o.bq % o.bk) {
+    snprintf(buf, sizeof buf, "N=%d must be a multiple of Bq=%d and Bk=%d, and Bq of Bk", o.n, o.bq, o.bk);
+    return fail(DSV_ERR_INVALID_ARGUMENT, buf);
+  }
+  if (o.k < 1 || o.k > o.nkb()) {
+    snprintf(buf, sizeof buf, "topk=%d out of range [1, N/Bk=%d]", o.k, o.nkb());
+    return fail(DSV_ERR_INVALID_ARGUMENT, buf);
+  }
+  if (o.dtype != DSV_F32 && o.dtype != DSV_BF16) return fail(DSV_ERR_INVALID_ARGUMENT, "dtype must be DSV_F32 or DSV_BF16");
+  if (need_rank && o.r < 1) return fail(DSV_ERR_INVALID_ARGUMENT, "rank must be positive");
+  if (!std::isfinite(o.sm) || !std::isfinite(o.ps)) return fail(DSV_ERR_INVALID_ARGUMENT, "scales must be finite");
+  if (o.sm <= 0.f) o.sm = 1.f / std::sqrt((float)o.d);
+  if (o.ps <= 0.f) o.ps = 1.f / std::sqrt((float)o.d);
+  if ((double)o.b * o.h * o.n * (o.d > o.r ? o.d : o.r) >= 2147483648.0 * 16)
+    return fail(DSV_ERR_UNSUPPORTED, "tensor too large");
+  if ((double)o.b * o.h * o.nqb() >= 2147483647.0 || (double)o.b * o.h * o.nkb() >= 2147483647.0)
+    return fail(DSV_ERR_UNSUPPORTED, "too many blocks");
+  if (o.nkb() > 4096) return fail(DSV_ERR_UNSUPPORTED, "N/Bk must be <= 4096");
+  return DSV_OK;
+}
+
+dsv_status check_bf16_attn(const Prob& o) {
+  if (o.dtype != DSV_BF16) return DSV_OK;
+  char buf[200];
+  if ((o.d != 64 && o.d != 128) || (o.bq != 64 && o.bq != 128) || o.bk != 64) {
+    snprintf(buf, sizeof buf, "bf16 instances need d in {64,128}, Bq in {64,128}, Bk = 64 (got d=%d Bq=%d Bk=%d)",
+             o.d, o.bq, o.bk);
+    return fail(DSV_ERR_UNSUPPORTED, buf);
+  }
+  return DSV_OK;
+}
+
+dsv_status check_f32_attn(const Prob& o) {
+  if (o.dtype == DSV_F32 && o.d > 128) return fail(DSV_ERR_UNSUPPORTED, "f32 instances need d <= 128");
+  return DSV_OK;
+}
+
+dsv_status check_ptr(const void* p, const char* name, size_t align = 16) {
+  if (!p) return fail(DSV_ERR_INVALID_ARGUMENT, std::string(name) + " is NULL");
+  if (!aligned(p, align))
+    return fail(DSV_ERR_INVALID_ARGUMENT, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  return DSV_OK;
+}
+
+dsv_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return DSV_OK;
+  return fail(DSV_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define TRY(x)                      \
+  do {                              \
+    dsv_status s_ = (x);            \
+    if (s_ != DSV_OK) return s_;    \
+  } while (0)
+#define TRY_HIP(x, where) TRY(hip_status((x), where))
+
+// ---------------------------------------------------------------- workspace layouts
+
+struct PredictWs {
+  size_t qlr, klr, scratch, lse, total;
+};
+PredictWs predict_ws(const Prob& o) {
+  PredictWs w{};
+  const size_t lr = align_up((size_t)o.bh() * o.n * o.r * o.esize());
+  w.qlr = 0;
+  w.klr = lr;
+  size_t off = 2 * lr;
+  if (o.dtype == DSV_BF16) {
+    w.scratch = off;
+    off += align_up(dsv::score_scratch_bytes(o.bh() * (o.n / 128), o.nkb()));
+  } else {
+    w.lse = off;
+    off += align_up((size_t)o.bh() * o.n * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+
+struct BwdWs {
+  size_t qt, dot, kt, dvec, lse2, bitmap, counts, col_ptr, rows, total;
+};
+BwdWs bwd_ws(const Prob& o) {
+  BwdWs w{};
+  size_t off = 0;
+  const size_t t = align_up(o.tensor_elems() * o.esize());
+  const size_t rowf = align_up((size_t)o.bh() * o.n * sizeof(float));
+  if (o.dtype == DSV_BF16) {
+    w.qt = off; off += t;
+    w.dot = off; off += t;
+    w.kt = off; off += t;
+    w.lse2 = off; off += rowf;
+  }
+  w.dvec = off; off += rowf;
+  const int words = (o.nqb() + 31) / 32;
+  w.bitmap = off; off += align_up((size_t)o.bh() * o.nkb() * words * 4);
+  w.counts = off; off += align_up((size_t)o.bh() * o.nkb() * 4);
+  w.col_ptr = off; off += align_up((size_t)o.bh() * (o.nkb() + 1) * 4);
+  w.rows = off; off += align_up((size_t)o.bh() * o.nqb() * o.k * 4);
+  w.total = off;
+  return w;
+}
+
+size_t fwd_ws_bytes(const Prob& o) { return o.dtype == DSV_BF16 ? align_up(o.tensor_elems() * 2) : 0; }
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsv_status_string(dsv_status s) {
+  switch (s) {
+    case DSV_OK: return "DSV_OK";
+    case DSV_ERR_INVALID_ARGUMENT: return "DSV_ERR_INVALID_ARGUMENT";
+    case DSV_ERR_UNSUPPORTED: return "DSV_ERR_UNSUPPORTED";
+    case DSV_ERR_WORKSPACE_TOO_SMALL: return "DSV_ERR_WORKSPACE_TOO_SMALL";
+    case DSV_ERR_HIP: return "DSV_ERR_HIP";
+  }
+  return "DSV_ERR_UNKNOWN";
+}
+
+const char* dsv_last_error(void) { return g_err.c_str(); }
+
+int32_t dsv_version(void) { return 100; }
+
+size_t dsv_predict_workspace_size(const dsv_problem* p) {
+  Prob o;
+  if (to_prob(p, o, true) != DSV_OK) return 0;
+  return predict_ws(o).total;
+}
+
+dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const void* wq, const void* wk,
+                       void* workspace, size_t workspace_bytes, float* block_scores, void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, true));
+  if (o.dtype == DSV_BF16) {
+    if ((o.d != 64 && o.d != 128) || (o.r != 16 && o.r != 32) || (o.bq != 64 && o.bq != 128) || o.bk != 64 ||
+        o.n % 128)
+      return fail(DSV_ERR_UNSUPPORTED, "bf16 predictor needs d in {64,128}, r in {16,32}, Bq in {64,128}, Bk = 64, N % 128 == 0");
+  } else if (o.r > 64) {
+    return fail(DSV_ERR_UNSUPPORTED, "f32 predictor needs r <= 64");
+  }
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(wq, "wq", o.dtype == DSV_BF16 ? 2 : 4));
+  TRY(check_ptr(wk, "wk", o.dtype == DSV_BF16 ? 2 : 4));
+  TRY(check_ptr(block_scores, "block_scores"));
+  TRY(check_ptr(workspace, "workspace", kWsAlign));
+  const PredictWs w = predict_ws(o);
+  if (workspace_bytes < w.total)
+    return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "predict workspace needs " + std::to_string(w.total) + " bytes");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (o.dtype == DSV_BF16) {
+    uint16_t* qlr = at<uint16_t>(workspace, w.qlr);
+    uint16_t* klr = at<uint16_t>(workspace, w.klr);
+    TRY_HIP(dsv::launch_proj_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(wq), qlr, o.bh(), o.n,
+                                  o.h, o.d, o.r, st), "projection of q");
+    TRY_HIP(dsv::launch_proj_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(wk), klr, o.bh(), o.n,
+                                  o.h, o.d, o.r, st), "projection of k");
+    TRY_HIP(dsv::launch_scores_bf16(qlr, klr, at<float>(workspace, w.scratch), block_scores, o.bh(), o.n, o.nkb(),
+                                    o.r, o.bq, o.ps, st), "block scores");
+  } else {
+    float* qlr = at<float>(workspace, w.qlr);
+    float* klr = at<float>(workspace, w.klr);
+    TRY_HIP(dsv::launch_proj_f32(static_cast<const float*>(q), static_cast<const float*>(wq), qlr, o.bh(), o.n, o.h,
+                                 o.d, o.r, st), "projection of q");
+    TRY_HIP(dsv::launch_proj_f32(static_cast<const float*>(k), static_cast<const float*>(wk), klr, o.bh(), o.n, o.h,
+                                 o.d, o.r, st), "projection of k");
+    TRY_HIP(dsv::launch_scores_f32(qlr, klr, at<float>(workspace, w.lse), block_scores, o.bh(), o.n, o.r, o.bq, o.bk,
+                                   o.ps, st), "block scores");
+  }
+  return DSV_OK;
+}
+
+dsv_status dsv_select_topk(const dsv_problem* p, const float* block_scores, int32_t* block_idx, void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, false));
+  TRY(check_ptr(block_scores, "block_scores", 4));
+  TRY(check_ptr(block_idx, "block_idx", 4));
+  TRY_HIP(dsv::launch_select_topk(block_scores, block_idx, o.bh() * o.nqb(), o.nkb(), o.k,
+                                  static_cast<hipStream_t>(stream)), "top-k selection");
+  return DSV_OK;
+}
+
+size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p) {
+  Prob o;
+  if (to_prob(p, o, false) != DSV_OK) return 0;
+  return fwd_ws_bytes(o);
+}
+
+dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, void* o_ptr, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, false));
+  TRY(check_bf16_attn(o));
+  TRY(check_f32_attn(o));
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(v, "v"));
+  TRY(check_ptr(block_idx, "block_idx", 4));
+  TRY(check_ptr(o_ptr, "o"));
+  TRY(check_ptr(lse, "lse"));
+  const size_t need = fwd_ws_bytes(o);
+  if (need) {
+    TRY(check_ptr(workspace, "workspace", kWsAlign));
+    if (workspace_bytes < need)
+      return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "forward workspace needs " + std::to_string(need) + " bytes");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (o.dtype == DSV_BF16) {
+    uint16_t* vt = at<uint16_t>(workspace, 0);
+    TRY_HIP(dsv::launch_transpose_bf16(static_cast<const uint16_t*>(v), vt, o.bh(), o.n, o.d, st), "transpose of v");
+    TRY_HIP(dsv::launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, block_idx,
+                                      static_cast<uint16_t*>(o_ptr), lse, o.bh(), o.n, o.d, o.bq, o.k, o.sm, st),
+            "sparse attention forward");
+  } else {
+    TRY_HIP(dsv::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                     static_cast<const float*>(v), block_idx, static_cast<float*>(o_ptr), lse, o.bh(),
+                                     o.n, o.d, o.bq, o.bk, o.k, o.sm, st), "sparse attention forward");
+  }
+  return DSV_OK;
+}
+
+size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p) {
+  Prob o;
+  if (to_prob(p, o, false) != DSV_OK) return 0;
+  return bwd_ws(o).total;
+}
+
+dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v, const void* o_ptr,
+                               const void* dout, const float* lse, const int32_t* block_idx, void* dq, void* dk,
+                               void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, false));
+  TRY(check_bf16_attn(o));
+  TRY(check_f32_attn(o));
+  const void* ptrs[] = {q, k, v, o_ptr, dout, lse, dq, dk, dv};
+  const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
+  for (int i = 0; i < 9; ++i) TRY(check_ptr(ptrs[i], names[i]));
+  TRY(check_ptr(block_idx, "block_idx", 4));
+  TRY(check_ptr(workspace, "workspace", kWsAlign));
+  const BwdWs w = bwd_ws(o);
+  if (workspace_bytes < w.total)
+    return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "backward workspace needs " + std::to_string(w.total) + " bytes");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* col_ptr = at<int32_t>(workspace, w.col_ptr);
+  int32_t* rows = at<int32_t>(workspace, w.rows);
+  TRY_HIP(dsv::launch_csc(block_idx, at<uint32_t>(workspace, w.bitmap), at<int32_t>(workspace, w.counts), col_ptr,
+                          rows, o.bh(), o.nqb(), o.nkb(), o.k, st), "block-list transpose");
+  float* dvec = at<float>(workspace, w.dvec);
+  if (o.dtype == DSV_BF16) {
+    const uint16_t* q16 = static_cast<const uint16_t*>(q);
+    const uint16_t* k16 = static_cast<const uint16_t*>(k);
+    const uint16_t* v16 = static_cast<const uint16_t*>(v);
+    const uint16_t* do16 = static_cast<const uint16_t*>(dout);
+    uint16_t* qt = at<uint16_t>(workspace, w.qt);
+    uint16_t* dot = at<uint16_t>(workspace, w.dot);
+    uint16_t* kt = at<uint16_t>(workspace, w.kt);
+    float* lse2 = at<float>(workspace, w.lse2);
+    TRY_HIP(dsv::launch_transpose_bf16(q16, qt, o.bh(), o.n, o.d, st), "transpose of q");
+    TRY_HIP(dsv::launch_transpose_bf16(do16, dot, o.bh(), o.n, o.d, st), "transpose of dout");
+    TRY_HIP(dsv::launch_transpose_bf16(k16, kt, o.bh(), o.n, o.d, st), "transpose of k");
+    TRY_HIP(dsv::launch_bwd_pre_bf16(static_cast<const uint16_t*>(o_ptr), do16, lse, dvec, lse2, o.bh() * o.n, o.d,
+                                     st), "backward preprocess");
+    TRY_HIP(dsv::launch_bwd_dkdv_bf16(q16, qt, k16, v16, do16, dot, lse2, dvec, col_ptr, rows,
+                                      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), o.bh(), o.n, o.d, o.bq,
+                                      o.k, o.sm, st), "backward dK/dV");
+    TRY_HIP(dsv::launch_bwd_dq_bf16(q16, k16, kt, v16, do16, lse2, dvec, block_idx, static_cast<uint16_t*>(dq), o.bh(),
+                                    o.n, o.d, o.bq, o.k, o.sm, st), "backward dQ");
+  } else {
+    TRY_HIP(dsv::launch_bwd_pre_f32(static_cast<const float*>(o_ptr), static_cast<const float*>(dout), dvec,
+                                    o.bh() * o.n, o.d, st), "backward preprocess");
+    TRY_HIP(dsv::launch_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                                static_cast<const float*>(dout), lse, dvec, block_idx, col_ptr, rows,
+                                static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), o.bh(), o.n,
+                                o.d, o.bq, o.bk, o.k, o.sm, st), "backward");
+  }
+  return DSV_OK;
+}
+
+}  // extern "C"

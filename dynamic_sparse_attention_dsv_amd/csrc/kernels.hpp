@@ -1,0 +1,54 @@
+// Host-callable launchers of the device kernels (each enqueues on `st` and
+// returns the launch status).  Pointers are device pointers; sizes are
+// validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsv {
+
+// predictor
+hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* w, uint16_t* out, int bh, int n, int heads,
+                            int d, int r, hipStream_t st);
+hipError_t launch_proj_f32(const float* x, const float* w, float* out, int bh, int n, int heads, int d, int r,
+                           hipStream_t st);
+int score_slots(int items);
+size_t score_scratch_bytes(int items, int nkb);
+hipError_t launch_scores_bf16(const uint16_t* qlr, const uint16_t* klr, float* scratch, float* scores, int bh,
+                              int n, int nkb, int r, int bq, float pred_scale, hipStream_t st);
+hipError_t launch_scores_f32(const float* qlr, const float* klr, float* lse, float* scores, int bh, int n, int r,
+                             int bq, int bk, float pred_scale, hipStream_t st);
+
+// selection
+hipError_t launch_select_topk(const float* scores, int32_t* idx, int rows, int nkb, int k, hipStream_t st);
+
+// forward
+hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt, const int32_t* idx,
+                                uint16_t* o, float* lse, int bh, int n, int d, int bq, int topk, float sm_scale,
+                                hipStream_t st);
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* idx, float* o,
+                               float* lse, int bh, int n, int d, int bq, int bk, int topk, float sm_scale,
+                               hipStream_t st);
+
+// backward and helpers
+hipError_t launch_transpose_bf16(const uint16_t* in, uint16_t* out, int bh, int n, int d, hipStream_t st);
+hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* dout, const float* lse, float* dvec, float* lse2,
+                               int rows, int d, hipStream_t st);
+hipError_t launch_bwd_pre_f32(const float* o, const float* dout, float* dvec, int rows, int d, hipStream_t st);
+hipError_t launch_csc(const int32_t* idx, uint32_t* bitmap, int32_t* counts, int32_t* col_ptr, int32_t* rows,
+                      int bh, int nqb, int nkb, int topk, hipStream_t st);
+hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* qt, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* dout, const uint16_t* dot, const float* lse2, const float* dvec,
+                                const int32_t* col_ptr, const int32_t* rows, uint16_t* dk, uint16_t* dv, int bh,
+                                int n, int d, int bq, int topk, float sm_scale, hipStream_t st);
+hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* kt, const uint16_t* v,
+                              const uint16_t* dout, const float* lse2, const float* dvec, const int32_t* idx,
+                              uint16_t* dq, int bh, int n, int d, int bq, int topk, float sm_scale, hipStream_t st);
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dout, const float* lse,
+                          const float* dvec, const int32_t* idx, const int32_t* col_ptr, const int32_t* rows,
+                          float* dq, float* dk, float* dv, int bh, int n, int d, int bq, int bk, int topk,
+                          float sm_scale, hipStream_t st);
+
+}  // namespace dsv

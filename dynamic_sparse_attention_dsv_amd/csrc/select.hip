@@ -1,0 +1,87 @@
+// Critical-KV selection: top-k KV blocks per query block.
+//
+// Method: the DSV pages ("DSV: Exploiting Dynamic Sparsity to Accelerate
+// Large-Scale Video DiT Training", gist.science/de and /es, technical summary
+// §2.B) select the top-k critical KV pairs from the low-rank estimate; tokens of
+// one query group share the selection.  Here the unit is the KV block: for each
+// (b, h, query block) the k blocks with the largest predicted mass are kept,
+// ties toward the smaller block index, and written in ascending block order.
+//
+// gfx950 design: one wave64 per query block.  Lane l holds blocks e*64 + l
+// (e = 0 .. NPL-1), loaded coalesced.  Scores become order-preserving 32-bit
+// keys; the k-th largest key is found by an MSB-first bit search whose counts
+// are wave ballots + scalar popcounts.  Ties at the threshold are resolved by
+// block index through a running prefix count in ascending block order, so the
+// output positions fall out of the same ballots.  The kernel is bound by the
+// HBM read of the score rows.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dsv {
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+template <int NPL>
+__global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
+                                                          int32_t* __restrict__ idx, int rows, int nkb,
+                                                          int k) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wave exits together
+  const float* src = scores + (size_t)row * nkb;
+  uint32_t key[NPL];
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) {
+    const int kb = e * 64 + lane;
+    key[e] = kb < nkb ? max(order_key(src[kb]), 1u) : 0u;  // padding = 0, valid keys >= 1
+  }
+  // MSB-first search for T = the k-th largest key: the largest T with count(key >= T) >= k.
+  // Valid keys are >= 1, so padding never counts (k <= nkb valid keys exist).
+  uint32_t prefix = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) cnt += popc64(__ballot(key[e] >= cand));
+    if (cnt >= k) prefix = cand;
+  }
+  const uint32_t T = prefix;
+  int gt = 0;
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) gt += popc64(__ballot(key[e] > T));
+  const int need = k - gt;  // number of ties at T to keep, smallest block index first
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t* dst = idx + (size_t)row * k;
+  int taken = 0, ties_seen = 0;
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) {
+    const bool tie = key[e] == T && key[e] != 0u;
+    const uint64_t tie_m = __ballot(tie);
+    const int tie_rank = ties_seen + popc64(tie_m & lt_mask);
+    const bool sel = key[e] > T || (tie && tie_rank < need);
+    const uint64_t sel_m = __ballot(sel);
+    if (sel) dst[taken + popc64(sel_m & lt_mask)] = e * 64 + lane;
+    taken += popc64(sel_m);
+    ties_seen += popc64(tie_m);
+  }
+}
+
+hipError_t launch_select_topk(const float* scores, int32_t* idx, int rows, int nkb, int k, hipStream_t st) {
+  const dim3 grid((rows + 3) / 4), block(256);
+  const int npl = (nkb + 63) / 64;
+#define SEL(N_)                                                                                   \
+  if (npl <= N_) {                                                                                \
+    hipLaunchKernelGGL((select_topk_kernel<N_>), grid, block, 0, st, scores, idx, rows, nkb, k); \
+    return hipGetLastError();                                                                     \
+  }
+  SEL(1) SEL(2) SEL(4) SEL(8) SEL(16) SEL(32) SEL(64)
+#undef SEL
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsv

@@ -1,0 +1,198 @@
+/*
+ * dsv.h -- C ABI of the DSV dynamic block-sparse attention library (libdsv.so) for
+ * AMD MI355X (gfx950).
+ *
+ * The method: DSV, as described by the explainer pages titled "DSV: Exploiting
+ * Dynamic Sparsity to Accelerate Large-Scale Video DiT Training"
+ * (gist.science/de/paper/2502.07590 -- cited [de] -- and
+ * gist.science/es/paper/2502.07590 -- cited [es]; section numbers refer to the
+ * pages' technical summaries).  A cheap per-head low-rank predictor estimates
+ * Q K^T, the critical KV blocks of every query block are chosen by top-k, and
+ * exact softmax attention runs over those blocks only, forward and backward.
+ *
+ * The four compute calls, in pipeline order:
+ *   dsv_predict          predicted attention mass per (query block, KV block)
+ *   dsv_select_topk      the k most important KV blocks of each query block
+ *   dsv_sparse_attn_fwd  softmax attention restricted to the selected blocks
+ *   dsv_sparse_attn_bwd  its gradients with respect to Q, K and V
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Every tensor argument is a DEVICE pointer into memory the caller
+ *   allocated (hipMalloc or equivalent) on the current HIP device.  The library
+ *   never allocates, frees or retains a pointer after the call returns.  Tensor
+ *   pointers must be 16-byte aligned; workspace pointers 256-byte aligned.
+ * Layout.  All tensors are dense, row-major (C order), no strides:
+ *     q, k, v, o, dout, dq, dk, dv   [B, H, N, d]   element type = problem.dtype
+ *     wq, wk                          [H, d, r]      element type = problem.dtype
+ *     lse                             [B, H, N]      float32
+ *     block_scores                    [B, H, N/Bq, N/Bk]  float32
+ *     block_idx                       [B, H, N/Bq, k]     int32
+ *   bf16 tensors hold IEEE bfloat16 bit patterns (uint16 storage).
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Calls only enqueue work on it and return; nothing is synchronised.
+ * Errors.  Arguments are validated on the host before any launch; on failure the
+ *   call returns a non-zero dsv_status, enqueues nothing, and dsv_last_error()
+ *   describes the problem (thread-local string, valid until the next call on the
+ *   same thread).  A failed launch returns DSV_ERR_HIP.  Non-finite inputs are
+ *   not checked: they propagate into the outputs.
+ * State.  The library has no global mutable state; calls are thread-safe and may
+ *   run concurrently on different streams with different buffers.  All calls are
+ *   deterministic (bitwise repeatable for the same inputs and problem).
+ */
+#ifndef DSV_H_
+#define DSV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSV_OK = 0,
+  DSV_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, inconsistent sizes   */
+  DSV_ERR_UNSUPPORTED = 2,        /* valid problem outside the compiled instances  */
+  DSV_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSV_ERR_HIP = 4                 /* a HIP runtime or launch error                 */
+} dsv_status;
+
+typedef enum { DSV_F32 = 0, DSV_BF16 = 1 } dsv_dtype;
+
+/*
+ * The problem.  Sizes follow the pages' statement: per attention head
+ * ([es] §2.A: the predictor approximates Q K^T of each head independently),
+ * queries grouped into blocks of consecutive tokens that share one selection
+ * ([de] §2.B / [es] §2.B "Query Grouping"), keys grouped into KV blocks that are
+ * the unit of selection, and k blocks kept per query block ([de] §2.B top-k).
+ *
+ *   batch, heads        B, H >= 1
+ *   seq_len             N >= 1 tokens (a flattened T x H x W video latent)
+ *   head_dim            d
+ *   q_block, kv_block   Bq, Bk; N % Bq == 0, N % Bk == 0, Bq % Bk == 0
+ *   topk                k, 1 <= k <= N / Bk
+ *   rank                r, the predictor rank
+ *   dtype               DSV_F32 or DSV_BF16 (storage and MFMA operand type)
+ *   sm_scale            softmax scale of the attention; <= 0 means 1/sqrt(d)
+ *   pred_scale          scale of the predicted logits;   <= 0 means 1/sqrt(d)
+ *
+ * Compiled instances (others return DSV_ERR_UNSUPPORTED):
+ *   bf16: d in {64, 128}, r in {16, 32}, Bq in {64, 128}, Bk = 64, N/Bk <= 4096;
+ *         dsv_predict additionally needs N % 128 == 0
+ *   f32 : d <= 128, r <= 64, any Bq/Bk satisfying the divisibility rules,
+ *         N/Bk <= 4096 (a plain VALU path meant for small problems)
+ */
+typedef struct {
+  int32_t batch;
+  int32_t heads;
+  int32_t seq_len;
+  int32_t head_dim;
+  int32_t q_block;
+  int32_t kv_block;
+  int32_t topk;
+  int32_t rank;
+  int32_t dtype;      /* dsv_dtype */
+  float sm_scale;
+  float pred_scale;
+} dsv_problem;
+
+/* Workspace bytes dsv_predict needs for this problem (0 if the problem is invalid).
+   The size depends on the current device's compute-unit count: query it on the
+   device the call will run on. */
+size_t dsv_predict_workspace_size(const dsv_problem* p);
+
+/*
+ * dsv_predict -- low-rank sparsity predictor ([es] §2.A "Estimadores de Baja
+ * Rango"; [de] §2.A stage 2, §2.B "Fused MM & Top-K"; [de] §2.B query grouping).
+ *
+ *   Q_lr = round(Q Wq[h]),  K_lr = round(K Wk[h])        (round = to dtype, RNE)
+ *   l_ij = pred_scale * <Q_lr_i, K_lr_j>                  (all j: no causal mask)
+ *   P_ij = exp(l_ij) / sum_j' exp(l_ij')                  (row softmax over all N keys)
+ *   block_scores[b,h,qb,kb] = sum_{i in qb} sum_{j in kb} P_ij
+ * i.e. the predicted attention mass of query block qb on KV block kb, summed
+ * over the block's rows (each score row sums to Bq).  The N x N matrix is never
+ * written to memory.
+ *
+ *   q, k          [B, H, N, d]   inputs
+ *   wq, wk        [H, d, r]      predictor weights
+ *   workspace     >= dsv_predict_workspace_size(p) bytes, caller-owned scratch.
+ *                 On return its first bytes hold Q_lr then K_lr, each
+ *                 [B, H, N, r] in dtype (a by-product callers may inspect).
+ *   block_scores  [B, H, N/Bq, N/Bk] float32 output.
+ */
+dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const void* wq,
+                       const void* wk, void* workspace, size_t workspace_bytes,
+                       float* block_scores, void* stream);
+
+/*
+ * dsv_select_topk -- critical-KV selection ([de] §2.B "Top-k-Selektion";
+ * [es] §2.B).  For every (b, h, qb) the k KV blocks with the largest
+ * block_scores, ties broken toward the smaller block index, written ascending
+ * (distinct indices).  Scores are compared as IEEE floats; a NaN sorts above +inf.
+ *
+ *   block_scores  [B, H, N/Bq, N/Bk] float32 input
+ *   block_idx     [B, H, N/Bq, k] int32 output
+ */
+dsv_status dsv_select_topk(const dsv_problem* p, const float* block_scores, int32_t* block_idx,
+                           void* stream);
+
+/* Workspace bytes dsv_sparse_attn_fwd needs (0 if none is needed or the problem is
+   invalid; with 0, `workspace` may be NULL). */
+size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);
+
+/*
+ * dsv_sparse_attn_fwd -- exact softmax attention over the selected KV blocks
+ * only ([es] §3 "kernels ... para estimación y atención dispersa"; [de] §2.A
+ * stage 2 sparse training).  For each query row i of block qb, with
+ * J = the keys of the blocks in block_idx[b,h,qb]:
+ *   s_ij = sm_scale <q_i, k_j>,  O_i = sum_{j in J} softmax_J(s_i)_j v_j,
+ *   lse_i = log sum_{j in J} exp(s_ij)   (natural log)
+ * block_idx rows must hold k distinct indices in [0, N/Bk); their order does not
+ * matter (dsv_select_topk emits them ascending).  Indices are not validated:
+ * an out-of-range index is clamped into range (the result is then meaningless
+ * but no memory outside the tensors is touched); duplicates count twice.
+ *
+ *   q, k, v     [B, H, N, d] inputs;  block_idx [B, H, N/Bq, k]
+ *   o           [B, H, N, d] output (dtype);  lse [B, H, N] float32 output
+ *   workspace   >= dsv_sparse_attn_fwd_workspace_size(p) bytes (holds V^T)
+ */
+dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, void* o, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Workspace bytes dsv_sparse_attn_bwd needs (0 if the problem is invalid). */
+size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p);
+
+/*
+ * dsv_sparse_attn_bwd -- gradients of the sparse attention (the method trains
+ * with it: [de] §2.A stage 2; [es] §2.A fase 2).  With P the sparse softmax of
+ * the forward and dO = dout:
+ *   dV_J += P^T dO,  dP = dO V_J^T,  dS = P o (dP - D),  D_i = sum_c dO_ic O_ic,
+ *   dQ = sm_scale dS K_J,  dK_J += sm_scale dS^T Q.
+ * o and lse must be the forward's outputs for the same q, k, v, block_idx.
+ * No gradient flows to the predictor or to block_idx.
+ *
+ *   q, k, v, o, dout  [B, H, N, d];  lse [B, H, N];  block_idx [B, H, N/Bq, k]
+ *   dq, dk, dv        [B, H, N, d] outputs (dtype), fully overwritten
+ *   workspace         >= dsv_sparse_attn_bwd_workspace_size(p) bytes
+ */
+dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
+                               const void* o, const void* dout, const float* lse,
+                               const int32_t* block_idx, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English name of a status code. */
+const char* dsv_status_string(dsv_status s);
+
+/* Detail of the last failure on this thread ("" if none). */
+const char* dsv_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t dsv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSV_H_ */

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares with C linkage, its struct layout matches the header, and
+invalid arguments are rejected on the host before any device work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dynamic_sparse_attention_dsv_amd as dsv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsv.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsv.LIB_PATH):
+        pytest.skip("libdsv.so not built")
+    return dsv.load_library()
+
+
+def test_every_declared_function_is_exported(lib):
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", dsv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert sorted(dsv.EXPORTED) == declared
+
+
+def test_problem_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "dsv.h"\n'
+                   "int main(void){printf(\"%zu %zu %zu %zu\\n\", sizeof(dsv_problem), "
+                   "offsetof(dsv_problem, dtype), offsetof(dsv_problem, sm_scale), offsetof(dsv_problem, pred_scale));"
+                   "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    size, off_dtype, off_sm, off_ps = map(int, subprocess.run([str(exe)], capture_output=True, text=True,
+                                                              check=True).stdout.split())
+    assert size == ctypes.sizeof(dsv.Problem)
+    assert off_dtype == dsv.Problem.dtype.offset
+    assert off_sm == dsv.Problem.sm_scale.offset and off_ps == dsv.Problem.pred_scale.offset
+
+
+def test_status_strings_and_version(lib):
+    for code, name in dsv.STATUS.items():
+        assert lib.dsv_status_string(code).decode() == name
+    assert lib.dsv_version() >= 100
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails validation first
+
+
+def _prob(**kw):
+    base = dict(batch=1, heads=2, seq_len=1024, head_dim=64, q_block=64, kv_block=64, topk=2, rank=16,
+                dtype=dsv.DSV_BF16, sm_scale=0.0, pred_scale=0.0)
+    base.update(kw)
+    return dsv.Problem(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(topk=0), 1), (dict(topk=17), 1), (dict(seq_len=1000), 1), (dict(q_block=96), 1),
+    (dict(batch=0), 1), (dict(dtype=7), 1), (dict(head_dim=96), 2), (dict(kv_block=32, q_block=64), 2),
+    (dict(seq_len=64 * 5000, q_block=64, kv_block=64), 2),
+])
+def test_forward_rejects_bad_problems_before_launch(lib, kw, code):
+    p = _prob(**kw)
+    st = lib.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == code, lib.dsv_last_error()
+    assert lib.dsv_last_error().decode()
+
+
+def test_null_and_misaligned_pointers_are_rejected(lib):
+    p = _prob()
+    assert lib.dsv_select_topk(None, FAKE, FAKE, None) == 1
+    assert lib.dsv_select_topk(ctypes.byref(p), None, FAKE, None) == 1
+    assert lib.dsv_select_topk(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 2), FAKE, None) == 1
+    assert "aligned" in lib.dsv_last_error().decode()
+    st = lib.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, ctypes.c_void_p((1 << 20) + 8), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 40, None)
+    assert st == 1
+
+
+def test_short_workspace_is_rejected(lib):
+    p = _prob()
+    need = lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(p))
+    assert need == 1 * 2 * 1024 * 64 * 2  # one transposed copy of V in bf16
+    st = lib.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+    assert st == 3
+    nb = lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(p))
+    assert nb > 3 * need
+    st = lib.dsv_sparse_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 nb - 1, None)
+    assert st == 3
+    assert lib.dsv_sparse_attn_fwd_workspace_size(None) == 0
+
+
+def test_predictor_rejects_unsupported_rank(lib):
+    p = _prob(rank=24)
+    st = lib.dsv_predict(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, FAKE, None)
+    assert st == 2
+    p = _prob(seq_len=64 * 3, q_block=64)  # N % 128 != 0 for the bf16 predictor
+    p.topk = 1
+    assert lib.dsv_predict(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, FAKE, None) == 2

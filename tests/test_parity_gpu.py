@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same
+seeded inputs.  Criteria: block indices bit-exact wherever the oracle's top-k gap
+exceeds 1e-3 (near-ties must be valid choices); with the oracle's indices fed in,
+forward max-abs <= 1e-5 (fp32) or <= 2e-2 with relative L2 <= 5e-3 (bf16);
+bf16 gradients max-abs <= 3e-2."""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_sparse_attention_dsv_amd as dsv
+from oracle import dsv_oracle as O
+from tests.gpu_helpers import (FWD_BF16_MAXABS, FWD_BF16_RELL2, FWD_F32_MAXABS, GRAD_BF16_MAXABS, check_indices, log,
+                               rel_l2, seeded_idx, to_dev, to_f64)
+from workloads import get_config, make_inputs
+from workloads.generator import widen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsv.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _scale(d):
+    return 1.0 / np.sqrt(d)
+
+
+def _run_gpu_path(cfg, inp, idx_fed=None):
+    """predict -> select (GPU); forward/backward with `idx_fed` (or the GPU's own selection)."""
+    t = {k: to_dev(v) for k, v in inp.items()}
+    scores, qlr, klr = dsv.predict(t["q"], t["k"], t["wq"], t["wk"], q_block=cfg.q_block, kv_block=cfg.kv_block,
+                                   return_projections=True)
+    idx = dsv.select_topk(scores, cfg.topk, q_block=cfg.q_block, kv_block=cfg.kv_block)
+    use = idx if idx_fed is None else to_dev(idx_fed)
+    o, lse = dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], use, q_block=cfg.q_block, kv_block=cfg.kv_block)
+    grads = None
+    if "do" in t:
+        grads = dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, use, q_block=cfg.q_block,
+                                    kv_block=cfg.kv_block)
+    torch.cuda.synchronize()
+    return dict(t=t, scores=scores, qlr=qlr, klr=klr, idx=idx, o=o, lse=lse, grads=grads)
+
+
+# ------------------------------------------------------------------ C1: tiny fp32, full path
+
+
+def test_c1_fp32_full_path():
+    cfg = get_config("C1")
+    log(f"[parity] C1 fp32 N={cfg.seq_len} H={cfg.heads}")
+    inp = make_inputs(cfg, with_grad=True)
+    x = {k: widen(v) for k, v in inp.items()}
+    sc = _scale(cfg.head_dim)
+    scores_o, qlr_o, klr_o = O.predict(x["q"], x["k"], x["wq"], x["wk"], cfg.q_block, cfg.kv_block, sc, "f32")
+    idx_o = O.select_topk(scores_o, cfg.topk)
+    o_o, lse_o = O.sparse_attn_fwd(x["q"], x["k"], x["v"], idx_o, cfg.q_block, cfg.kv_block, sc)
+    g_o = O.sparse_attn_bwd(x["q"], x["k"], x["v"], x["do"], idx_o, cfg.q_block, cfg.kv_block, sc)
+    r = _run_gpu_path(cfg, inp, idx_fed=idx_o)
+    np.testing.assert_allclose(to_f64(r["qlr"]), qlr_o, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(to_f64(r["scores"]), scores_o, rtol=1e-4, atol=1e-5)
+    cov = check_indices(r["idx"].cpu().numpy(), scores_o, cfg.topk)
+    log(f"[parity] C1 index coverage {cov:.3f}")
+    assert np.abs(to_f64(r["o"]) - o_o).max() <= FWD_F32_MAXABS
+    assert np.abs(to_f64(r["lse"]) - lse_o).max() <= FWD_F32_MAXABS
+    for got, ref in zip(r["grads"], g_o):
+        assert np.abs(to_f64(got) - ref).max() <= 1e-4
+
+
+# ------------------------------------------------------------------ selection alone, bit-exact
+
+
+@pytest.mark.parametrize("b,h,nqb,nkb,k", [(1, 2, 16, 16, 2), (1, 3, 128, 128, 13), (2, 2, 64, 1024, 103),
+                                           (1, 2, 64, 2048, 205), (1, 1, 8, 4096, 4096), (1, 1, 4, 100, 1),
+                                           (1, 1, 4, 100, 100), (1, 1, 4, 100, 37)])
+def test_select_matches_oracle_bit_exactly(b, h, nqb, nkb, k):
+    log(f"[parity] select nkb={nkb} k={k}")
+    rng = np.random.default_rng(nkb + k)
+    s = rng.random((b, h, nqb, nkb)).astype(np.float32)
+    s[..., ::7] = np.float32(0.5)  # many exact ties
+    s[0, 0, 0] = 0.0               # an all-zero row
+    idx = dsv.select_topk(to_dev(s), k, q_block=nkb * 64 // nqb, kv_block=64)
+    want = O.select_topk(s.astype(np.float64), k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+
+
+# ------------------------------------------------------------------ bf16 configs, full oracle on sampled heads
+
+
+def _bf16_config_check(name, heads_checked):
+    cfg = get_config(name)
+    log(f"[parity] {name} bf16 N={cfg.seq_len} H={cfg.heads} d={cfg.head_dim} r={cfg.rank} k={cfg.topk}")
+    inp = make_inputs(cfg, workers=8)
+    sc = _scale(cfg.head_dim)
+    # oracle indices for the checked heads; other heads get a seeded list
+    hs = list(heads_checked)
+    x = {k: widen(v[:, hs]) if v.ndim == 4 else widen(v[hs]) for k, v in inp.items()}
+    scores_o, qlr_o, klr_o = O.predict(x["q"], x["k"], x["wq"], x["wk"], cfg.q_block, cfg.kv_block, sc, "bf16")
+    idx_o = O.select_topk(scores_o, cfg.topk)
+    idx_fed = seeded_idx(7, (cfg.batch, cfg.heads), cfg.nqb, cfg.nkb, cfg.topk)
+    idx_fed[:, hs] = idx_o
+    r = _run_gpu_path(cfg, inp, idx_fed=idx_fed)
+    # projections: nearest bf16 of an fp32 accumulation; rare 1-ulp differences from the exact product
+    qg, kg = to_f64(r["qlr"][:, hs]), to_f64(r["klr"][:, hs])
+    for got, ref in ((qg, qlr_o), (kg, klr_o)):
+        diff = got != ref
+        assert diff.mean() < 1e-3, diff.mean()
+        ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+        assert np.all(np.abs(got - ref)[diff] <= ulp[diff] * 1.0001)
+    # scores: against the oracle's score step fed with the GPU's own projections
+    sg = to_f64(r["scores"][:, hs])
+    for bi in range(cfg.batch):
+        for j in range(len(hs)):
+            ref = O.block_scores_head(qg[bi, j], kg[bi, j], cfg.q_block, cfg.kv_block, sc)
+            np.testing.assert_allclose(sg[bi, j], ref, rtol=2e-4, atol=2e-5)
+    np.testing.assert_allclose(to_f64(r["scores"]).sum(-1), cfg.q_block, rtol=1e-4)
+    cov = check_indices(r["idx"][:, hs].cpu().numpy(), scores_o, cfg.topk)
+    log(f"[parity] {name} index coverage (rows under the exact rule) {cov:.3f}")
+    # forward with the oracle's indices
+    o_o, lse_o = O.sparse_attn_fwd(x["q"], x["k"], x["v"], idx_o, cfg.q_block, cfg.kv_block, sc)
+    og = to_f64(r["o"][:, hs])
+    err, rl2 = np.abs(og - o_o).max(), rel_l2(og, o_o)
+    log(f"[parity] {name} fwd max-abs {err:.3e} rel-L2 {rl2:.3e}")
+    assert err <= FWD_BF16_MAXABS and rl2 <= FWD_BF16_RELL2
+    assert np.abs(to_f64(r["lse"][:, hs]) - lse_o).max() <= 1e-2
+    # backward
+    g_o = O.sparse_attn_bwd(x["q"], x["k"], x["v"], x["do"], idx_o, cfg.q_block, cfg.kv_block, sc)
+    for nm, got, ref in zip(("dq", "dk", "dv"), r["grads"], g_o):
+        gg = to_f64(got[:, hs])
+        e = np.abs(gg - ref).max()
+        log(f"[parity] {name} {nm} max-abs {e:.3e} rel-L2 {rel_l2(gg, ref):.3e}")
+        assert e <= GRAD_BF16_MAXABS
+    return cfg, inp, r, idx_fed
+
+
+def test_c2_bf16_all_heads():
+    cfg, inp, r, idx_fed = _bf16_config_check("C2", range(12))
+    # determinism: a second run is bitwise identical
+    r2 = _run_gpu_path(cfg, inp, idx_fed=idx_fed)
+    for key in ("scores", "idx", "o", "lse"):
+        assert torch.equal(r[key], r2[key]), key
+    for a, b in zip(r["grads"], r2["grads"]):
+        assert torch.equal(a, b)
+
+
+def test_c3_bf16_sampled_heads():
+    _bf16_config_check("C3", [0, 23])
+
+
+# ------------------------------------------------------------------ small shapes: batch > 1, every instance, k = all
+
+
+@pytest.mark.parametrize("d,bq,r", [(64, 64, 16), (64, 128, 32), (128, 64, 16), (128, 128, 32)])
+def test_bf16_instances_batch2(d, bq, r):
+    cfg = get_config("C2").with_(batch=2, heads=3, latent=(4, 16, 16), head_dim=d, rank=r, q_block=bq, topk=3)
+    log(f"[parity] instance d={d} Bq={bq} r={r} B=2")
+    inp = make_inputs(cfg)
+    sc = _scale(d)
+    x = {k: widen(v) for k, v in inp.items()}
+    scores_o, _, _ = O.predict(x["q"], x["k"], x["wq"], x["wk"], bq, 64, sc, "bf16")
+    idx_o = O.select_topk(scores_o, cfg.topk)
+    rr = _run_gpu_path(cfg, inp, idx_fed=idx_o)
+    check_indices(rr["idx"].cpu().numpy(), scores_o, cfg.topk)
+    o_o, _ = O.sparse_attn_fwd(x["q"], x["k"], x["v"], idx_o, bq, 64, sc)
+    og = to_f64(rr["o"])
+    assert np.abs(og - o_o).max() <= FWD_BF16_MAXABS and rel_l2(og, o_o) <= FWD_BF16_RELL2
+    g_o = O.sparse_attn_bwd(x["q"], x["k"], x["v"], x["do"], idx_o, bq, 64, sc)
+    for got, ref in zip(rr["grads"], g_o):
+        assert np.abs(to_f64(got) - ref).max() <= GRAD_BF16_MAXABS
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_all_blocks_selected_is_dense_attention(dtype):
+    # k = N/Bk: the sparse kernels must reproduce dense attention (torch SDPA in fp32 on the CPU)
+    cfg = get_config("C2").with_(heads=2, latent=(2, 16, 16), head_dim=64, rank=16, q_block=64, topk=8, dtype=dtype)
+    log(f"[parity] dense special case {dtype}")
+    inp = make_inputs(cfg)
+    x = {k: widen(v) for k, v in inp.items()}
+    idx = np.tile(np.arange(8, dtype=np.int32), (1, 2, 8, 1))
+    rr = _run_gpu_path(cfg, inp, idx_fed=idx)
+    assert np.array_equal(rr["idx"].cpu().numpy(), idx)  # k = nkb selects every block
+    ref = torch.nn.functional.scaled_dot_product_attention(*(torch.from_numpy(x[n]).float() for n in ("q", "k", "v")))
+    err = np.abs(to_f64(rr["o"]) - ref.double().numpy()).max()
+    assert err <= (FWD_BF16_MAXABS if dtype == "bf16" else 1e-5), err
+
+
+def test_single_block_and_unselected_blocks_get_zero_gradient():
+    cfg = get_config("C2").with_(heads=1, latent=(2, 16, 16), head_dim=128, rank=32, q_block=128, topk=1)
+    inp = make_inputs(cfg)
+    x = {k: widen(v) for k, v in inp.items()}
+    idx = np.full((1, 1, 4, 1), 3, dtype=np.int32)  # every query block picks KV block 3 only
+    rr = _run_gpu_path(cfg, inp, idx_fed=idx)
+    sc = _scale(128)
+    o_o, _ = O.sparse_attn_fwd(x["q"], x["k"], x["v"], idx, 128, 64, sc)
+    assert np.abs(to_f64(rr["o"]) - o_o).max() <= FWD_BF16_MAXABS
+    dq, dk, dv = (to_f64(g) for g in rr["grads"])
+    assert np.all(dk[0, 0, :192] == 0) and np.all(dv[0, 0, :192] == 0) and np.all(dk[0, 0, 256:] == 0)
+    g_o = O.sparse_attn_bwd(x["q"], x["k"], x["v"], x["do"], idx, 128, 64, sc)
+    for got, ref in zip((dq, dk, dv), g_o):
+        assert np.abs(got - ref).max() <= GRAD_BF16_MAXABS
+
+
+# ------------------------------------------------------------------ full-size configs, sampled outputs
+
+
+@pytest.mark.parametrize("name", ["C4", "C5"])
+def test_full_size_sampled(name):
+    cfg = get_config(name)
+    log(f"[parity] {name} full size N={cfg.seq_len} H={cfg.heads} k={cfg.topk}: generating inputs")
+    inp = make_inputs(cfg, workers=16)
+    sc = _scale(cfg.head_dim)
+    idx_fed = seeded_idx(11, (cfg.batch, cfg.heads), cfg.nqb, cfg.nkb, cfg.topk)
+    log(f"[parity] {name} running the GPU path")
+    r = _run_gpu_path(cfg, inp, idx_fed=idx_fed)
+    # properties over every row
+    s_all = r["scores"]
+    assert torch.isfinite(s_all).all()
+    np.testing.assert_allclose(s_all.sum(-1).double().cpu().numpy(), cfg.q_block, rtol=2e-4)
+    idx_all = r["idx"].cpu().numpy()
+    assert np.all(np.diff(idx_all, axis=-1) > 0) and idx_all.min() >= 0 and idx_all.max() < cfg.nkb
+    assert torch.isfinite(r["o"].float()).all()
+    rng = np.random.default_rng(5)
+    for h in (0, cfg.heads - 1):
+        xq, xk, xv, xdo = (widen(inp[n][0, h]) for n in ("q", "k", "v", "do"))
+        qlr_o = O.project(xq, widen(inp["wq"][h]), "bf16")
+        klr_o = O.project(xk, widen(inp["wk"][h]), "bf16")
+        for qb in rng.choice(cfg.nqb, size=3, replace=False):
+            rows = slice(qb * cfg.q_block, (qb + 1) * cfg.q_block)
+            s_o = O.block_scores_qblock(qlr_o[rows], klr_o, cfg.kv_block, sc)
+            cov = check_indices(idx_all[0, h, qb][None], s_o[None], cfg.topk)
+            o_o, lse_o = O.attn_fwd_qblock(xq[rows], xk, xv, idx_fed[0, h, qb], cfg.kv_block, sc)
+            og = to_f64(r["o"][0, h, rows])
+            assert np.abs(og - o_o).max() <= FWD_BF16_MAXABS and rel_l2(og, o_o) <= FWD_BF16_RELL2
+            assert np.abs(to_f64(r["lse"][0, h, rows]) - lse_o).max() <= 1e-2
+            dq_o, _, _, _ = O.attn_bwd_qblock(xq[rows], xk, xv, xdo[rows], idx_fed[0, h, qb], cfg.kv_block, sc)
+            assert np.abs(to_f64(r["grads"][0][0, h, rows]) - dq_o).max() <= GRAD_BF16_MAXABS
+            log(f"[parity] {name} h={h} qb={qb} ok (exact-rule row: {bool(cov)})")
+        kbs = rng.choice(cfg.nkb, size=2, replace=False)
+        for kb in kbs:
+            dk_o, dv_o = O.attn_bwd_kvblock(xq, xk, xv, xdo, idx_fed[0, h], kb, cfg.q_block, cfg.kv_block, sc)
+            keys = slice(kb * cfg.kv_block, (kb + 1) * cfg.kv_block)
+            assert np.abs(to_f64(r["grads"][1][0, h, keys]) - dk_o).max() <= GRAD_BF16_MAXABS
+            assert np.abs(to_f64(r["grads"][2][0, h, keys]) - dv_o).max() <= GRAD_BF16_MAXABS
+            log(f"[parity] {name} h={h} kb={kb} dK/dV ok")

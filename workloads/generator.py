@@ -155,13 +155,20 @@ def make_head(cfg: Config, b: int, h: int, with_grad: bool = True) -> Dict[str, 
     return out
 
 
+def _head_job(args):
+    cfg, b, h, with_grad = args
+    t = make_head(cfg, b, h, with_grad)
+    return {nm: _to_storage(x, cfg.dtype) for nm, x in t.items()}
+
+
 def make_inputs(cfg: Config, heads: Optional[Iterable[int]] = None, with_grad: Optional[bool] = None,
-                batches: Optional[Iterable[int]] = None) -> Dict[str, np.ndarray]:
+                batches: Optional[Iterable[int]] = None, workers: int = 1) -> Dict[str, np.ndarray]:
     """Storage arrays for the selected heads (default: all).
 
     Returns q, k, v (and do) as [B', H', N, d] and wq, wk as [H', d, r], in the
     config's storage dtype: float32 arrays for "f32", uint16 bf16 bit patterns
-    for "bf16".  Use :func:`widen` for their exact float64 values.
+    for "bf16".  Use :func:`widen` for their exact float64 values.  ``workers``
+    > 1 generates heads in parallel processes (same values).
     """
     if with_grad is None:
         with_grad = cfg.backward
@@ -173,12 +180,18 @@ def make_inputs(cfg: Config, heads: Optional[Iterable[int]] = None, with_grad: O
     out = {nm: np.empty((len(bs), len(hs), n, d), dtype=sdt) for nm in names}
     out["wq"] = np.empty((len(hs), d, r), dtype=sdt)
     out["wk"] = np.empty((len(hs), d, r), dtype=sdt)
-    for bi, b in enumerate(bs):
-        for hi, h in enumerate(hs):
-            t = make_head(cfg, b, h, with_grad)
-            for nm in names:
-                out[nm][bi, hi] = _to_storage(t[nm], cfg.dtype)
-            if bi == 0:
-                out["wq"][hi] = _to_storage(t["wq"], cfg.dtype)
-                out["wk"][hi] = _to_storage(t["wk"], cfg.dtype)
+    jobs = [(cfg, b, h, with_grad) for b in bs for h in hs]
+    if workers > 1 and len(jobs) > 1:
+        import multiprocessing as mp
+        with mp.get_context("fork").Pool(min(workers, len(jobs))) as pool:
+            results = pool.map(_head_job, jobs, chunksize=1)
+    else:
+        results = map(_head_job, jobs)
+    for j, t in enumerate(results):
+        bi, hi = divmod(j, len(hs))
+        for nm in names:
+            out[nm][bi, hi] = t[nm]
+        if bi == 0:
+            out["wq"][hi] = t["wq"]
+            out["wk"][hi] = t["wk"]
     return out
