@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of one DSV attention-layer step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic video tokens:
+predict (low-rank block scores) -> select (top-k KV blocks) -> sparse attention
+forward -> sparse attention backward, all in the HIP library.  The default
+workload is the long-video layer: B=1, H=40, N=131072 (32x64x64 latent), d=128,
+r=32, 128-token query blocks, 64-token KV blocks, k=205 of 2048 (10% density).
+
+Prints ONE JSON line.  `value` is the effective sparse-attention throughput of
+the whole step: forward+backward attention flops (4*B*H*N*k*Bk*d, times 3.5)
+divided by the full step time, predictor and selection included.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C5]
+                       [--no-dense] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (vendor figure)
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak (vendor figure)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="C5")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense (k = N/Bk) comparator")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device copy (a reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def kernel_units(cfg):
+    """Algorithmic work per launch of each kernel, and the roofline it is judged against."""
+    pairs = cfg.batch * cfg.heads * cfg.nqb * cfg.topk          # selected (query block, KV block) pairs
+    unit = cfg.q_block * cfg.kv_block * cfg.head_dim              # Bq*Bk*d
+    elems = cfg.batch * cfg.heads * cfg.seq_len * cfg.head_dim
+    return {
+        # forward: S = Q K^T and O = P V over every selected pair
+        "attn_fwd_kernel": ("mfma", 4.0 * pairs * unit),
+        # backward, 10*Bq*Bk*d per pair: S, dP, dV, dK (8 units) in the KV-parallel kernel,
+        # dQ (2 units) in the query-parallel kernel (its S and dP are recomputation)
+        "attn_bwd_dkdv_kernel": ("mfma", 8.0 * pairs * unit),
+        "attn_bwd_dq_kernel": ("mfma", 2.0 * pairs * unit),
+        # predictor sweep: reads Q_lr, K_lr per head and writes the scores (HBM-compulsory bytes)
+        "scores_kernel": ("alu", None),
+        "select_topk_kernel": ("hbm", 4.0 * cfg.batch * cfg.heads * cfg.nqb * (cfg.nkb + cfg.topk)),
+        "transpose_kernel(v)": ("hbm", 4.0 * elems),
+        "bwd_pre_kernel": ("hbm", 2.0 * 2 * elems + 12.0 * cfg.batch * cfg.heads * cfg.seq_len),
+    }
+
+
+def cpu_baseline(cfg, inp, target_s):
+    """The CPU oracle on a bounded sample of the same workload (one head, the first query blocks)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dsv_oracle as O
+    from workloads.generator import widen
+
+    cores = len(os.sched_getaffinity(0))
+    sc = 1.0 / np.sqrt(cfg.head_dim)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        xq, xk, xv, xdo = (widen(inp[n][0, 0]) for n in ("q", "k", "v", "do"))
+        qlr = O.project(xq, widen(inp["wq"][0]), cfg.dtype)
+        klr = O.project(xk, widen(inp["wk"][0]), cfg.dtype)
+        done = 0
+        while True:
+            rows = slice(done * cfg.q_block, (done + 1) * cfg.q_block)
+            s = O.block_scores_qblock(qlr[rows], klr, cfg.kv_block, sc)
+            idx = O.select_topk_row(s, cfg.topk)
+            O.attn_fwd_qblock(xq[rows], xk, xv, idx, cfg.kv_block, sc)
+            O.attn_bwd_qblock(xq[rows], xk, xv, xdo[rows], idx, cfg.kv_block, sc)
+            done += 1
+            if time.perf_counter() - t0 >= target_s or done >= cfg.nqb:
+                break
+        dt = time.perf_counter() - t0
+    flops = 14.0 * done * cfg.q_block * cfg.topk * cfg.kv_block * cfg.head_dim
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"head 0 of {cfg.name}, {done} of {cfg.nqb} query blocks: projections, full-key predictor "
+                      f"sweep, top-k, sparse forward and backward in float64 NumPy ({dt:.1f} s)",
+            "seconds": dt, "query_blocks": done}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path; "
+              "the sharding design is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import dynamic_sparse_attention_dsv_amd as dsv
+    from workloads import get_config, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dsv.load_library()
+    cfg = get_config(a.config)
+    dev = torch.device("cuda:0")
+    log(f"[bench] {cfg.name}: B={cfg.batch} H={cfg.heads} N={cfg.seq_len} d={cfg.head_dim} r={cfg.rank} "
+        f"Bq={cfg.q_block} Bk={cfg.kv_block} k={cfg.topk}/{cfg.nkb}; generating inputs")
+    t0 = time.perf_counter()
+    inp = make_inputs(cfg, with_grad=True, workers=min(16, len(os.sched_getaffinity(0))))
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    t = {k: to_dev(v) for k, v in inp.items()}
+    B, H, N, D = t["q"].shape
+    kw = dict(q_block=cfg.q_block, kv_block=cfg.kv_block)
+    ws_p, ws_f, ws_b = dsv.workspace_sizes(t["q"], topk=cfg.topk, rank=cfg.rank, **kw)
+    wsp = torch.empty(ws_p, dtype=torch.uint8, device=dev)
+    wsf = torch.empty(max(ws_f, 1), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    scores = torch.empty((B, H, cfg.nqb, cfg.nkb), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, H, cfg.nqb, cfg.topk), dtype=torch.int32, device=dev)
+    o, lse = torch.empty_like(t["q"]), torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def step(marks=None):
+        if marks: marks[0].record(stream)
+        dsv.predict(t["q"], t["k"], t["wq"], t["wk"], workspace=wsp, out=scores, **kw)
+        if marks: marks[1].record(stream)
+        dsv.select_topk(scores, cfg.topk, out=idx, **kw)
+        if marks: marks[2].record(stream)
+        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx, workspace=wsf, out=(o, lse), **kw)
+        if marks: marks[3].record(stream)
+        dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, idx, workspace=wsb, out=(dq, dk, dv), **kw)
+        if marks: marks[4].record(stream)
+
+    if a.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
+        del src, dst
+    for i in range(a.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{a.warmup} done")
+    phases = np.zeros(4)
+    dsv.timing_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(ev)
+        ev[4].synchronize()
+        phases += [ev[j].elapsed_time(ev[j + 1]) for j in range(4)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kstats = dsv.timing_end()
+    ms_step = wall * 1e3 / a.steps
+    phases /= a.steps
+    log(f"[bench] {a.steps} steps: {ms_step:.2f} ms/step (predict {phases[0]:.2f}, select {phases[1]:.2f}, "
+        f"fwd {phases[2]:.2f}, bwd {phases[3]:.2f} ms)")
+
+    attn_flops = cfg.fwd_flops() + cfg.bwd_flops()
+    value = attn_flops / (ms_step * 1e-3) / 1e12
+    attn_ms = phases[2] + phases[3]
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    kern = {n: {"launches": s[0], "avg_ms": s[1] / s[0], "min_ms": s[2], "max_ms": s[3]} for n, s in kstats.items()}
+
+    # roofline of the dominant kernel (largest total time)
+    units = kernel_units(cfg)
+    dom = max(kstats, key=lambda n: kstats[n][1])
+    bound, work = units.get(dom, ("unknown", None))
+    avg_s = kstats[dom][1] / kstats[dom][0] * 1e-3
+    roof = {"kernel": dom, "avg_ms": avg_s * 1e3}
+    if bound == "mfma":
+        ach = work / avg_s / 1e12
+        roof.update(bound="mfma", achieved=ach, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=ach / MFMA_BF16_PEAK_TFLOPS, traffic=None)
+    elif bound == "hbm":
+        ach = work / avg_s / 1e9
+        roof.update(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS, traffic=None)
+    else:
+        roof.update(bound=bound, achieved=None, peak=None, unit=None, frac=None, traffic=None)
+    # per-kernel rates for the attention kernels
+    rates = {}
+    for n in ("attn_fwd_kernel", "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"):
+        if n in kstats:
+            s = kstats[n][1] / kstats[n][0] * 1e-3
+            rates[n] = {"tflops": units[n][1] / s / 1e12, "frac": units[n][1] / s / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+    dense = None
+    if not a.no_dense:
+        log("[bench] dense comparator (k = N/Bk through the same kernels)")
+        idx_d = torch.arange(cfg.nkb, dtype=torch.int32, device=dev).repeat(B, H, cfg.nqb, 1).contiguous()
+        _, wsf_d, wsb_d = dsv.workspace_sizes(t["q"], topk=cfg.nkb, rank=cfg.rank, **kw)
+        wsb2 = torch.empty(wsb_d, dtype=torch.uint8, device=dev)
+        del wsb
+        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_d, workspace=wsf, out=(o, lse), **kw)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_d, workspace=wsf, out=(o, lse), **kw)
+        e1.record(stream)
+        dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, idx_d, workspace=wsb2, out=(dq, dk, dv), **kw)
+        e2.record(stream)
+        e2.synchronize()
+        dfwd, dbwd = e0.elapsed_time(e1), e1.elapsed_time(e2)
+        dense_flops = 3.5 * 4.0 * B * H * N * N * D
+        dense = {"fwd_ms": dfwd, "bwd_ms": dbwd, "tflops": dense_flops / ((dfwd + dbwd) * 1e-3) / 1e12,
+                 "speedup_attn": (dfwd + dbwd) / attn_ms, "ideal_speedup": cfg.nkb / cfg.topk}
+        log(f"[bench] dense fwd {dfwd:.1f} ms bwd {dbwd:.1f} ms")
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] CPU oracle baseline (bounded sample)")
+        cpu = cpu_baseline(cfg, inp, a.cpu_seconds)
+
+    rec = {
+        "metric": "sparse attn fwd+bwd effective TFLOP/s & tokens/s at N=131k, 10% density",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic (seeded smooth-bias video-token generator, random-init predictor)",
+        "config": {"workload": f"{cfg.name}: long-video attention layer, B={B} H={H} latent "
+                               f"{'x'.join(map(str, cfg.latent))} N={N} d={D} r={cfg.rank} Bq={cfg.q_block} "
+                               f"Bk={cfg.kv_block} top-{cfg.topk} of {cfg.nkb} KV blocks",
+                   "batch": B, "heads": H, "seq_len": N, "head_dim": D, "rank": cfg.rank, "q_block": cfg.q_block,
+                   "kv_block": cfg.kv_block, "topk": cfg.topk, "density": cfg.topk / cfg.nkb,
+                   "generator": cfg.generator},
+        "tokens_per_s": B * N / (ms_step * 1e-3),
+        "attn_fwd_bwd": {"ms": attn_ms, "tflops": attn_tflops, "frac_of_peak": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
+                         "tokens_per_s": B * N / (attn_ms * 1e-3)},
+        "phases_ms": {"predict": phases[0], "select": phases[1], "fwd": phases[2], "bwd": phases[3]},
+        "kernels": kern, "kernel_rates": rates, "dense": dense,
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

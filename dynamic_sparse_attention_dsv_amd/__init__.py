@@ -29,7 +29,7 @@ STATUS = {0: "DSV_OK", 1: "DSV_ERR_INVALID_ARGUMENT", 2: "DSV_ERR_UNSUPPORTED", 
 
 EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_select_topk", "dsv_sparse_attn_fwd_workspace_size",
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd_workspace_size", "dsv_sparse_attn_bwd", "dsv_status_string",
-            "dsv_last_error", "dsv_version")
+            "dsv_last_error", "dsv_version", "dsv_timing_begin", "dsv_timing_end")
 
 
 class Problem(ctypes.Structure):
@@ -38,6 +38,12 @@ class Problem(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("pred_scale", ctypes.c_float)]
+
+
+class KernelStat(ctypes.Structure):
+    """Mirror of ``dsv_kernel_stat`` in include/dsv.h."""
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double),
+                ("min_ms", ctypes.c_float), ("max_ms", ctypes.c_float)]
 
 
 class DSVError(RuntimeError):
@@ -69,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dsv_last_error": (ctypes.c_char_p, []),
         "dsv_version": (ctypes.c_int32, []),
+        "dsv_timing_begin": (ctypes.c_int, []),
+        "dsv_timing_end": (ctypes.c_int32, [ctypes.POINTER(KernelStat), ctypes.c_int32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -138,7 +146,8 @@ def predict_workspace_size(prob: Problem) -> int:
 
 
 def predict(q, k, wq, wk, *, q_block: int, kv_block: int = 64, pred_scale: Optional[float] = None,
-            workspace: Optional[torch.Tensor] = None, return_projections: bool = False):
+            workspace: Optional[torch.Tensor] = None, return_projections: bool = False,
+            out: Optional[torch.Tensor] = None):
     """Predicted attention mass per (query block, KV block): [B, H, N/Bq, N/Bk] float32."""
     lib = load_library()
     dev = _dev(q, k, wq, wk)
@@ -151,7 +160,8 @@ def predict(q, k, wq, wk, *, q_block: int, kv_block: int = 64, pred_scale: Optio
     r = wq.shape[2]
     prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=1, rank=r, pred_scale=pred_scale)
     ws = _workspace(int(lib.dsv_predict_workspace_size(ctypes.byref(prob))), dev, workspace)
-    scores = torch.empty((b, h, n // q_block, n // kv_block), dtype=torch.float32, device=dev)
+    scores = out if out is not None else torch.empty((b, h, n // q_block, n // kv_block), dtype=torch.float32,
+                                                     device=dev)
     _check(lib.dsv_predict(ctypes.byref(prob), _p(q), _p(k), _p(wq), _p(wk), _p(ws), ws.numel() * ws.element_size(),
                            _p(scores), _stream(dev)), "dsv_predict")
     if return_projections:
@@ -184,7 +194,8 @@ def select_topk(scores: torch.Tensor, topk: int, *, q_block: int, kv_block: int 
 
 
 def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_scale: Optional[float] = None,
-                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    workspace: Optional[torch.Tensor] = None,
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Softmax attention over the selected KV blocks only -> (o [B,H,N,d], lse [B,H,N] float32)."""
     lib = load_library()
     dev = _dev(q, k, v, block_idx)
@@ -196,8 +207,11 @@ def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_
     if tuple(block_idx.shape) != (b, h, n // q_block, prob.topk):
         raise ValueError("block_idx must be [B, H, N/Bq, k]")
     ws = _workspace(int(lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(prob))), dev, workspace)
-    o = torch.empty_like(q)
-    lse = torch.empty((b, h, n), dtype=torch.float32, device=dev)
+    if out is not None:
+        o, lse = out
+    else:
+        o = torch.empty_like(q)
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=dev)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.dsv_sparse_attn_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(block_idx), _p(o), _p(lse), _p(ws),
                                    nbytes, _stream(dev)), "dsv_sparse_attn_fwd")
@@ -205,7 +219,8 @@ def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_
 
 
 def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block: int = 64,
-                    sm_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+                    sm_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """Gradients (dq, dk, dv) of the sparse attention."""
     lib = load_library()
     dev = _dev(q, k, v, o, dout, lse, block_idx)
@@ -213,11 +228,34 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block:
     b, h, n, d = q.shape
     prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1], sm_scale=sm_scale)
     ws = _workspace(int(lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(prob))), dev, workspace)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     _check(lib.dsv_sparse_attn_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(o), _p(dout), _p(lse), _p(block_idx),
                                    _p(dq), _p(dk), _p(dv), _p(ws), ws.numel() * ws.element_size(), _stream(dev)),
            "dsv_sparse_attn_bwd")
     return dq, dk, dv
+
+
+def workspace_sizes(q: torch.Tensor, *, q_block: int, kv_block: int, topk: int, rank: int):
+    """(predict, forward, backward) workspace bytes for a problem shaped like q."""
+    lib = load_library()
+    prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=topk, rank=rank)
+    return (int(lib.dsv_predict_workspace_size(ctypes.byref(prob))),
+            int(lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(prob))),
+            int(lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(prob))))
+
+
+def timing_begin() -> None:
+    """Start bracketing every library launch from this thread with HIP events."""
+    _check(load_library().dsv_timing_begin(), "dsv_timing_begin")
+
+
+def timing_end() -> dict:
+    """Stop timing; {kernel name: (launches, total_ms, min_ms, max_ms)} (synchronises on the events)."""
+    lib = load_library()
+    buf = (KernelStat * 64)()
+    n = lib.dsv_timing_end(buf, 64)
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms, buf[i].min_ms, buf[i].max_ms)
+            for i in range(min(n, 64))}
 
 
 class DSVAttention(torch.autograd.Function):

@@ -420,15 +420,23 @@ __global__ __launch_bounds__(BQ * 2) void attn_bwd_dq_bf16_kernel(
         dp[t][vv] = p * (dp[t][vv] - my_d);
       }
     }
+    // dQ^T += K^T dS^T with dS split into bf16 hi + lo parts: K's large entries would otherwise
+    // amplify dS's bf16 rounding into dQ errors comparable to dQ's own bf16 storage rounding
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const f32x16& st = dp[cc >> 1];
       const int b0 = (cc & 1) * 8;
-      const bf16x8 db = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
+      const bf16x8 hi = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
                              st[b0 + 7]);
+      const bf16x8 lo = cvt8(st[b0] - (float)hi[0], st[b0 + 1] - (float)hi[1], st[b0 + 2] - (float)hi[2],
+                             st[b0 + 3] - (float)hi[3], st[b0 + 4] - (float)hi[4], st[b0 + 5] - (float)hi[5],
+                             st[b0 + 6] - (float)hi[6], st[b0 + 7] - (float)hi[7]);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = mfma32(as_bf16x8(ld16(&Kts[buf][(dt * 32 + c32) * TS + cc * 16 + g * 8])), db, acc[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const bf16x8 ka = as_bf16x8(ld16(&Kts[buf][(dt * 32 + c32) * TS + cc * 16 + g * 8]));
+        acc[dt] = mfma32(ka, hi, acc[dt]);
+        acc[dt] = mfma32(ka, lo, acc[dt]);
+      }
     }
     if (j + 1 < topk) {
 #pragma unroll

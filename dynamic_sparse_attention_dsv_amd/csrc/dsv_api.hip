@@ -5,7 +5,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/dsv.h"
 #include "kernels.hpp"
@@ -99,7 +101,32 @@ dsv_status hip_status(hipError_t e, const char* where) {
     dsv_status s_ = (x);            \
     if (s_ != DSV_OK) return s_;    \
   } while (0)
-#define TRY_HIP(x, where) TRY(hip_status((x), where))
+
+// Optional per-launch timing (dsv_timing_begin / dsv_timing_end): when enabled on
+// this thread, every launch is bracketed by two HIP events on its stream.
+struct TimingRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimingRec> g_recs;
+
+template <class F>
+dsv_status timed(const char* name, hipStream_t st, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  const bool on = g_timing && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess;
+  if (on) (void)hipEventRecord(a, st);
+  const hipError_t e = launch();
+  if (on) {
+    (void)hipEventRecord(b, st);
+    g_recs.push_back({name, a, b});
+  } else {
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+  }
+  return hip_status(e, name);
+}
+#define TRY_HIP(x, name) TRY(timed(name, st, [&] { return (x); }))
 
 // ---------------------------------------------------------------- workspace layouts
 
@@ -173,6 +200,44 @@ const char* dsv_last_error(void) { return g_err.c_str(); }
 
 int32_t dsv_version(void) { return 100; }
 
+dsv_status dsv_timing_begin(void) {
+  g_err.clear();
+  if (g_timing) return fail(DSV_ERR_INVALID_ARGUMENT, "timing already active on this thread");
+  g_recs.clear();
+  g_timing = true;
+  return DSV_OK;
+}
+
+int32_t dsv_timing_end(dsv_kernel_stat* out, int32_t capacity) {
+  g_timing = false;
+  std::vector<dsv_kernel_stat> agg;
+  for (const TimingRec& r : g_recs) {
+    float ms = 0.f;
+    const bool ok = hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess;
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+    if (!ok) continue;
+    dsv_kernel_stat* a = nullptr;
+    for (auto& x : agg)
+      if (std::strncmp(x.name, r.name, sizeof x.name) == 0) a = &x;
+    if (!a) {
+      agg.push_back({});
+      a = &agg.back();
+      std::strncpy(a->name, r.name, sizeof a->name - 1);
+      a->min_ms = ms;
+      a->max_ms = ms;
+    }
+    a->launches += 1;
+    a->total_ms += ms;
+    a->min_ms = ms < a->min_ms ? ms : a->min_ms;
+    a->max_ms = ms > a->max_ms ? ms : a->max_ms;
+  }
+  g_recs.clear();
+  const int32_t n = (int32_t)agg.size();
+  for (int32_t i = 0; out && i < n && i < capacity; ++i) out[i] = agg[i];
+  return n;
+}
+
 size_t dsv_predict_workspace_size(const dsv_problem* p) {
   Prob o;
   if (to_prob(p, o, true) != DSV_OK) return 0;
@@ -205,20 +270,20 @@ dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const
     uint16_t* qlr = at<uint16_t>(workspace, w.qlr);
     uint16_t* klr = at<uint16_t>(workspace, w.klr);
     TRY_HIP(dsv::launch_proj_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(wq), qlr, o.bh(), o.n,
-                                  o.h, o.d, o.r, st), "projection of q");
+                                  o.h, o.d, o.r, st), "proj_kernel(q)");
     TRY_HIP(dsv::launch_proj_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(wk), klr, o.bh(), o.n,
-                                  o.h, o.d, o.r, st), "projection of k");
+                                  o.h, o.d, o.r, st), "proj_kernel(k)");
     TRY_HIP(dsv::launch_scores_bf16(qlr, klr, at<float>(workspace, w.scratch), block_scores, o.bh(), o.n, o.nkb(),
-                                    o.r, o.bq, o.ps, st), "block scores");
+                                    o.r, o.bq, o.ps, st), "scores_kernel");
   } else {
     float* qlr = at<float>(workspace, w.qlr);
     float* klr = at<float>(workspace, w.klr);
     TRY_HIP(dsv::launch_proj_f32(static_cast<const float*>(q), static_cast<const float*>(wq), qlr, o.bh(), o.n, o.h,
-                                 o.d, o.r, st), "projection of q");
+                                 o.d, o.r, st), "proj_kernel(q)");
     TRY_HIP(dsv::launch_proj_f32(static_cast<const float*>(k), static_cast<const float*>(wk), klr, o.bh(), o.n, o.h,
-                                 o.d, o.r, st), "projection of k");
+                                 o.d, o.r, st), "proj_kernel(k)");
     TRY_HIP(dsv::launch_scores_f32(qlr, klr, at<float>(workspace, w.lse), block_scores, o.bh(), o.n, o.r, o.bq, o.bk,
-                                   o.ps, st), "block scores");
+                                   o.ps, st), "scores_kernel");
   }
   return DSV_OK;
 }
@@ -229,8 +294,8 @@ dsv_status dsv_select_topk(const dsv_problem* p, const float* block_scores, int3
   TRY(to_prob(p, o, false));
   TRY(check_ptr(block_scores, "block_scores", 4));
   TRY(check_ptr(block_idx, "block_idx", 4));
-  TRY_HIP(dsv::launch_select_topk(block_scores, block_idx, o.bh() * o.nqb(), o.nkb(), o.k,
-                                  static_cast<hipStream_t>(stream)), "top-k selection");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY_HIP(dsv::launch_select_topk(block_scores, block_idx, o.bh() * o.nqb(), o.nkb(), o.k, st), "select_topk_kernel");
   return DSV_OK;
 }
 
@@ -263,14 +328,14 @@ dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (o.dtype == DSV_BF16) {
     uint16_t* vt = at<uint16_t>(workspace, 0);
-    TRY_HIP(dsv::launch_transpose_bf16(static_cast<const uint16_t*>(v), vt, o.bh(), o.n, o.d, st), "transpose of v");
+    TRY_HIP(dsv::launch_transpose_bf16(static_cast<const uint16_t*>(v), vt, o.bh(), o.n, o.d, st), "transpose_kernel(v)");
     TRY_HIP(dsv::launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, block_idx,
                                       static_cast<uint16_t*>(o_ptr), lse, o.bh(), o.n, o.d, o.bq, o.k, o.sm, st),
-            "sparse attention forward");
+            "attn_fwd_kernel");
   } else {
     TRY_HIP(dsv::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                      static_cast<const float*>(v), block_idx, static_cast<float*>(o_ptr), lse, o.bh(),
-                                     o.n, o.d, o.bq, o.bk, o.k, o.sm, st), "sparse attention forward");
+                                     o.n, o.d, o.bq, o.bk, o.k, o.sm, st), "attn_fwd_kernel");
   }
   return DSV_OK;
 }
@@ -301,7 +366,7 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
   int32_t* col_ptr = at<int32_t>(workspace, w.col_ptr);
   int32_t* rows = at<int32_t>(workspace, w.rows);
   TRY_HIP(dsv::launch_csc(block_idx, at<uint32_t>(workspace, w.bitmap), at<int32_t>(workspace, w.counts), col_ptr,
-                          rows, o.bh(), o.nqb(), o.nkb(), o.k, st), "block-list transpose");
+                          rows, o.bh(), o.nqb(), o.nkb(), o.k, st), "csc_kernels");
   float* dvec = at<float>(workspace, w.dvec);
   if (o.dtype == DSV_BF16) {
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
@@ -312,23 +377,23 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
     uint16_t* dot = at<uint16_t>(workspace, w.dot);
     uint16_t* kt = at<uint16_t>(workspace, w.kt);
     float* lse2 = at<float>(workspace, w.lse2);
-    TRY_HIP(dsv::launch_transpose_bf16(q16, qt, o.bh(), o.n, o.d, st), "transpose of q");
-    TRY_HIP(dsv::launch_transpose_bf16(do16, dot, o.bh(), o.n, o.d, st), "transpose of dout");
-    TRY_HIP(dsv::launch_transpose_bf16(k16, kt, o.bh(), o.n, o.d, st), "transpose of k");
+    TRY_HIP(dsv::launch_transpose_bf16(q16, qt, o.bh(), o.n, o.d, st), "transpose_kernel(q)");
+    TRY_HIP(dsv::launch_transpose_bf16(do16, dot, o.bh(), o.n, o.d, st), "transpose_kernel(dout)");
+    TRY_HIP(dsv::launch_transpose_bf16(k16, kt, o.bh(), o.n, o.d, st), "transpose_kernel(k)");
     TRY_HIP(dsv::launch_bwd_pre_bf16(static_cast<const uint16_t*>(o_ptr), do16, lse, dvec, lse2, o.bh() * o.n, o.d,
-                                     st), "backward preprocess");
+                                     st), "bwd_pre_kernel");
     TRY_HIP(dsv::launch_bwd_dkdv_bf16(q16, qt, k16, v16, do16, dot, lse2, dvec, col_ptr, rows,
                                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), o.bh(), o.n, o.d, o.bq,
-                                      o.k, o.sm, st), "backward dK/dV");
+                                      o.k, o.sm, st), "attn_bwd_dkdv_kernel");
     TRY_HIP(dsv::launch_bwd_dq_bf16(q16, k16, kt, v16, do16, lse2, dvec, block_idx, static_cast<uint16_t*>(dq), o.bh(),
-                                    o.n, o.d, o.bq, o.k, o.sm, st), "backward dQ");
+                                    o.n, o.d, o.bq, o.k, o.sm, st), "attn_bwd_dq_kernel");
   } else {
     TRY_HIP(dsv::launch_bwd_pre_f32(static_cast<const float*>(o_ptr), static_cast<const float*>(dout), dvec,
-                                    o.bh() * o.n, o.d, st), "backward preprocess");
+                                    o.bh() * o.n, o.d, st), "bwd_pre_kernel");
     TRY_HIP(dsv::launch_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
                                 static_cast<const float*>(dout), lse, dvec, block_idx, col_ptr, rows,
                                 static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), o.bh(), o.n,
-                                o.d, o.bq, o.bk, o.k, o.sm, st), "backward");
+                                o.d, o.bq, o.bk, o.k, o.sm, st), "attn_bwd_f32_kernels");
   }
   return DSV_OK;
 }

@@ -36,8 +36,9 @@
  *   describes the problem (thread-local string, valid until the next call on the
  *   same thread).  A failed launch returns DSV_ERR_HIP.  Non-finite inputs are
  *   not checked: they propagate into the outputs.
- * State.  The library has no global mutable state; calls are thread-safe and may
- *   run concurrently on different streams with different buffers.  All calls are
+ * State.  The library has no global mutable state (only the optional per-thread
+ *   timing record below); calls are thread-safe and may run concurrently on
+ *   different streams with different buffers.  All calls are
  *   deterministic (bitwise repeatable for the same inputs and problem).
  */
 #ifndef DSV_H_
@@ -190,6 +191,26 @@ const char* dsv_last_error(void);
 
 /* Library version, major*10000 + minor*100 + patch. */
 int32_t dsv_version(void);
+
+/*
+ * Kernel timing (diagnostics).  dsv_timing_begin() makes every kernel launch the
+ * library issues from the calling thread be bracketed by two HIP events on the
+ * launch's stream (a few microseconds of host overhead per launch; the GPU work
+ * is unchanged).  dsv_timing_end() waits for those events, aggregates the
+ * elapsed times by kernel name into `out` (at most `capacity` entries, in order
+ * of first launch), frees the events, stops timing, and returns the number of
+ * distinct names.  The only per-thread state of the library is this record.
+ */
+typedef struct {
+  char name[64];
+  int32_t launches;
+  double total_ms;
+  float min_ms;
+  float max_ms;
+} dsv_kernel_stat;
+
+dsv_status dsv_timing_begin(void);
+int32_t dsv_timing_end(dsv_kernel_stat* out, int32_t capacity);
 
 #ifdef __cplusplus
 }

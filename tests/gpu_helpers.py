@@ -64,6 +64,12 @@ def check_indices(gpu_idx: np.ndarray, oracle_scores: np.ndarray, k: int):
     return float(exact.mean())
 
 
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 numbers at |x| (8 significant bits; fixed 2^-133 below 2^-126)."""
+    e = np.frexp(np.abs(x))[1]
+    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+
+
 def seeded_idx(seed: int, shape_bh, nqb: int, nkb: int, k: int) -> np.ndarray:
     """Random ascending, duplicate-free block lists (an input, drawn from a seeded generator)."""
     rng = np.random.default_rng(seed)
