@@ -1,6 +1,6 @@
-// Block-sparse attention backward, plus the small helper kernels of the path
-// (layout transposes, the D = rowsum(dO o O) preprocess, and the transpose of
-// the block lists from "query block -> KV blocks" to "KV block -> query blocks").
+// Block-sparse attention backward, plus its small helper kernels (the
+// D = rowsum(dO o O) preprocess, and the transpose of the block lists from
+// "query block -> KV blocks" to "KV block -> query blocks").
 //
 // Method: the DSV pages ("DSV: Exploiting Dynamic Sparsity to Accelerate
 // Large-Scale Video DiT Training", gist.science/de technical summary §2.A,
@@ -16,40 +16,16 @@
 //    accumulated in registers -- no atomics, deterministic;
 //  * dQ: one workgroup per query block walks its own k blocks (recomputing P and
 //    dP), accumulating dQ in registers -- again no atomics;
-//  * every GEMM is a v_mfma 32x32x16 bf16 whose operands come from LDS tiles in
-//    the layout the operand needs; operands that contract over the query (or
-//    key) index read transposed copies of Q, dO and K made once per call.
+//  * every GEMM is a v_mfma 32x32x16 bf16; operands that contract along a row
+//    of a gathered tile are plain LDS reads, operands that contract down its
+//    columns come from transposing LDS reads (ds_read_b64_tr_b16) of the same
+//    row-major tile, so no transposed copy of any tensor is made.
 #include "common.hpp"
 #include "kernels.hpp"
 
 #include <algorithm>
 
 namespace dsv {
-
-// ---------------------------------------------------------------- transpose [BH, N, D] -> [BH, D, N]
-
-template <int D>
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
-                                                             uint16_t* __restrict__ out, int n) {
-  constexpr int TS = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t t[64 * TS];
-  const int bh = blockIdx.y, r0 = blockIdx.x * 64;
-  const uint16_t* src = in + ((size_t)bh * n + r0) * D;
-  for (int ch = threadIdx.x; ch < 64 * D / 8; ch += 256) {
-    const int row = ch / (D / 8), c8 = ch % (D / 8);
-    st16(&t[row * TS + c8 * 8], ld16(src + (size_t)row * D + c8 * 8));
-  }
-  __syncthreads();
-  uint16_t* dst = out + (size_t)bh * D * n + r0;
-  for (int ch = threadIdx.x; ch < D * 8; ch += 256) {
-    const int d = ch / 8, c8 = ch % 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)t[(c8 * 8 + 2 * e) * TS + d] | ((uint32_t)t[(c8 * 8 + 2 * e + 1) * TS + d] << 16);
-    st16(dst + (size_t)d * n + c8 * 8, u32x4{w[0], w[1], w[2], w[3]});
-  }
-}
 
 // ---------------------------------------------------------------- D = rowsum(dO o O), lse2 = lse * log2(e)
 
@@ -124,6 +100,38 @@ __global__ __launch_bounds__(256) void csc_count_kernel(const uint32_t* __restri
   if (lane == 0) counts[col] = c;
 }
 
+// one workgroup of 1024 threads per bh: the KV blocks of the head sorted by
+// descending column length (ties: ascending block index), by a bitonic sort of
+// unique keys ((nqb - count) << 12 | kb) in LDS.  The dK/dV kernel visits blocks
+// in this order: the longest columns start first (load balance) and blocks
+// that most query blocks selected run side by side, sharing Q/dO tiles in L2.
+__global__ __launch_bounds__(1024) void csc_order_kernel(const int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ order, int nkb, int nqb) {
+  __shared__ uint32_t key[4096];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  int p2 = 1;
+  while (p2 < nkb) p2 <<= 1;
+  for (int i = tid; i < p2; i += 1024)
+    key[i] = i < nkb ? ((uint32_t)(nqb - counts[(size_t)bh * nkb + i]) << 12) | (uint32_t)i : 0xffffffffu;
+  __syncthreads();
+  for (int size = 2; size <= p2; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < p2; i += 1024) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const uint32_t a = key[i], b = key[j];
+          if ((a > b) == up) {
+            key[i] = b;
+            key[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = tid; i < nkb; i += 1024) order[(size_t)bh * nkb + i] = (int32_t)(key[i] & 0xfffu);
+}
+
 // one workgroup of 1024 threads per bh: exclusive scan of counts[nkb] -> col_ptr[nkb + 1]
 __global__ __launch_bounds__(1024) void csc_scan_kernel(const int32_t* __restrict__ counts,
                                                         int32_t* __restrict__ col_ptr, int nkb) {
@@ -189,33 +197,41 @@ __global__ __launch_bounds__(256) void csc_emit_kernel(const uint32_t* __restric
 }
 
 // ---------------------------------------------------------------- dK, dV (bf16, MFMA)
+//
+// One workgroup (4 waves) per KV block, in the per-head order of csc_order_kernel.
+// Wave w owns keys (w % 2) * 32 .. +32 of the block and the query half (w / 2)
+// of every 64-row chunk of the query blocks that selected the block.  K^T and
+// V^T fragments stay in registers; Q and dO chunks are gathered into swizzled
+// LDS tiles (double-buffered) and read both row-wise (A operands of S = Q K^T
+// and dP = dO V^T) and transposed (B operands of dV += P^T dO, dK += dS^T Q).
+// The two query halves' partial dK/dV are summed through LDS at the end.
 
 template <int D, int BQ>
-__global__ __launch_bounds__(128) void attn_bwd_dkdv_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ dot,
-    const float* __restrict__ lse2, const float* __restrict__ dvec, const int32_t* __restrict__ col_ptr,
-    const int32_t* __restrict__ rows, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int n, int nnz_per_bh,
-    int nwg, float c /* sm_scale*log2e */, float sm_scale) {
-  constexpr int RS = D + 8;   // row-major chunk tiles [32][D]
-  constexpr int TS = 32 + 8;  // transposed chunk tiles [D][32]
-  constexpr int RCH = 32 * D / 8, TCH = D * 4;  // 16-byte chunks per tile
-  constexpr int CH = 2 * (RCH + TCH) / 128;
-  constexpr int SUBS = BQ / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[2][32 * RS];  // dO rows
-  __shared__ __attribute__((aligned(16))) uint16_t Qts[2][D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Ots[2][D * TS];  // dO^T
-  __shared__ __attribute__((aligned(16))) float Ls[2][32];
-  __shared__ __attribute__((aligned(16))) float Dsh[2][32];
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dvec,
+    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ rows, const int32_t* __restrict__ order,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int n, int nnz_per_bh, int nwg,
+    float c /* sm_scale*log2e */, float sm_scale) {
+  constexpr int QR = 64;             // query rows per chunk
+  constexpr int TCH = QR * D / 8;    // 16-byte chunks per tile
+  constexpr int CH = 2 * TCH / 256;  // per thread per chunk (Q and dO tiles)
+  constexpr int SUBS = BQ / QR;
+  static_assert(BQ % QR == 0, "query block must be a multiple of 64 rows");
+  static_assert((D / 32) * 16 * 64 * 4 * 4 <= 4 * QR * D * 2, "reduction buffer must fit the tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QR * D];  // Q[2], dO[2]
+  __shared__ __attribute__((aligned(16))) float Ls[2][QR];
+  __shared__ __attribute__((aligned(16))) float Dsh[2][QR];
 
   const int nkb = n / 64;
   const int id = xcd_remap(blockIdx.x, nwg);
-  const int bh = id / nkb, kb = id % nkb;
+  const int bh = id / nkb;
+  const int kb = order[(size_t)bh * nkb + id % nkb];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c32 = lane & 31;
+  const int kh = wave & 1, qh = wave >> 1;
   const size_t head = (size_t)bh * n * D;
-  const int key = kb * 64 + wave * 32 + c32;  // this lane's key (column of S)
+  const int key = kb * 64 + kh * 32 + c32;  // this lane's key (column of S)
 
   const int32_t* cp = col_ptr + (size_t)bh * (nkb + 1);
   const int start = cp[kb], cnt = cp[kb + 1] - start;
@@ -224,6 +240,9 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_bf16_kernel(
   f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) { dka[dt] = f32x16{}; dva[dt] = f32x16{}; }
+
+  auto qtile = [&](int buf) { return smem + buf * QR * D; };
+  auto otile = [&](int buf) { return smem + (2 + buf) * QR * D; };
 
   if (cnt > 0) {
     // K^T and V^T as B operands: lane holds its key, 8 consecutive d per chunk
@@ -234,64 +253,55 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_bf16_kernel(
       vf[dc] = as_bf16x8(ld16(v + head + (size_t)key * D + dc * 16 + g * 8));
     }
     const int nch = cnt * SUBS;
-    auto q0_of = [&](int j) { return list[j / SUBS] * BQ + (j % SUBS) * 32; };
+    auto q0_of = [&](int j) { return list[j / SUBS] * BQ + (j % SUBS) * QR; };
     auto gsrc = [&](int q0, int ch) -> const uint16_t* {
-      const int tsel = ch / (RCH + TCH) ;  // 0: Q family, 1: dO family
-      int r = ch % (RCH + TCH);
-      if (r < RCH) return (tsel ? dout : q) + head + (size_t)(q0 + r / (D / 8)) * D + (r % (D / 8)) * 8;
-      r -= RCH;
-      return (tsel ? dot : qt) + head + (size_t)(r / 4) * n + q0 + (r % 4) * 8;
+      const int t = ch % TCH;
+      return (ch < TCH ? q : dout) + head + (size_t)(q0 + t / (D / 8)) * D + (t % (D / 8)) * 8;
     };
     auto ldst = [&](int buf, int ch) -> uint16_t* {
-      const int tsel = ch / (RCH + TCH);
-      int r = ch % (RCH + TCH);
-      if (r < RCH) return &(tsel ? Os : Qs)[buf][(r / (D / 8)) * RS + (r % (D / 8)) * 8];
-      r -= RCH;
-      return &(tsel ? Ots : Qts)[buf][(r / 4) * TS + (r % 4) * 8];
+      const int t = ch % TCH;
+      return (ch < TCH ? qtile(buf) : otile(buf)) + toff<D>(t / (D / 8), (t % (D / 8)) * 8);
     };
     u32x4 stage[CH];
     u32x4 small = {};
-    auto load_small = [&](int q0) {  // threads 0..15: lse2 (8 chunks) and D (8 chunks)
-      if (threadIdx.x < 16) {
-        const float* s = (threadIdx.x < 8 ? lse2 : dvec) + (size_t)bh * n + q0 + (threadIdx.x % 8) * 4;
-        small = ld16(s);
-      }
+    auto load_small = [&](int q0) {  // threads 0..31: lse2 (16 chunks) and D (16 chunks)
+      if (threadIdx.x < 32) small = ld16((threadIdx.x < 16 ? lse2 : dvec) + (size_t)bh * n + q0 + (threadIdx.x % 16) * 4);
     };
     auto store_small = [&](int buf) {
-      if (threadIdx.x < 16) st16(&(threadIdx.x < 8 ? Ls : Dsh)[buf][(threadIdx.x % 8) * 4], small);
+      if (threadIdx.x < 32) st16(&(threadIdx.x < 16 ? Ls : Dsh)[buf][(threadIdx.x % 16) * 4], small);
     };
     {
       const int q0 = q0_of(0);
 #pragma unroll
-      for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(q0, threadIdx.x + i * 128));
+      for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(q0, threadIdx.x + i * 256));
       load_small(q0);
 #pragma unroll
-      for (int i = 0; i < CH; ++i) st16(ldst(0, threadIdx.x + i * 128), stage[i]);
+      for (int i = 0; i < CH; ++i) st16(ldst(0, threadIdx.x + i * 256), stage[i]);
       store_small(0);
     }
     __syncthreads();
-    const int arow = sigma(c32);
+    const int arow = qh * 32 + sigma(c32);
     for (int j = 0; j < nch; ++j) {
       const int buf = j & 1;
       if (j + 1 < nch) {
         const int q0 = q0_of(j + 1);
 #pragma unroll
-        for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(q0, threadIdx.x + i * 128));
+        for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(q0, threadIdx.x + i * 256));
         load_small(q0);
       }
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys (A rows in sigma order)
+      const uint16_t* qs = qtile(buf);
+      const uint16_t* os = otile(buf);
+      // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys (A rows in sigma order)
       f32x16 s = f32x16{}, dp = f32x16{};
-      const uint16_t* qa = &Qs[buf][arow * RS + g * 8];
-      const uint16_t* oa = &Os[buf][arow * RS + g * 8];
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        s = mfma32(as_bf16x8(ld16(qa + dc * 16)), kf[dc], s);
-        dp = mfma32(as_bf16x8(ld16(oa + dc * 16)), vf[dc], dp);
+        s = mfma32(row_frag<D>(qs, arow, dc * 16, lane), kf[dc], s);
+        dp = mfma32(row_frag<D>(os, arow, dc * 16, lane), vf[dc], dp);
       }
-      // register v holds query (v/8)*16 + g*8 + v%8 of the chunk
+      // register vv holds query qh*32 + (vv/8)*16 + g*8 + vv%8 of the chunk
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        const int qi = (vv >> 3) * 16 + g * 8 + (vv & 7);
+        const int qi = qh * 32 + (vv >> 3) * 16 + g * 8 + (vv & 7);
         const float p = fast_exp2(fmaf(s[vv], c, -Ls[buf][qi]));
         s[vv] = p;
         dp[vv] = p * (dp[vv] - Dsh[buf][qi]);
@@ -304,46 +314,62 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_bf16_kernel(
                                dp[b0 + 7]);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          dva[dt] = mfma32(pa, as_bf16x8(ld16(&Ots[buf][(dt * 32 + c32) * TS + cc * 16 + g * 8])), dva[dt]);
-          dka[dt] = mfma32(da, as_bf16x8(ld16(&Qts[buf][(dt * 32 + c32) * TS + cc * 16 + g * 8])), dka[dt]);
+          dva[dt] = mfma32(pa, tr_frag<D>(os, qh * 32 + cc * 16, dt * 32, lane), dva[dt]);
+          dka[dt] = mfma32(da, tr_frag<D>(qs, qh * 32 + cc * 16, dt * 32, lane), dka[dt]);
         }
       }
       if (j + 1 < nch) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i) st16(ldst(buf ^ 1, threadIdx.x + i * 128), stage[i]);
+        for (int i = 0; i < CH; ++i) st16(ldst(buf ^ 1, threadIdx.x + i * 256), stage[i]);
         store_small(buf ^ 1);
       }
       __syncthreads();
     }
   }
-  // D layout of dK/dV tiles: lane holds d = dt*32 + c32; register v holds key (v/4)*8 + g*4 + v%4
+  // sum the two query halves through LDS (the tiles are free after the last barrier)
+  float* red = reinterpret_cast<float*>(smem);
+  auto ridx = [&](int which, int dt, int vv) { return (((kh * 2 + which) * (D / 32) + dt) * 16 + vv) * 64 + lane; };
+  if (qh == 1) {
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int vv = 0; vv < 16; ++vv) {
-      const int kr = kb * 64 + wave * 32 + (vv >> 2) * 8 + g * 4 + (vv & 3);
-      const size_t off = head + (size_t)kr * D + dt * 32 + c32;
-      dk[off] = f32_to_bf16(dka[dt][vv] * sm_scale);
-      dv[off] = f32_to_bf16(dva[dt][vv]);
-    }
+      for (int vv = 0; vv < 16; ++vv) {
+        red[ridx(0, dt, vv)] = dka[dt][vv];
+        red[ridx(1, dt, vv)] = dva[dt][vv];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+    // D layout of dK/dV tiles: lane holds d = dt*32 + c32; register vv holds key (vv/4)*8 + g*4 + vv%4
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int kr = kb * 64 + kh * 32 + (vv >> 2) * 8 + g * 4 + (vv & 3);
+        const size_t off = head + (size_t)kr * D + dt * 32 + c32;
+        dk[off] = f32_to_bf16((dka[dt][vv] + red[ridx(0, dt, vv)]) * sm_scale);
+        dv[off] = f32_to_bf16(dva[dt][vv] + red[ridx(1, dt, vv)]);
+      }
+  }
 }
 
 // ---------------------------------------------------------------- dQ (bf16, MFMA)
+//
+// One workgroup per query block (Bq/32 waves, 32 rows each) walking its k
+// selected blocks: S^T = K Q^T and dP^T = V dO^T are recomputed, and
+// dQ^T += K^T dS^T takes K^T from transposing reads of the row-major K tile.
 
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2) void attn_bwd_dq_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kt,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
-    const float* __restrict__ dvec, const int32_t* __restrict__ idx, uint16_t* __restrict__ dq, int n, int topk,
-    int nwg, float c, float sm_scale) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dvec,
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ dq, int n, int topk, int nwg, float c, float sm_scale) {
   constexpr int THREADS = BQ * 2;
-  constexpr int RS = D + 8, TS = 64 + 8;
-  constexpr int RCH = 64 * D / 8, TCH = D * 8;
-  constexpr int CH = (2 * RCH + TCH) / THREADS;
-  static_assert((2 * RCH + TCH) % THREADS == 0, "staging must divide evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kts[2][D * TS];
+  constexpr int TCH = 64 * D / 8;
+  constexpr int CH = 2 * TCH / THREADS;
+  static_assert((2 * TCH) % THREADS == 0, "staging must divide evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * D];
 
   const int nqb = n / BQ;
   const int id = xcd_remap(blockIdx.x, nwg);
@@ -357,20 +383,12 @@ __global__ __launch_bounds__(BQ * 2) void attn_bwd_dq_bf16_kernel(
   auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };  // clamp out-of-range indices
 
   auto gsrc = [&](int blk, int ch) -> const uint16_t* {
-    if (ch < 2 * RCH) {
-      const int r = ch % RCH;
-      return (ch < RCH ? k : v) + head + (size_t)(blk * 64 + r / (D / 8)) * D + (r % (D / 8)) * 8;
-    }
-    const int r = ch - 2 * RCH;
-    return kt + head + (size_t)(r / 8) * n + blk * 64 + (r % 8) * 8;
+    const int t = ch % TCH;
+    return (ch < TCH ? k : v) + head + (size_t)(blk * 64 + t / (D / 8)) * D + (t % (D / 8)) * 8;
   };
   auto ldst = [&](int buf, int ch) -> uint16_t* {
-    if (ch < 2 * RCH) {
-      const int r = ch % RCH;
-      return &(ch < RCH ? Ks : Vs)[buf][(r / (D / 8)) * RS + (r % (D / 8)) * 8];
-    }
-    const int r = ch - 2 * RCH;
-    return &Kts[buf][(r / 8) * TS + (r % 8) * 8];
+    const int t = ch % TCH;
+    return (ch < TCH ? Ks[buf] : Vs[buf]) + toff<D>(t / (D / 8), (t % (D / 8)) * 8);
   };
 
   bf16x8 qf[D / 16], of[D / 16];
@@ -407,12 +425,10 @@ __global__ __launch_bounds__(BQ * 2) void attn_bwd_dq_bf16_kernel(
     for (int t = 0; t < 2; ++t) {
       s[t] = f32x16{};
       dp[t] = f32x16{};
-      const uint16_t* ka = &Ks[buf][(t * 32 + arow) * RS + g * 8];
-      const uint16_t* va = &Vs[buf][(t * 32 + arow) * RS + g * 8];
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        s[t] = mfma32(as_bf16x8(ld16(ka + dc * 16)), qf[dc], s[t]);
-        dp[t] = mfma32(as_bf16x8(ld16(va + dc * 16)), of[dc], dp[t]);
+        s[t] = mfma32(row_frag<D>(Ks[buf], t * 32 + arow, dc * 16, lane), qf[dc], s[t]);
+        dp[t] = mfma32(row_frag<D>(Vs[buf], t * 32 + arow, dc * 16, lane), of[dc], dp[t]);
       }
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
@@ -433,7 +449,7 @@ __global__ __launch_bounds__(BQ * 2) void attn_bwd_dq_bf16_kernel(
                              st[b0 + 6] - (float)hi[6], st[b0 + 7] - (float)hi[7]);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16x8 ka = as_bf16x8(ld16(&Kts[buf][(dt * 32 + c32) * TS + cc * 16 + g * 8]));
+        const bf16x8 ka = tr_frag<D>(Ks[buf], cc * 16, dt * 32, lane);
         acc[dt] = mfma32(ka, hi, acc[dt]);
         acc[dt] = mfma32(ka, lo, acc[dt]);
       }
@@ -530,14 +546,6 @@ __global__ void attn_bwd_dkdv_f32_kernel(const float* __restrict__ q, const floa
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_transpose_bf16(const uint16_t* in, uint16_t* out, int bh, int n, int d, hipStream_t st) {
-  dim3 grid(n / 64, bh);
-  if (d == 64) hipLaunchKernelGGL(transpose_bf16_kernel<64>, grid, dim3(256), 0, st, in, out, n);
-  else if (d == 128) hipLaunchKernelGGL(transpose_bf16_kernel<128>, grid, dim3(256), 0, st, in, out, n);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
 hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* dout, const float* lse, float* dvec, float* lse2,
                                int rows, int d, hipStream_t st) {
   const int lanes = rows * (d / 8);
@@ -555,7 +563,7 @@ hipError_t launch_bwd_pre_f32(const float* o, const float* dout, float* dvec, in
 }
 
 hipError_t launch_csc(const int32_t* idx, uint32_t* bitmap, int32_t* counts, int32_t* col_ptr, int32_t* rows,
-                      int bh, int nqb, int nkb, int topk, hipStream_t st) {
+                      int32_t* order, int bh, int nqb, int nkb, int topk, hipStream_t st) {
   const int words = (nqb + 31) / 32;
   const size_t nbits = (size_t)bh * nkb * words;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<size_t>((nbits + 255) / 256, 65535)), dim3(256), 0,
@@ -571,39 +579,43 @@ hipError_t launch_csc(const int32_t* idx, uint32_t* bitmap, int32_t* counts, int
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(csc_scan_kernel, dim3(bh), dim3(1024), 0, st, counts, col_ptr, nkb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (order) {
+    hipLaunchKernelGGL(csc_order_kernel, dim3(bh), dim3(1024), 0, st, counts, order, nkb, nqb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(csc_emit_kernel, dim3((cols + 3) / 4), dim3(256), 0, st, bitmap, col_ptr, rows, cols, nkb,
                      words, nqb * topk);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* qt, const uint16_t* k, const uint16_t* v,
-                                const uint16_t* dout, const uint16_t* dot, const float* lse2, const float* dvec,
-                                const int32_t* col_ptr, const int32_t* rows, uint16_t* dk, uint16_t* dv, int bh,
-                                int n, int d, int bq, int topk, float sm_scale, hipStream_t st) {
+hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                                const float* lse2, const float* dvec, const int32_t* col_ptr, const int32_t* rows,
+                                const int32_t* order, uint16_t* dk, uint16_t* dv, int bh, int n, int d, int bq,
+                                int topk, float sm_scale, hipStream_t st) {
   const int nwg = bh * (n / 64);
   const int nnz = (n / bq) * topk;
   const float c = sm_scale * kLog2e;
-#define DKDV(D_, BQ_)                                                                                      \
-  if (d == D_ && bq == BQ_) {                                                                              \
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(128), 0, st, q, qt, k, v, dout, \
-                       dot, lse2, dvec, col_ptr, rows, dk, dv, n, nnz, nwg, c, sm_scale);                  \
-    return hipGetLastError();                                                                              \
+#define DKDV(D_, BQ_)                                                                                       \
+  if (d == D_ && bq == BQ_) {                                                                               \
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(256), 0, st, q, k, v, dout, lse2, \
+                       dvec, col_ptr, rows, order, dk, dv, n, nnz, nwg, c, sm_scale);                       \
+    return hipGetLastError();                                                                               \
   }
   DKDV(64, 64) DKDV(64, 128) DKDV(128, 64) DKDV(128, 128)
 #undef DKDV
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* kt, const uint16_t* v,
-                              const uint16_t* dout, const float* lse2, const float* dvec, const int32_t* idx,
-                              uint16_t* dq, int bh, int n, int d, int bq, int topk, float sm_scale, hipStream_t st) {
+hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                              const float* lse2, const float* dvec, const int32_t* idx, uint16_t* dq, int bh, int n,
+                              int d, int bq, int topk, float sm_scale, hipStream_t st) {
   const int nwg = bh * (n / bq);
   const float c = sm_scale * kLog2e;
-#define DQ(D_, BQ_)                                                                                         \
-  if (d == D_ && bq == BQ_) {                                                                               \
-    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, kt, v, dout, \
-                       lse2, dvec, idx, dq, n, topk, nwg, c, sm_scale);                                     \
-    return hipGetLastError();                                                                               \
+#define DQ(D_, BQ_)                                                                                          \
+  if (d == D_ && bq == BQ_) {                                                                                \
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, dout, lse2, \
+                       dvec, idx, dq, n, topk, nwg, c, sm_scale);                                            \
+    return hipGetLastError();                                                                                \
   }
   DQ(64, 64) DQ(64, 128) DQ(128, 64) DQ(128, 128)
 #undef DQ

@@ -10,9 +10,10 @@
 //  * one workgroup per (b, h, qb), Bq/32 waves, each wave owns 32 query rows;
 //    workgroup ids are remapped so that one XCD works on one head at a time;
 //  * Q stays in registers as the B operand of S^T = K Q^T (v_mfma 32x32x16);
-//  * each selected KV block is gathered into LDS (K row-major, V^T from a
-//    transposed copy of V) with double buffering: the next block's global loads
-//    are in flight while the current block is computed;
+//  * each selected KV block is gathered into swizzled LDS tiles (K and V both
+//    row-major, as stored) with double buffering: the next block's global loads
+//    are in flight while the current block is computed; the V^T operand of
+//    O^T += V^T P^T comes from transposing LDS reads (ds_read_b64_tr_b16);
 //  * S^T's D layout puts one query per lane, so the online-softmax row max and
 //    row sum are lane-local plus one exchange with lane ^ 32; K rows are loaded
 //    in the sigma order so that P^T feeds O^T += V^T P^T directly from registers.
@@ -23,17 +24,15 @@ namespace dsv {
 
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse, int n, int topk,
     int nwg, float c /* sm_scale * log2(e) */) {
-  constexpr int THREADS = BQ * 2;  // (BQ / 32) waves of 64
-  constexpr int KS = D + 8;        // padded row (elements) of the K tile
-  constexpr int VS = 64 + 8;       // padded row of the V^T tile
-  constexpr int KCH = 64 * D / 8;  // 16-byte chunks of the K tile
-  constexpr int CH = (KCH + D * 8) / THREADS;
-  static_assert((KCH + D * 8) % THREADS == 0, "staging must divide evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VS];
+  constexpr int THREADS = BQ * 2;        // (BQ / 32) waves of 64
+  constexpr int TCH = 64 * D / 8;        // 16-byte chunks of one 64 x D tile
+  constexpr int CH = 2 * TCH / THREADS;  // chunks staged per thread (K and V tiles)
+  static_assert((2 * TCH) % THREADS == 0, "staging must divide evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * D];
 
   const int nqb = n / BQ;
   const int id = xcd_remap(blockIdx.x, nwg);
@@ -46,19 +45,17 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
   // out-of-range block indices are clamped: wrong results, but no access outside the tensors
   auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };
 
-  // staging helpers: chunk ch -> (global source, LDS destination)
+  // staging: chunk ch < TCH is K (row ch / (D/8)), otherwise V; both row-major in memory
   auto gsrc = [&](int blk, int ch) -> const uint16_t* {
-    if (ch < KCH) return k + head + (size_t)(blk * 64 + ch / (D / 8)) * D + (ch % (D / 8)) * 8;
-    const int c2 = ch - KCH;
-    return vt + head + (size_t)(c2 / 8) * n + blk * 64 + (c2 % 8) * 8;
+    const int t = ch % TCH;
+    return (ch < TCH ? k : v) + head + (size_t)(blk * 64 + t / (D / 8)) * D + (t % (D / 8)) * 8;
   };
   auto ldst = [&](int buf, int ch) -> uint16_t* {
-    if (ch < KCH) return &Ks[buf][(ch / (D / 8)) * KS + (ch % (D / 8)) * 8];
-    const int c2 = ch - KCH;
-    return &Vs[buf][(c2 / 8) * VS + (c2 % 8) * 8];
+    const int t = ch % TCH;
+    return (ch < TCH ? Ks[buf] : Vs[buf]) + toff<D>(t / (D / 8), (t % (D / 8)) * 8);
   };
 
-  // Q^T as the B operand: lane holds its query row, 8 consecutive d per 16-wide chunk
+  // Q^T as the B operand of S^T = K Q^T: lane holds its query row, 8 consecutive d per 16-wide chunk
   const int qrow = qb * BQ + wave * 32 + c32;
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -87,21 +84,20 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(blk, threadIdx.x + i * THREADS));
     }
-    // S^T = K Q^T: two 32-key tiles, rows loaded in sigma order
+    // S^T = K Q^T: two 32-key tiles, K rows read in sigma order
     f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = f32x16{};
-      const uint16_t* kr = &Ks[buf][(t * 32 + arow) * KS + g * 8];
 #pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) s[t] = mfma32(as_bf16x8(ld16(kr + dc * 16)), qf[dc], s[t]);
+      for (int dc = 0; dc < D / 16; ++dc) s[t] = mfma32(row_frag<D>(Ks[buf], t * 32 + arow, dc * 16, lane), qf[dc], s[t]);
     }
     // online softmax (log2 domain); lane owns one query, 32 of the block's 64 keys
     float mx = s[0][0];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
+    for (int vv = 1; vv < 16; ++vv) mx = fmaxf(mx, s[0][vv]);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[1][v]);
+    for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[1][vv]);
     mx = fmaxf(mx, xor32(mx));
     const float m_new = fmaxf(m_run, mx * c);
     const float alpha = fast_exp2(m_run - m_new);
@@ -110,14 +106,15 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s[t][v] = fast_exp2(fmaf(s[t][v], c, -m_new));
-        psum += s[t][v];
+      for (int vv = 0; vv < 16; ++vv) {
+        s[t][vv] = fast_exp2(fmaf(s[t][vv], c, -m_new));
+        psum += s[t][vv];
       }
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-    // O^T += V^T P^T: P^T chunk cc = registers (cc%2)*8.. of tile cc/2
+    // O^T += V^T P^T: V^T operands by transposed reads of the row-major V tile;
+    // P^T chunk cc = registers (cc%2)*8.. of tile cc/2
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const f32x16& st = s[cc >> 1];
@@ -125,8 +122,7 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
       const bf16x8 pb = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
                              st[b0 + 7]);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        oacc[dt] = mfma32(as_bf16x8(ld16(&Vs[buf][(dt * 32 + c32) * VS + cc * 16 + g * 8])), pb, oacc[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(tr_frag<D>(Vs[buf], cc * 16, dt * 32, lane), pb, oacc[dt]);
     }
     if (j + 1 < topk) {
 #pragma unroll
@@ -190,14 +186,14 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restric
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt, const int32_t* idx,
+hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
                                 uint16_t* o, float* lse, int bh, int n, int d, int bq, int topk, float sm_scale,
                                 hipStream_t st) {
   const int nwg = bh * (n / bq);
   const float c = sm_scale * kLog2e;
 #define FWD(D_, BQ_)                                                                                      \
   if (d == D_ && bq == BQ_) {                                                                             \
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, vt, idx, o, \
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, idx, o,  \
                        lse, n, topk, nwg, c);                                                             \
     return hipGetLastError();                                                                             \
   }

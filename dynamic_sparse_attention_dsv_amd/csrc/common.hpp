@@ -83,6 +83,56 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// ---------------------------------------------------------------- LDS tiles
+//
+// A tile of rows x D bf16 values is stored row-major with no padding; the
+// 16-byte chunks of row r are XOR-swizzled by h(r) = 2*(r % 4) + (r / 8) % 2.
+// With this swizzle both access patterns the kernels use are free of LDS bank
+// conflicts, for D = 64 and D = 128:
+//  * row reads: 8 lanes read 16 bytes each from rows sigma(0..7) (+8t), same
+//    logical chunk (MFMA A/B operands whose k runs along the row);
+//  * transposed reads (ds_read_b64_tr_b16): a 16-lane group reads a 4-row x
+//    16-column block (2 logical chunks of 4 consecutive rows).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+
+// element offset of (row, col) in a swizzled tile with D columns
+template <int D>
+__device__ __forceinline__ int toff(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz(r)) & (D / 8 - 1)) << 3) + (col & 7);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ds_read_b64_tr_b16, measured lane layout: within each 16-lane group, source
+// lane s supplies the address of 4 consecutive elements of row s/4, columns
+// 4*(s%4)..+3 of a 4 x 16 block; output lane i receives column i of the block
+// (its 4 rows, in row order).
+__device__ __forceinline__ i16x4 ds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// MFMA 32x32x16 operand (A or B) whose k index runs down the ROWS of a
+// row-major swizzled tile X[k][m]: lane l receives m = m0 + l % 32 and
+// k = k0 + (l / 32) * 8 + 0..7 -- the same fragment a row-major X^T would give.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int k0, int m0, int lane) {
+  const int row = k0 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+  const int col = m0 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  const i16x4 a = ds_read_tr16(tile + toff<D>(row, col));
+  const i16x4 b = ds_read_tr16(tile + toff<D>(row + 4, col));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+// MFMA operand whose k index runs ALONG a row of a swizzled tile: lane l reads
+// row `row`, columns k0 + (l / 32) * 8 + 0..7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const uint16_t* tile, int row, int k0, int lane) {
+  return as_bf16x8(ld16(tile + toff<D>(row, k0 + (lane >> 5) * 8)));
+}
+
 // Map a workgroup id so that consecutive logical ids run on the same XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); with this
 // remap XCD x processes the contiguous logical range [x*per, (x+1)*per), so the

@@ -151,18 +151,15 @@ PredictWs predict_ws(const Prob& o) {
 }
 
 struct BwdWs {
-  size_t qt, dot, kt, dvec, lse2, bitmap, counts, col_ptr, rows, total;
+  size_t dvec, lse2, bitmap, counts, col_ptr, rows, order, total;
 };
 BwdWs bwd_ws(const Prob& o) {
   BwdWs w{};
   size_t off = 0;
-  const size_t t = align_up(o.tensor_elems() * o.esize());
   const size_t rowf = align_up((size_t)o.bh() * o.n * sizeof(float));
   if (o.dtype == DSV_BF16) {
-    w.qt = off; off += t;
-    w.dot = off; off += t;
-    w.kt = off; off += t;
     w.lse2 = off; off += rowf;
+    w.order = off; off += align_up((size_t)o.bh() * o.nkb() * 4);
   }
   w.dvec = off; off += rowf;
   const int words = (o.nqb() + 31) / 32;
@@ -174,7 +171,7 @@ BwdWs bwd_ws(const Prob& o) {
   return w;
 }
 
-size_t fwd_ws_bytes(const Prob& o) { return o.dtype == DSV_BF16 ? align_up(o.tensor_elems() * 2) : 0; }
+size_t fwd_ws_bytes(const Prob&) { return 0; }  // the forward needs no scratch
 
 template <typename T>
 T* at(void* base, size_t off) {
@@ -327,9 +324,8 @@ dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* 
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (o.dtype == DSV_BF16) {
-    uint16_t* vt = at<uint16_t>(workspace, 0);
-    TRY_HIP(dsv::launch_transpose_bf16(static_cast<const uint16_t*>(v), vt, o.bh(), o.n, o.d, st), "transpose_kernel(v)");
-    TRY_HIP(dsv::launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, block_idx,
+    TRY_HIP(dsv::launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                      static_cast<const uint16_t*>(v), block_idx,
                                       static_cast<uint16_t*>(o_ptr), lse, o.bh(), o.n, o.d, o.bq, o.k, o.sm, st),
             "attn_fwd_kernel");
   } else {
@@ -365,27 +361,22 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* col_ptr = at<int32_t>(workspace, w.col_ptr);
   int32_t* rows = at<int32_t>(workspace, w.rows);
+  int32_t* order = o.dtype == DSV_BF16 ? at<int32_t>(workspace, w.order) : nullptr;
   TRY_HIP(dsv::launch_csc(block_idx, at<uint32_t>(workspace, w.bitmap), at<int32_t>(workspace, w.counts), col_ptr,
-                          rows, o.bh(), o.nqb(), o.nkb(), o.k, st), "csc_kernels");
+                          rows, order, o.bh(), o.nqb(), o.nkb(), o.k, st), "csc_kernels");
   float* dvec = at<float>(workspace, w.dvec);
   if (o.dtype == DSV_BF16) {
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(k);
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
     const uint16_t* do16 = static_cast<const uint16_t*>(dout);
-    uint16_t* qt = at<uint16_t>(workspace, w.qt);
-    uint16_t* dot = at<uint16_t>(workspace, w.dot);
-    uint16_t* kt = at<uint16_t>(workspace, w.kt);
     float* lse2 = at<float>(workspace, w.lse2);
-    TRY_HIP(dsv::launch_transpose_bf16(q16, qt, o.bh(), o.n, o.d, st), "transpose_kernel(q)");
-    TRY_HIP(dsv::launch_transpose_bf16(do16, dot, o.bh(), o.n, o.d, st), "transpose_kernel(dout)");
-    TRY_HIP(dsv::launch_transpose_bf16(k16, kt, o.bh(), o.n, o.d, st), "transpose_kernel(k)");
     TRY_HIP(dsv::launch_bwd_pre_bf16(static_cast<const uint16_t*>(o_ptr), do16, lse, dvec, lse2, o.bh() * o.n, o.d,
                                      st), "bwd_pre_kernel");
-    TRY_HIP(dsv::launch_bwd_dkdv_bf16(q16, qt, k16, v16, do16, dot, lse2, dvec, col_ptr, rows,
+    TRY_HIP(dsv::launch_bwd_dkdv_bf16(q16, k16, v16, do16, lse2, dvec, col_ptr, rows, order,
                                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), o.bh(), o.n, o.d, o.bq,
                                       o.k, o.sm, st), "attn_bwd_dkdv_kernel");
-    TRY_HIP(dsv::launch_bwd_dq_bf16(q16, k16, kt, v16, do16, lse2, dvec, block_idx, static_cast<uint16_t*>(dq), o.bh(),
+    TRY_HIP(dsv::launch_bwd_dq_bf16(q16, k16, v16, do16, lse2, dvec, block_idx, static_cast<uint16_t*>(dq), o.bh(),
                                     o.n, o.d, o.bq, o.k, o.sm, st), "attn_bwd_dq_kernel");
   } else {
     TRY_HIP(dsv::launch_bwd_pre_f32(static_cast<const float*>(o_ptr), static_cast<const float*>(dout), dvec,
