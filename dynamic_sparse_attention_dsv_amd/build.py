@@ -37,9 +37,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-file extra flags.  The predictor's sweep is VALU-bound and keeps few MFMA
+# accumulators: forcing MFMA results into VGPRs saves a register copy per logit.
+FILE_FLAGS = {"predict.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if r.returncode != 0:

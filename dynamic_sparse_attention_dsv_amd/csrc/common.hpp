@@ -72,6 +72,18 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // Value held by lane (l ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// max / sum of a value and its lane ^ 32 partner, via v_permlane32_swap (a VALU
+// exchange of the two wave halves, no LDS).  The two results of the swap hold
+// {x[l], x[l ^ 32]} in some order, and both reductions are symmetric.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // sigma: swap bits 2 and 3 of a row index (see the header comment).

@@ -117,48 +117,57 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
 #pragma unroll
       for (int c = 0; c < R / 16; ++c) qf[c] = as_bf16x8(ld16(qrow + c * 16 + g * 8));
     }
-    float run_m = -INFINITY, run_s = 0.f;
-    // prefetch the first KV block's A operands (K_lr rows, 8 consecutive r)
-    u32x4 ka[2][R / 16];
+    // A operands (K_lr rows, 8 consecutive r) of one KV block: 2 tiles x R/16 chunks
+    auto load_k = [&](int kb, u32x4 (&ka)[2][R / 16]) {
+      const uint16_t* kp = kh + (size_t)kb * 64 * R;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int c = 0; c < R / 16; ++c) ka[t][c] = ld16(kh + (size_t)(t * 32 + c32) * R + c * 16 + g * 8);
-
-    for (int kb = 0; kb < nkb; ++kb) {
-      f32x16 acc[2];
+        for (int c = 0; c < R / 16; ++c) ka[t][c] = ld16(kp + (size_t)(t * 32 + c32) * R + c * 16 + g * 8);
+    };
+    auto logits = [&](const u32x4 (&ka)[2][R / 16], f32x16 (&acc)[2]) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         acc[t] = f32x16{};
 #pragma unroll
         for (int c = 0; c < R / 16; ++c) acc[t] = mfma32(as_bf16x8(ka[t][c]), qf[c], acc[t]);
       }
+    };
+    float run_m = -INFINITY, run_s = 0.f;
+    u32x4 ka[2][R / 16], kn[2][R / 16];
+    f32x16 cur[2], nxt[2];
+    load_k(0, ka);
+    if (nkb > 1) load_k(1, kn);
+    logits(ka, cur);
+    for (int kb = 0; kb < nkb; ++kb) {
+      // logits of the next block are issued before this block's exponentials
       if (kb + 1 < nkb) {
-        const uint16_t* kn = kh + (size_t)(kb + 1) * 64 * R;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int c = 0; c < R / 16; ++c) ka[t][c] = ld16(kn + (size_t)(t * 32 + c32) * R + c * 16 + g * 8);
+        logits(kn, nxt);
+        if (kb + 2 < nkb) load_k(kb + 2, kn);
       }
       // lane holds query row (wave*32 + c32); 32 of the block's 64 keys, the other 32 in lane ^ 32
-      float m = acc[0][0];
+      float m0 = cur[0][0], m1 = cur[1][0];
 #pragma unroll
-      for (int v = 1; v < 16; ++v) m = fmaxf(m, acc[0][v]);
+      for (int v = 1; v < 16; ++v) {
+        m0 = fmaxf(m0, cur[0][v]);
+        m1 = fmaxf(m1, cur[1][v]);
+      }
+      const float mc = max_xor32(fmaxf(m0, m1)) * pc;
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) m = fmaxf(m, acc[1][v]);
-      m = fmaxf(m, xor32(m));
-      const float mc = m * pc;
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s += fast_exp2(fmaf(acc[t][v], pc, -mc));
-      s += xor32(s);
-      const float t2 = mc + fast_log2(s);  // log2 of the block's unnormalised mass
+      for (int v = 0; v < 16; ++v) {
+        s0 += fast_exp2(fmaf(cur[0][v], pc, -mc));
+        s1 += fast_exp2(fmaf(cur[1][v], pc, -mc));
+      }
+      const float t2 = mc + fast_log2(sum_xor32(s0 + s1));  // log2 of the block's unnormalised mass
       if (g == 0) slot[(size_t)kb * kScoreRows + wave * 32 + c32] = t2;
       const float nm = fmaxf(run_m, t2);
       run_s = run_s * fast_exp2(run_m - nm) + fast_exp2(t2 - nm);
       run_m = nm;
+      if (kb + 1 < nkb) {
+        cur[0] = nxt[0];
+        cur[1] = nxt[1];
+      }
     }
     if (g == 0) lse2_s[wave * 32 + c32] = run_m + fast_log2(run_s);
     __threadfence_block();
@@ -173,17 +182,17 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
     for (int i = 0; i < 32; ++i) lse_r[i] = lse2_s[wave * 32 + i];
     for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
       const int kb = kb0 + lane;
-      float acc = 0.f;
+      float acc0 = 0.f, acc1 = 0.f;
       if (kb < nkb) {
         const float* src = slot + (size_t)kb * kScoreRows + wave * 32;
 #pragma unroll
         for (int i = 0; i < 32; i += 4) {
           const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
-          acc += fast_exp2(tv[0] - lse_r[i]) + fast_exp2(tv[1] - lse_r[i + 1]) +
-                 fast_exp2(tv[2] - lse_r[i + 2]) + fast_exp2(tv[3] - lse_r[i + 3]);
+          acc0 += fast_exp2(tv[0] - lse_r[i]) + fast_exp2(tv[1] - lse_r[i + 1]);
+          acc1 += fast_exp2(tv[2] - lse_r[i + 2]) + fast_exp2(tv[3] - lse_r[i + 3]);
         }
       }
-      part_s[wave][lane] = acc;
+      part_s[wave][lane] = acc0 + acc1;
       __syncthreads();
       if (threadIdx.x < 64 * (kScoreRows / BQ)) {
         const int q = threadIdx.x / 64, kk = kb0 + (threadIdx.x & 63);
@@ -275,7 +284,7 @@ int score_slots(int items) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
   }
-  const int slots = cus * 2;
+  const int slots = cus * 4;  // 4 resident workgroups (16 waves) per compute unit
   return items < slots ? items : slots;
 }
 
