@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void csc_emit_kernel(const uint32_t* __restric
 // Wave w owns keys (w % 2) * 32 .. +32 of the block and the query half (w / 2)
 // of every 64-row chunk of the query blocks that selected the block.  K^T and
 // V^T fragments stay in registers; Q and dO chunks are gathered into swizzled
-// LDS tiles (double-buffered) and read both row-wise (A operands of S = Q K^T
+// LDS tiles by direct global->LDS loads (double-buffered) and read both row-wise (A operands of S = Q K^T
 // and dP = dO V^T) and transposed (B operands of dV += P^T dO, dK += dS^T Q).
 // The two query halves' partial dK/dV are summed through LDS at the end.
 
@@ -213,21 +213,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
     const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ rows, const int32_t* __restrict__ order,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int n, int nnz_per_bh, int nwg,
     float c /* sm_scale*log2e */, float sm_scale) {
-  constexpr int QR = 64;             // query rows per chunk
-  constexpr int TCH = QR * D / 8;    // 16-byte chunks per tile
-  constexpr int CH = 2 * TCH / 256;  // per thread per chunk (Q and dO tiles)
+  constexpr int QR = 64;                 // query rows per chunk
+  constexpr int NT = QR * D / 512;       // global->LDS instructions per tile
   constexpr int SUBS = BQ / QR;
   static_assert(BQ % QR == 0, "query block must be a multiple of 64 rows");
-  static_assert((D / 32) * 16 * 64 * 4 * 4 <= 4 * QR * D * 2, "reduction buffer must fit the tiles");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QR * D];  // Q[2], dO[2]
-  __shared__ __attribute__((aligned(16))) float Ls[2][QR];
-  __shared__ __attribute__((aligned(16))) float Dsh[2][QR];
+  // one array per buffer (see the dQ kernel): Q0/O0/L0 and Q1/O1/L1 (L: lse2[QR]
+  // then D[QR]).  The four tile arrays double as the final reduction buffer.
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[QR * D], O0[QR * D], Q1[QR * D], O1[QR * D];
+  __shared__ __attribute__((aligned(16))) float L0[2 * QR], L1[2 * QR];
 
   const int nkb = n / 64;
   const int id = xcd_remap(blockIdx.x, nwg);
   const int bh = id / nkb;
   const int kb = order[(size_t)bh * nkb + id % nkb];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
   const int kh = wave & 1, qh = wave >> 1;
   const size_t head = (size_t)bh * n * D;
@@ -241,8 +240,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) { dka[dt] = f32x16{}; dva[dt] = f32x16{}; }
 
-  auto qtile = [&](int buf) { return smem + buf * QR * D; };
-  auto otile = [&](int buf) { return smem + (2 + buf) * QR * D; };
 
   if (cnt > 0) {
     // K^T and V^T as B operands: lane holds its key, 8 consecutive d per chunk
@@ -254,43 +251,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
     }
     const int nch = cnt * SUBS;
     auto q0_of = [&](int j) { return list[j / SUBS] * BQ + (j % SUBS) * QR; };
-    auto gsrc = [&](int q0, int ch) -> const uint16_t* {
-      const int t = ch % TCH;
-      return (ch < TCH ? q : dout) + head + (size_t)(q0 + t / (D / 8)) * D + (t % (D / 8)) * 8;
-    };
-    auto ldst = [&](int buf, int ch) -> uint16_t* {
-      const int t = ch % TCH;
-      return (ch < TCH ? qtile(buf) : otile(buf)) + toff<D>(t / (D / 8), (t % (D / 8)) * 8);
-    };
-    u32x4 stage[CH];
-    u32x4 small = {};
-    auto load_small = [&](int q0) {  // threads 0..31: lse2 (16 chunks) and D (16 chunks)
-      if (threadIdx.x < 32) small = ld16((threadIdx.x < 16 ? lse2 : dvec) + (size_t)bh * n + q0 + (threadIdx.x % 16) * 4);
-    };
-    auto store_small = [&](int buf) {
-      if (threadIdx.x < 32) st16(&(threadIdx.x < 16 ? Ls : Dsh)[buf][(threadIdx.x % 16) * 4], small);
-    };
-    {
-      const int q0 = q0_of(0);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(q0, threadIdx.x + i * 256));
-      load_small(q0);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) st16(ldst(0, threadIdx.x + i * 256), stage[i]);
-      store_small(0);
-    }
-    __syncthreads();
-    const int arow = qh * 32 + sigma(c32);
-    for (int j = 0; j < nch; ++j) {
-      const int buf = j & 1;
-      if (j + 1 < nch) {
-        const int q0 = q0_of(j + 1);
-#pragma unroll
-        for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(q0, threadIdx.x + i * 256));
-        load_small(q0);
+    // asynchronous gather of a 64-row chunk (Q and dO tiles, lse2 and D) into one buffer set
+    auto issue = [&](int q0, uint16_t* qd, uint16_t* od, float* ld) {
+      for (int i = wave; i < 2 * NT; i += 4) {
+        const bool iso = i >= NT;
+        const int ii = iso ? i - NT : i;
+        lds_load_rows<D>((iso ? dout : q) + head + (size_t)q0 * D, iso ? od : qd, ii, lane);
       }
-      const uint16_t* qs = qtile(buf);
-      const uint16_t* os = otile(buf);
+      if (wave == 3 && lane < 32)  // lanes 0-15: 64 lse2 values, lanes 16-31: 64 D values
+        __builtin_amdgcn_global_load_lds((lane < 16 ? lse2 : dvec) + (size_t)bh * n + q0 + (lane & 15) * 4, ld, 16,
+                                         0, 0);
+    };
+    const int arow = qh * 32 + sigma(c32);
+    auto chunk = [&](const uint16_t* qs, const uint16_t* os, const float* ld) {
       // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys (A rows in sigma order)
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -298,13 +271,29 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
         s = mfma32(row_frag<D>(qs, arow, dc * 16, lane), kf[dc], s);
         dp = mfma32(row_frag<D>(os, arow, dc * 16, lane), vf[dc], dp);
       }
-      // register vv holds query qh*32 + (vv/8)*16 + g*8 + vv%8 of the chunk
+      // register vv holds query qh*32 + (vv/8)*16 + g*8 + vv%8 of the chunk: two runs of 8
+      // consecutive queries, read as vectors
+      float lq[16], dq_[16];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int q0 = qh * 32 + hh * 16 + g * 8;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&ld[q0]);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&ld[q0 + 4]);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&ld[QR + q0]);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&ld[QR + q0 + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lq[hh * 8 + e] = l0[e];
+          lq[hh * 8 + 4 + e] = l1[e];
+          dq_[hh * 8 + e] = d0[e];
+          dq_[hh * 8 + 4 + e] = d1[e];
+        }
+      }
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        const int qi = qh * 32 + (vv >> 3) * 16 + g * 8 + (vv & 7);
-        const float p = fast_exp2(fmaf(s[vv], c, -Ls[buf][qi]));
+        const float p = fast_exp2(fmaf(s[vv], c, -lq[vv]));
         s[vv] = p;
-        dp[vv] = p * (dp[vv] - Dsh[buf][qi]);
+        dp[vv] = p * (dp[vv] - dq_[vv]);
       }
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -318,24 +307,35 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
           dka[dt] = mfma32(da, tr_frag<D>(qs, qh * 32 + cc * 16, dt * 32, lane), dka[dt]);
         }
       }
-      if (j + 1 < nch) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) st16(ldst(buf ^ 1, threadIdx.x + i * 256), stage[i]);
-        store_small(buf ^ 1);
-      }
+    };
+    // two chunks per trip so that each buffer is a distinct array
+    issue(q0_of(0), Q0, O0, L0);
+    __syncthreads();
+    for (int j = 0; j < nch; j += 2) {
+      if (j + 1 < nch) issue(q0_of(j + 1), Q1, O1, L1);
+      chunk(Q0, O0, L0);
       __syncthreads();
+      if (j + 1 < nch) {
+        if (j + 2 < nch) issue(q0_of(j + 2), Q0, O0, L0);
+        chunk(Q1, O1, L1);
+        __syncthreads();
+      }
     }
   }
   // sum the two query halves through LDS (the tiles are free after the last barrier)
-  float* red = reinterpret_cast<float*>(smem);
-  auto ridx = [&](int which, int dt, int vv) { return (((kh * 2 + which) * (D / 32) + dt) * 16 + vv) * 64 + lane; };
+  // array kh*2 + which of {Q0, O0, Q1, O1} holds (D/32) x 16 x 64 floats: exactly its size
+  static_assert((D / 32) * 16 * 64 * 4 == QR * D * 2, "each tile array holds one reduction slab");
+  auto red = [&](int which) {
+    return reinterpret_cast<float*>(kh == 0 ? (which == 0 ? Q0 : O0) : (which == 0 ? Q1 : O1));
+  };
+  auto ridx = [&](int dt, int vv) { return (dt * 16 + vv) * 64 + lane; };
   if (qh == 1) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        red[ridx(0, dt, vv)] = dka[dt][vv];
-        red[ridx(1, dt, vv)] = dva[dt][vv];
+        red(0)[ridx(dt, vv)] = dka[dt][vv];
+        red(1)[ridx(dt, vv)] = dva[dt][vv];
       }
   }
   __syncthreads();
@@ -347,8 +347,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
       for (int vv = 0; vv < 16; ++vv) {
         const int kr = kb * 64 + kh * 32 + (vv >> 2) * 8 + g * 4 + (vv & 3);
         const size_t off = head + (size_t)kr * D + dt * 32 + c32;
-        dk[off] = f32_to_bf16((dka[dt][vv] + red[ridx(0, dt, vv)]) * sm_scale);
-        dv[off] = f32_to_bf16(dva[dt][vv] + red[ridx(1, dt, vv)]);
+        dk[off] = f32_to_bf16((dka[dt][vv] + red(0)[ridx(dt, vv)]) * sm_scale);
+        dv[off] = f32_to_bf16(dva[dt][vv] + red(1)[ridx(dt, vv)]);
       }
   }
 }
@@ -360,35 +360,33 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
 // dQ^T += K^T dS^T takes K^T from transposing reads of the row-major K tile.
 
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2) void attn_bwd_dq_bf16_kernel(
+__global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dvec,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ dq, int n, int topk, int nwg, float c, float sm_scale) {
-  constexpr int THREADS = BQ * 2;
-  constexpr int TCH = 64 * D / 8;
-  constexpr int CH = 2 * TCH / THREADS;
-  static_assert((2 * TCH) % THREADS == 0, "staging must divide evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * D];
+  constexpr int WAVES = BQ / 32;
+  constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
+  // one array per buffer, so the compiler can see that the asynchronous copy into
+  // one buffer never aliases the reads of the other (no waits mid-compute)
+  __shared__ __attribute__((aligned(16))) uint16_t K0[64 * D], K1[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[64 * D], V1[64 * D];
 
   const int nqb = n / BQ;
   const int id = xcd_remap(blockIdx.x, nwg);
   const int bh = id / nqb, qb = id % nqb;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
   const size_t head = (size_t)bh * n * D;
   const int32_t* blocks = idx + ((size_t)bh * nqb + qb) * topk;
   const int qrow = qb * BQ + wave * 32 + c32;
   const int nkb = n / 64;
   auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };  // clamp out-of-range indices
-
-  auto gsrc = [&](int blk, int ch) -> const uint16_t* {
-    const int t = ch % TCH;
-    return (ch < TCH ? k : v) + head + (size_t)(blk * 64 + t / (D / 8)) * D + (t % (D / 8)) * 8;
-  };
-  auto ldst = [&](int buf, int ch) -> uint16_t* {
-    const int t = ch % TCH;
-    return (ch < TCH ? Ks[buf] : Vs[buf]) + toff<D>(t / (D / 8), (t % (D / 8)) * 8);
+  auto issue = [&](int blk, uint16_t* kd, uint16_t* vd) {  // asynchronous gather of a K and V block
+    for (int i = wave; i < NI; i += WAVES) {
+      const bool isv = i >= NI / 2;
+      const int ii = isv ? i - NI / 2 : i;
+      lds_load_rows<D>((isv ? v : k) + head + (size_t)blk * 64 * D, isv ? vd : kd, ii, lane);
+    }
   };
 
   bf16x8 qf[D / 16], of[D / 16];
@@ -400,65 +398,56 @@ __global__ __launch_bounds__(BQ * 2) void attn_bwd_dq_bf16_kernel(
   const float my_lse2 = lse2[(size_t)bh * n + qrow];
   const float my_d = dvec[(size_t)bh * n + qrow];
 
-  u32x4 stage[CH];
-  {
-    const int blk = blk_at(0);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(blk, threadIdx.x + i * THREADS));
-#pragma unroll
-    for (int i = 0; i < CH; ++i) st16(ldst(0, threadIdx.x + i * THREADS), stage[i]);
-  }
+  issue(blk_at(0), K0, V0);
   __syncthreads();
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   const int arow = sigma(c32);
-  for (int j = 0; j < topk; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < topk) {
-      const int blk = blk_at(j + 1);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(blk, threadIdx.x + i * THREADS));
-    }
-    f32x16 s[2], dp[2];
+  auto block = [&](const uint16_t* Kc, const uint16_t* Vc) {
+    // one 32-key tile at a time: S^T, dP^T, dS^T, then its two 16-key chunks of dQ^T += K^T dS^T.
+    // dS is split into bf16 hi + lo parts: K's large entries would otherwise amplify dS's bf16
+    // rounding into dQ errors comparable to dQ's own bf16 storage rounding.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      s[t] = f32x16{};
-      dp[t] = f32x16{};
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        s[t] = mfma32(row_frag<D>(Ks[buf], t * 32 + arow, dc * 16, lane), qf[dc], s[t]);
-        dp[t] = mfma32(row_frag<D>(Vs[buf], t * 32 + arow, dc * 16, lane), of[dc], dp[t]);
+        s = mfma32(row_frag<D>(Kc, t * 32 + arow, dc * 16, lane), qf[dc], s);
+        dp = mfma32(row_frag<D>(Vc, t * 32 + arow, dc * 16, lane), of[dc], dp);
       }
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        const float p = fast_exp2(fmaf(s[t][vv], c, -my_lse2));
-        dp[t][vv] = p * (dp[t][vv] - my_d);
+        const float p = fast_exp2(fmaf(s[vv], c, -my_lse2));
+        dp[vv] = p * (dp[vv] - my_d);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int b0 = h2 * 8, cc = t * 2 + h2;
+        const bf16x8 hi = cvt8(dp[b0], dp[b0 + 1], dp[b0 + 2], dp[b0 + 3], dp[b0 + 4], dp[b0 + 5], dp[b0 + 6],
+                               dp[b0 + 7]);
+        const bf16x8 lo = cvt8(dp[b0] - (float)hi[0], dp[b0 + 1] - (float)hi[1], dp[b0 + 2] - (float)hi[2],
+                               dp[b0 + 3] - (float)hi[3], dp[b0 + 4] - (float)hi[4], dp[b0 + 5] - (float)hi[5],
+                               dp[b0 + 6] - (float)hi[6], dp[b0 + 7] - (float)hi[7]);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const bf16x8 ka = tr_frag<D>(Kc, cc * 16, dt * 32, lane);
+          acc[dt] = mfma32(ka, hi, acc[dt]);
+          acc[dt] = mfma32(ka, lo, acc[dt]);
+        }
       }
     }
-    // dQ^T += K^T dS^T with dS split into bf16 hi + lo parts: K's large entries would otherwise
-    // amplify dS's bf16 rounding into dQ errors comparable to dQ's own bf16 storage rounding
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const f32x16& st = dp[cc >> 1];
-      const int b0 = (cc & 1) * 8;
-      const bf16x8 hi = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
-                             st[b0 + 7]);
-      const bf16x8 lo = cvt8(st[b0] - (float)hi[0], st[b0 + 1] - (float)hi[1], st[b0 + 2] - (float)hi[2],
-                             st[b0 + 3] - (float)hi[3], st[b0 + 4] - (float)hi[4], st[b0 + 5] - (float)hi[5],
-                             st[b0 + 6] - (float)hi[6], st[b0 + 7] - (float)hi[7]);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16x8 ka = tr_frag<D>(Ks[buf], cc * 16, dt * 32, lane);
-        acc[dt] = mfma32(ka, hi, acc[dt]);
-        acc[dt] = mfma32(ka, lo, acc[dt]);
-      }
-    }
-    if (j + 1 < topk) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) st16(ldst(buf ^ 1, threadIdx.x + i * THREADS), stage[i]);
-    }
+  };
+  // two blocks per trip so that each buffer is a distinct array
+  for (int j = 0; j < topk; j += 2) {
+    if (j + 1 < topk) issue(blk_at(j + 1), K1, V1);
+    block(K0, V0);
     __syncthreads();
+    if (j + 1 < topk) {
+      if (j + 2 < topk) issue(blk_at(j + 2), K0, V0);
+      block(K1, V1);
+      __syncthreads();
+    }
   }
   uint16_t* out = dq + head + (size_t)qrow * D;
 #pragma unroll

@@ -8,11 +8,14 @@
 //
 // gfx950 design (bf16, d in {64,128}, Bq in {64,128}, Bk = 64):
 //  * one workgroup per (b, h, qb), Bq/32 waves, each wave owns 32 query rows;
+//    registers are capped so that two waves share each SIMD (one's softmax
+//    VALU work overlaps the other's MFMAs);
 //    workgroup ids are remapped so that one XCD works on one head at a time;
 //  * Q stays in registers as the B operand of S^T = K Q^T (v_mfma 32x32x16);
 //  * each selected KV block is gathered into swizzled LDS tiles (K and V both
-//    row-major, as stored) with double buffering: the next block's global loads
-//    are in flight while the current block is computed; the V^T operand of
+//    row-major, as stored) by direct global->LDS loads, double-buffered: the
+//    next block's copies are in flight while the current block is computed,
+//    without staging registers; the V^T operand of
 //    O^T += V^T P^T comes from transposing LDS reads (ds_read_b64_tr_b16);
 //  * S^T's D layout puts one query per lane, so the online-softmax row max and
 //    row sum are lane-local plus one exchange with lane ^ 32; K rows are loaded
@@ -23,36 +26,35 @@
 namespace dsv {
 
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse, int n, int topk,
     int nwg, float c /* sm_scale * log2(e) */) {
-  constexpr int THREADS = BQ * 2;        // (BQ / 32) waves of 64
-  constexpr int TCH = 64 * D / 8;        // 16-byte chunks of one 64 x D tile
-  constexpr int CH = 2 * TCH / THREADS;  // chunks staged per thread (K and V tiles)
-  static_assert((2 * TCH) % THREADS == 0, "staging must divide evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * D];
+  constexpr int WAVES = BQ / 32;
+  constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
+  // separate arrays per buffer: with one array the compiler cannot tell that the
+  // asynchronous copy into one buffer never aliases reads of the other, and would
+  // wait for the copy before every transposing read
+  __shared__ __attribute__((aligned(16))) uint16_t K0[64 * D], K1[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[64 * D], V1[64 * D];
 
   const int nqb = n / BQ;
   const int id = xcd_remap(blockIdx.x, nwg);
   const int bh = id / nqb, qb = id % nqb;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
   const size_t head = (size_t)bh * n * D;
   const int32_t* blocks = idx + ((size_t)bh * nqb + qb) * topk;
   const int nkb = n / 64;
   // out-of-range block indices are clamped: wrong results, but no access outside the tensors
   auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };
-
-  // staging: chunk ch < TCH is K (row ch / (D/8)), otherwise V; both row-major in memory
-  auto gsrc = [&](int blk, int ch) -> const uint16_t* {
-    const int t = ch % TCH;
-    return (ch < TCH ? k : v) + head + (size_t)(blk * 64 + t / (D / 8)) * D + (t % (D / 8)) * 8;
-  };
-  auto ldst = [&](int buf, int ch) -> uint16_t* {
-    const int t = ch % TCH;
-    return (ch < TCH ? Ks[buf] : Vs[buf]) + toff<D>(t / (D / 8), (t % (D / 8)) * 8);
+  // gather KV block `blk` into LDS buffer `buf` (asynchronous; visible after the next barrier)
+  auto issue = [&](int blk, uint16_t* kd, uint16_t* vd) {
+    for (int i = wave; i < NI; i += WAVES) {
+      const bool isv = i >= NI / 2;
+      const int ii = isv ? i - NI / 2 : i;
+      lds_load_rows<D>((isv ? v : k) + head + (size_t)blk * 64 * D, isv ? vd : kd, ii, lane);
+    }
   };
 
   // Q^T as the B operand of S^T = K Q^T: lane holds its query row, 8 consecutive d per 16-wide chunk
@@ -61,14 +63,7 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) qf[dc] = as_bf16x8(ld16(q + head + (size_t)qrow * D + dc * 16 + g * 8));
 
-  u32x4 stage[CH];
-  {
-    const int blk = blk_at(0);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(blk, threadIdx.x + i * THREADS));
-#pragma unroll
-    for (int i = 0; i < CH; ++i) st16(ldst(0, threadIdx.x + i * THREADS), stage[i]);
-  }
+  issue(blk_at(0), K0, V0);
   __syncthreads();
 
   f32x16 oacc[D / 32];
@@ -77,20 +72,15 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   const int arow = sigma(c32);
 
-  for (int j = 0; j < topk; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < topk) {
-      const int blk = blk_at(j + 1);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) stage[i] = ld16(gsrc(blk, threadIdx.x + i * THREADS));
-    }
+  // one selected KV block: scores from Kc, online softmax, O^T += V^T P^T from Vc
+  auto block = [&](const uint16_t* Kc, const uint16_t* Vc) {
     // S^T = K Q^T: two 32-key tiles, K rows read in sigma order
     f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = f32x16{};
 #pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) s[t] = mfma32(row_frag<D>(Ks[buf], t * 32 + arow, dc * 16, lane), qf[dc], s[t]);
+      for (int dc = 0; dc < D / 16; ++dc) s[t] = mfma32(row_frag<D>(Kc, t * 32 + arow, dc * 16, lane), qf[dc], s[t]);
     }
     // online softmax (log2 domain); lane owns one query, 32 of the block's 64 keys
     float mx = s[0][0];
@@ -98,7 +88,7 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
     for (int vv = 1; vv < 16; ++vv) mx = fmaxf(mx, s[0][vv]);
 #pragma unroll
     for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[1][vv]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx * c);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
@@ -122,13 +112,20 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16_kernel(
       const bf16x8 pb = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
                              st[b0 + 7]);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(tr_frag<D>(Vs[buf], cc * 16, dt * 32, lane), pb, oacc[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(tr_frag<D>(Vc, cc * 16, dt * 32, lane), pb, oacc[dt]);
     }
-    if (j + 1 < topk) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) st16(ldst(buf ^ 1, threadIdx.x + i * THREADS), stage[i]);
-    }
+  };
+
+  // two blocks per trip so that each buffer is a distinct array (see the declarations)
+  for (int j = 0; j < topk; j += 2) {
+    if (j + 1 < topk) issue(blk_at(j + 1), K1, V1);
+    block(K0, V0);
     __syncthreads();
+    if (j + 1 < topk) {
+      if (j + 2 < topk) issue(blk_at(j + 2), K0, V0);
+      block(K1, V1);
+      __syncthreads();
+    }
   }
 
   const float l = l_run + xor32(l_run);

@@ -98,19 +98,26 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // ---------------------------------------------------------------- LDS tiles
 //
 // A tile of rows x D bf16 values is stored row-major with no padding; the
-// 16-byte chunks of row r are XOR-swizzled by h(r) = 2*(r % 4) + (r / 8) % 2.
-// With this swizzle both access patterns the kernels use are free of LDS bank
-// conflicts, for D = 64 and D = 128:
-//  * row reads: 8 lanes read 16 bytes each from rows sigma(0..7) (+8t), same
-//    logical chunk (MFMA A/B operands whose k runs along the row);
-//  * transposed reads (ds_read_b64_tr_b16): a 16-lane group reads a 4-row x
-//    16-column block (2 logical chunks of 4 consecutive rows).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+// 16-byte chunks of row r are XOR-swizzled by h(r):
+//   D = 128 (256-byte rows):  h(r) = 4*(r % 4) + (r / 4) % 4
+//   D = 64  (128-byte rows):  h(r) = 4*((r / 2) % 2) + (r / 4) % 4
+// The LDS serves 64 banks x 4 bytes per cycle (16 lanes of a 16-byte read, 32
+// lanes of an 8-byte read; bank-conflict counters confirm the width).  With
+// this swizzle both access patterns the kernels use are conflict-free:
+//  * row reads: 16 lanes read 16 bytes each from 16 consecutive rows (in sigma
+//    order), same logical chunk (MFMA operands whose k runs along the row);
+//  * transposed reads (ds_read_b64_tr_b16): 32 lanes read a 4-row x 32-column
+//    block (4 logical chunks of 4 consecutive rows).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 // element offset of (row, col) in a swizzled tile with D columns
 template <int D>
 __device__ __forceinline__ int toff(int r, int col) {
-  return r * D + ((((col >> 3) ^ swz(r)) & (D / 8 - 1)) << 3) + (col & 7);
+  return r * D + ((((col >> 3) ^ swz<D>(r)) & (D / 8 - 1)) << 3) + (col & 7);
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -143,6 +150,22 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int k0, int m0, 
 template <int D>
 __device__ __forceinline__ bf16x8 row_frag(const uint16_t* tile, int row, int k0, int lane) {
   return as_bf16x8(ld16(tile + toff<D>(row, k0 + (lane >> 5) * 8)));
+}
+
+// Asynchronous copy of global memory into a swizzled LDS tile: one
+// global_load_lds_dwordx4 moves 64 x 16 bytes, lane L landing at LDS base +
+// 16 * L (measured on the device), i.e. rows [i*R, i*R + R) of the tile with
+// R = 512 / D.  Lane L fills physical chunk p = L % (D/8) of its row, which holds
+// logical chunk p ^ swz(row).  `src` points at the tile's first global row (row
+// stride D elements); `dst` is the LDS tile; `i` is the instruction index.
+// The data is visible after the next __syncthreads() (the compiler waits for
+// the outstanding loads before the barrier).
+template <int D>
+__device__ __forceinline__ void lds_load_rows(const uint16_t* src, uint16_t* dst, int i, int lane) {
+  constexpr int R = 512 / D;
+  const int row = i * R + lane / (D / 8);
+  const int c = ((lane % (D / 8)) ^ swz<D>(row)) & (D / 8 - 1);
+  __builtin_amdgcn_global_load_lds(src + (size_t)row * D + c * 8, dst + i * 512, 16, 0, 0);
 }
 
 // Map a workgroup id so that consecutive logical ids run on the same XCD.

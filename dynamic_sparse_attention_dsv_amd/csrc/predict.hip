@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(const uint16_t* __restri
   // grid: (ceil(n/256), B*H). x, out: [BH, n, D] / [BH, n, R]; w: [H, D, R].
   const int bh = blockIdx.y;
   const int h = bh % heads;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const uint16_t* wh = w + (size_t)h * D * R;
   // A operand = W^T [R x D]: lane holds row r = rt*16 + c16, k = kc*32 + g*8 + e
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
   static_assert(kScoreRows % BQ == 0, "BQ must divide 128");
   __shared__ float lse2_s[kScoreRows];
   __shared__ float part_s[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
   float* slot = scratch + (size_t)blockIdx.x * nkb * kScoreRows;
   const int items_per_head = n / kScoreRows;
