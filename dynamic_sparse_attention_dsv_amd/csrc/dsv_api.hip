@@ -141,7 +141,7 @@ PredictWs predict_ws(const Prob& o) {
   size_t off = 2 * lr;
   if (o.dtype == DSV_BF16) {
     w.scratch = off;
-    off += align_up(dsv::score_scratch_bytes(o.bh() * (o.n / 128), o.nkb()));
+    off += align_up(dsv::score_scratch_bytes(o.bh() * (o.n / 256), o.nkb()));
   } else {
     w.lse = off;
     off += align_up((size_t)o.bh() * o.n * sizeof(float));
@@ -248,8 +248,8 @@ dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const
   TRY(to_prob(p, o, true));
   if (o.dtype == DSV_BF16) {
     if ((o.d != 64 && o.d != 128) || (o.r != 16 && o.r != 32) || (o.bq != 64 && o.bq != 128) || o.bk != 64 ||
-        o.n % 128)
-      return fail(DSV_ERR_UNSUPPORTED, "bf16 predictor needs d in {64,128}, r in {16,32}, Bq in {64,128}, Bk = 64, N % 128 == 0");
+        o.n % 256)
+      return fail(DSV_ERR_UNSUPPORTED, "bf16 predictor needs d in {64,128}, r in {16,32}, Bq in {64,128}, Bk = 64, N % 256 == 0");
   } else if (o.r > 64) {
     return fail(DSV_ERR_UNSUPPORTED, "f32 predictor needs r <= 64");
   }

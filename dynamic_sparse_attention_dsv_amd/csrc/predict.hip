@@ -88,7 +88,7 @@ __global__ void proj_f32_kernel(const float* __restrict__ x, const float* __rest
 
 // ---------------------------------------------------------------- scores (bf16, MFMA)
 
-constexpr int kScoreRows = 128;  // query rows per work item (4 waves x 32)
+constexpr int kScoreRows = 256;  // query rows per work item (4 waves x 64)
 
 template <int R, int BQ>
 __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __restrict__ qlr,
@@ -96,9 +96,12 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
                                                           float* __restrict__ scratch,
                                                           float* __restrict__ scores, int n, int nkb,
                                                           int items, float pc) {
-  // qlr, klr: [BH, n, R] bf16.  scratch: gridDim.x slots of [nkb][128] float.
+  // qlr, klr: [BH, n, R] bf16.  scratch: gridDim.x slots of [nkb][256] float.
   // scores: [BH, n/BQ, nkb].  pc = pred_scale * log2(e).
-  static_assert(kScoreRows % BQ == 0, "BQ must divide 128");
+  // Each wave owns 64 query rows (two 32-row halves): every K_lr fragment it loads feeds
+  // two MFMA tiles, halving the K_lr traffic per logit.
+  static_assert(kScoreRows % BQ == 0 && BQ % 64 == 0, "BQ must be 64 or 128");
+  constexpr int NC = R / 16;
   __shared__ float lse2_s[kScoreRows];
   __shared__ float part_s[4][64];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -110,32 +113,35 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
     const int bh = item / items_per_head;
     const int row0 = (item % items_per_head) * kScoreRows;
     const uint16_t* kh = klr + (size_t)bh * n * R;
-    // B operand = Q_lr^T [R x 32 rows]: lane holds its query row, 8 consecutive r
-    bf16x8 qf[R / 16];
-    {
-      const uint16_t* qrow = qlr + ((size_t)bh * n + row0 + wave * 32 + c32) * R;
+    // B operands = Q_lr^T for the wave's two 32-row halves: lane holds its query row, 8 consecutive r
+    bf16x8 qf[2][NC];
 #pragma unroll
-      for (int c = 0; c < R / 16; ++c) qf[c] = as_bf16x8(ld16(qrow + c * 16 + g * 8));
+    for (int h = 0; h < 2; ++h) {
+      const uint16_t* qrow = qlr + ((size_t)bh * n + row0 + wave * 64 + h * 32 + c32) * R;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qf[h][c] = as_bf16x8(ld16(qrow + c * 16 + g * 8));
     }
-    // A operands (K_lr rows, 8 consecutive r) of one KV block: 2 tiles x R/16 chunks
-    auto load_k = [&](int kb, u32x4 (&ka)[2][R / 16]) {
+    // A operands (K_lr rows, 8 consecutive r) of one KV block: 2 tiles x NC chunks
+    auto load_k = [&](int kb, u32x4 (&ka)[2][NC]) {
       const uint16_t* kp = kh + (size_t)kb * 64 * R;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < R / 16; ++c) ka[t][c] = ld16(kp + (size_t)(t * 32 + c32) * R + c * 16 + g * 8);
+        for (int c = 0; c < NC; ++c) ka[t][c] = ld16(kp + (size_t)(t * 32 + c32) * R + c * 16 + g * 8);
     };
-    auto logits = [&](const u32x4 (&ka)[2][R / 16], f32x16 (&acc)[2]) {
+    auto logits = [&](const u32x4 (&ka)[2][NC], f32x16 (&acc)[2][2]) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        acc[t] = f32x16{};
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int c = 0; c < R / 16; ++c) acc[t] = mfma32(as_bf16x8(ka[t][c]), qf[c], acc[t]);
-      }
+        for (int t = 0; t < 2; ++t) {
+          acc[h][t] = f32x16{};
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[h][t] = mfma32(as_bf16x8(ka[t][c]), qf[h][c], acc[h][t]);
+        }
     };
-    float run_m = -INFINITY, run_s = 0.f;
-    u32x4 ka[2][R / 16], kn[2][R / 16];
-    f32x16 cur[2], nxt[2];
+    float run_m[2] = {-INFINITY, -INFINITY}, run_s[2] = {0.f, 0.f};
+    u32x4 ka[2][NC], kn[2][NC];
+    f32x16 cur[2][2], nxt[2][2];
     load_k(0, ka);
     if (nkb > 1) load_k(1, kn);
     logits(ka, cur);
@@ -145,63 +151,71 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
         logits(kn, nxt);
         if (kb + 2 < nkb) load_k(kb + 2, kn);
       }
-      // lane holds query row (wave*32 + c32); 32 of the block's 64 keys, the other 32 in lane ^ 32
-      float m0 = cur[0][0], m1 = cur[1][0];
 #pragma unroll
-      for (int v = 1; v < 16; ++v) {
-        m0 = fmaxf(m0, cur[0][v]);
-        m1 = fmaxf(m1, cur[1][v]);
-      }
-      const float mc = max_xor32(fmaxf(m0, m1)) * pc;
-      float s0 = 0.f, s1 = 0.f;
+      for (int h = 0; h < 2; ++h) {
+        // lane holds query row (wave*64 + h*32 + c32); 32 of the block's 64 keys, the other 32 in lane ^ 32
+        float m0 = cur[h][0][0], m1 = cur[h][1][0];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s0 += fast_exp2(fmaf(cur[0][v], pc, -mc));
-        s1 += fast_exp2(fmaf(cur[1][v], pc, -mc));
+        for (int v = 1; v < 16; ++v) {
+          m0 = fmaxf(m0, cur[h][0][v]);
+          m1 = fmaxf(m1, cur[h][1][v]);
+        }
+        const float mc = max_xor32(fmaxf(m0, m1)) * pc;
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          s0 += fast_exp2(fmaf(cur[h][0][v], pc, -mc));
+          s1 += fast_exp2(fmaf(cur[h][1][v], pc, -mc));
+        }
+        const float t2 = mc + fast_log2(sum_xor32(s0 + s1));  // log2 of the block's unnormalised mass
+        if (g == 0) slot[(size_t)kb * kScoreRows + wave * 64 + h * 32 + c32] = t2;
+        const float nm = fmaxf(run_m[h], t2);
+        run_s[h] = run_s[h] * fast_exp2(run_m[h] - nm) + fast_exp2(t2 - nm);
+        run_m[h] = nm;
       }
-      const float t2 = mc + fast_log2(sum_xor32(s0 + s1));  // log2 of the block's unnormalised mass
-      if (g == 0) slot[(size_t)kb * kScoreRows + wave * 32 + c32] = t2;
-      const float nm = fmaxf(run_m, t2);
-      run_s = run_s * fast_exp2(run_m - nm) + fast_exp2(t2 - nm);
-      run_m = nm;
       if (kb + 1 < nkb) {
-        cur[0] = nxt[0];
-        cur[1] = nxt[1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          cur[h][0] = nxt[h][0];
+          cur[h][1] = nxt[h][1];
+        }
       }
     }
-    if (g == 0) lse2_s[wave * 32 + c32] = run_m + fast_log2(run_s);
+    if (g == 0) {
+      lse2_s[wave * 64 + c32] = run_m[0] + fast_log2(run_s[0]);
+      lse2_s[wave * 64 + 32 + c32] = run_m[1] + fast_log2(run_s[1]);
+    }
     __threadfence_block();
     __syncthreads();
 
     // finalize: score[qb, kb] = sum_{i in qb} 2^(t2[kb][i] - lse2[i]).
-    // chunks of 64 KV blocks: lane <-> kb, wave w sums rows [32w, 32w+32).
+    // chunks of 64 KV blocks: lane <-> kb, wave w sums its rows [64w, 64w+64).
     float* sc_head = scores + (size_t)bh * (n / BQ) * nkb;
     const int qb0 = row0 / BQ;
-    float lse_r[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) lse_r[i] = lse2_s[wave * 32 + i];
     for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
       const int kb = kb0 + lane;
       float acc0 = 0.f, acc1 = 0.f;
       if (kb < nkb) {
-        const float* src = slot + (size_t)kb * kScoreRows + wave * 32;
+        const float* src = slot + (size_t)kb * kScoreRows + wave * 64;
+        const float* ls = lse2_s + wave * 64;
 #pragma unroll
-        for (int i = 0; i < 32; i += 4) {
+        for (int i = 0; i < 64; i += 4) {
           const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
-          acc0 += fast_exp2(tv[0] - lse_r[i]) + fast_exp2(tv[1] - lse_r[i + 1]);
-          acc1 += fast_exp2(tv[2] - lse_r[i + 2]) + fast_exp2(tv[3] - lse_r[i + 3]);
+          acc0 += fast_exp2(tv[0] - ls[i]) + fast_exp2(tv[1] - ls[i + 1]);
+          acc1 += fast_exp2(tv[2] - ls[i + 2]) + fast_exp2(tv[3] - ls[i + 3]);
         }
       }
       part_s[wave][lane] = acc0 + acc1;
       __syncthreads();
-      if (threadIdx.x < 64 * (kScoreRows / BQ)) {
-        const int q = threadIdx.x / 64, kk = kb0 + (threadIdx.x & 63);
+      constexpr int QBS = kScoreRows / BQ;    // query blocks per item
+      constexpr int WPQ = BQ / 64;            // waves per query block
+      if (threadIdx.x < 64 * QBS) {
+        const int qq = threadIdx.x / 64, kk = kb0 + (threadIdx.x & 63);
         if (kk < nkb) {
-          float tot;
-          if (BQ == 128) tot = (part_s[0][threadIdx.x & 63] + part_s[1][threadIdx.x & 63]) +
-                               (part_s[2][threadIdx.x & 63] + part_s[3][threadIdx.x & 63]);
-          else tot = part_s[2 * q][threadIdx.x & 63] + part_s[2 * q + 1][threadIdx.x & 63];
-          sc_head[(size_t)(qb0 + q) * nkb + kk] = tot;
+          float tot = 0.f;
+#pragma unroll
+          for (int w = 0; w < WPQ; ++w) tot += part_s[qq * WPQ + w][threadIdx.x & 63];
+          sc_head[(size_t)(qb0 + qq) * nkb + kk] = tot;
         }
       }
       __syncthreads();

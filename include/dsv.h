@@ -80,7 +80,7 @@ typedef enum { DSV_F32 = 0, DSV_BF16 = 1 } dsv_dtype;
  *
  * Compiled instances (others return DSV_ERR_UNSUPPORTED):
  *   bf16: d in {64, 128}, r in {16, 32}, Bq in {64, 128}, Bk = 64, N/Bk <= 4096;
- *         dsv_predict additionally needs N % 128 == 0
+ *         dsv_predict additionally needs N % 256 == 0
  *   f32 : d <= 128, r <= 64, any Bq/Bk satisfying the divisibility rules,
  *         N/Bk <= 4096 (a plain VALU path meant for small problems)
  */
