@@ -139,45 +139,95 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
           for (int c = 0; c < NC; ++c) acc[h][t] = mfma32(as_bf16x8(ka[t][c]), qf[h][c], acc[h][t]);
         }
     };
-    float run_m[2] = {-INFINITY, -INFINITY}, run_s[2] = {0.f, 0.f};
+    float run_m[2], run_s[2];
+    auto fold = [&](int h, float t2) {  // online log-sum-exp over blocks
+      const float nm = fmaxf(run_m[h], t2);
+      run_s[h] = run_s[h] * fast_exp2(run_m[h] - nm) + fast_exp2(t2 - nm);
+      run_m[h] = nm;
+    };
+    // block mass of half h with shift sh (log2 units): t = sh + log2 sum_j 2^(pc a_ij - sh)
+    auto block_t2 = [&](const f32x16 (&acc)[2], float sh) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s0 += fast_exp2(fmaf(acc[0][v], pc, -sh));
+        s1 += fast_exp2(fmaf(acc[1][v], pc, -sh));
+      }
+      return sh + fast_log2(sum_xor32(s0 + s1));
+    };
+    auto own_max = [&](const f32x16 (&acc)[2]) {  // the block's largest logit, log2 units
+      float m0 = acc[0][0], m1 = acc[1][0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) {
+        m0 = fmaxf(m0, acc[0][v]);
+        m1 = fmaxf(m1, acc[1][v]);
+      }
+      return max_xor32(fmaxf(m0, m1)) * pc;
+    };
+    auto store = [&](int kb, int h, float t2) {
+      if (g == 0) slot[(size_t)kb * kScoreRows + wave * 64 + h * 32 + c32] = t2;
+    };
+    // Fast sweep.  Block 0 is shifted by its own max; every later block by the row's running
+    // log-mass bound one block back (>= each earlier logit, up to +6), so no per-block max is
+    // needed and consecutive blocks stay independent.  A logit more than 127 above that bound
+    // would overflow; this is detected once per item below and the item is redone exactly.
     u32x4 ka[2][NC], kn[2][NC];
     f32x16 cur[2][2], nxt[2][2];
+    float lag[2];
     load_k(0, ka);
     if (nkb > 1) load_k(1, kn);
     logits(ka, cur);
-    for (int kb = 0; kb < nkb; ++kb) {
-      // logits of the next block are issued before this block's exponentials
-      if (kb + 1 < nkb) {
-        logits(kn, nxt);
-        if (kb + 2 < nkb) load_k(kb + 2, kn);
-      }
+    if (nkb > 1) logits(kn, nxt);
+    if (nkb > 2) load_k(2, kn);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float t0 = block_t2(cur[h], own_max(cur[h]));
+      store(0, h, t0);
+      run_m[h] = t0;
+      run_s[h] = 1.f;
+      lag[h] = t0;
+    }
+    // steady state without branches: issue block kb+1, prefetch kb+2 (clamped), finish kb
+    for (int kb = 1; kb + 1 < nkb; ++kb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        // lane holds query row (wave*64 + h*32 + c32); 32 of the block's 64 keys, the other 32 in lane ^ 32
-        float m0 = cur[h][0][0], m1 = cur[h][1][0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) {
-          m0 = fmaxf(m0, cur[h][0][v]);
-          m1 = fmaxf(m1, cur[h][1][v]);
-        }
-        const float mc = max_xor32(fmaxf(m0, m1)) * pc;
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s0 += fast_exp2(fmaf(cur[h][0][v], pc, -mc));
-          s1 += fast_exp2(fmaf(cur[h][1][v], pc, -mc));
-        }
-        const float t2 = mc + fast_log2(sum_xor32(s0 + s1));  // log2 of the block's unnormalised mass
-        if (g == 0) slot[(size_t)kb * kScoreRows + wave * 64 + h * 32 + c32] = t2;
-        const float nm = fmaxf(run_m[h], t2);
-        run_s[h] = run_s[h] * fast_exp2(run_m[h] - nm) + fast_exp2(t2 - nm);
-        run_m[h] = nm;
+        cur[h][0] = nxt[h][0];
+        cur[h][1] = nxt[h][1];
       }
-      if (kb + 1 < nkb) {
+      logits(kn, nxt);
+      load_k(min(kb + 2, nkb - 1), kn);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float t2 = block_t2(cur[h], lag[h]);
+        store(kb, h, t2);
+        lag[h] = run_m[h];
+        fold(h, t2);
+      }
+    }
+    if (nkb > 1) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float t2 = block_t2(nxt[h], lag[h]);
+        store(nkb - 1, h, t2);
+        fold(h, t2);
+      }
+    }
+    // an overflowed row redoes the item with a per-block max (the exact path)
+    if (__syncthreads_or(!(run_m[0] + fast_log2(run_s[0]) < INFINITY) ||
+                         !(run_m[1] + fast_log2(run_s[1]) < INFINITY))) {
+      for (int kb = 0; kb < nkb; ++kb) {
+        load_k(kb, ka);
+        logits(ka, cur);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          cur[h][0] = nxt[h][0];
-          cur[h][1] = nxt[h][1];
+          const float t2 = block_t2(cur[h], own_max(cur[h]));
+          store(kb, h, t2);
+          if (kb == 0) {
+            run_m[h] = t2;
+            run_s[h] = 1.f;
+          } else {
+            fold(h, t2);
+          }
         }
       }
     }

@@ -246,3 +246,27 @@ def test_full_size_sampled(name):
             assert np.abs(to_f64(r["grads"][1][0, h, keys]) - dk_o).max() <= GRAD_BF16_MAXABS
             assert np.abs(to_f64(r["grads"][2][0, h, keys]) - dv_o).max() <= GRAD_BF16_MAXABS
             log(f"[parity] {name} h={h} kb={kb} dK/dV ok")
+
+
+def test_predictor_extreme_logits_use_the_exact_fallback():
+    # With W = [I; 0], Q_lr and K_lr are the first r columns of Q and K.  Block 0's keys are 0
+    # (its logits are 0), block 5's keys give logits ~150 (log2 units) above block 0's bound:
+    # the fast sweep's shifted exponentials overflow and the item must be redone exactly.
+    n, d, r, bq, bk = 1024, 64, 16, 64, 64
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((1, 1, n, d)).astype(np.float32) * 0.1
+    k = rng.standard_normal((1, 1, n, d)).astype(np.float32) * 0.1
+    q[..., :r] = 1.0
+    k[0, 0, 0:64, :r] = 0.0
+    k[0, 0, 5 * 64:6 * 64, :r] = 48.0
+    w = np.zeros((1, d, r), np.float32)
+    w[0, :r, :r] = np.eye(r)
+    from workloads.generator import bf16_bits_from_f32
+    t = {nm: to_dev(bf16_bits_from_f32(a)) for nm, a in (("q", q), ("k", k), ("w", w))}
+    scores, qlr, klr = dsv.predict(t["q"], t["k"], t["w"], t["w"], q_block=bq, kv_block=bk, return_projections=True)
+    torch.cuda.synchronize()
+    sg = to_f64(scores)[0, 0]
+    ref = O.block_scores_head(to_f64(qlr)[0, 0], to_f64(klr)[0, 0], bq, bk, 1 / 8)
+    assert np.isfinite(sg).all()
+    np.testing.assert_allclose(sg, ref, rtol=2e-4, atol=2e-5)
+    assert np.all(sg[:, 5] > 0.99 * bq)  # block 5 takes essentially all the mass
