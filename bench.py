@@ -29,6 +29,9 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (vendor figure)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak (vendor figure)
+# Transcendental (v_exp_f32) peak: 256 CUs x 4 SIMDs x 8 lanes per cycle (half the non-packed fp32 FMA
+# rate, 16 lanes per SIMD per cycle) x 2.4 GHz.  The predictor needs one exponential per logit.
+EXP_PEAK_T = 256 * 4 * 8 * 2.4e9 / 1e12
 
 
 def log(msg):
@@ -61,12 +64,28 @@ def kernel_units(cfg):
         # dQ (2 units) in the query-parallel kernel (its S and dP are recomputation)
         "attn_bwd_dkdv_kernel": ("mfma", 8.0 * pairs * unit),
         "attn_bwd_dq_kernel": ("mfma", 2.0 * pairs * unit),
-        # predictor sweep: reads Q_lr, K_lr per head and writes the scores (HBM-compulsory bytes)
-        "scores_kernel": ("alu", None),
+        # predictor sweep: one exponential per predicted logit, B*H*N^2 of them
+        "scores_kernel": ("alu", float(cfg.batch * cfg.heads) * cfg.seq_len * cfg.seq_len),
         "select_topk_kernel": ("hbm", 4.0 * cfg.batch * cfg.heads * cfg.nqb * (cfg.nkb + cfg.topk)),
-        "transpose_kernel(v)": ("hbm", 4.0 * elems),
+        # projection of one tensor: read [B,H,N,d] bf16, write [B,H,N,r] bf16
+        "proj_kernel(q)": ("hbm", 2.0 * elems + 2.0 * cfg.batch * cfg.heads * cfg.seq_len * cfg.rank),
         "bwd_pre_kernel": ("hbm", 2.0 * 2 * elems + 12.0 * cfg.batch * cfg.heads * cfg.seq_len),
     }
+
+
+def measured_traffic(cfg, timing_name):
+    """HBM bytes per launch (read + write) of a kernel from the committed counter summary of this
+    workload, or None when there is none or the kernel's sources changed since it was taken."""
+    from dynamic_sparse_attention_dsv_amd.profile_summary import source_hash
+
+    path = os.path.join(ROOT, "profiles", f"{cfg.name.lower()}_kernel_traffic.json")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as fh:
+        rec = json.load(fh).get("kernels", {}).get(timing_name)
+    if rec is None or rec.get("source_sha256") != source_hash(timing_name):
+        return None, None
+    return rec["read_bytes"] + rec["write_bytes"], os.path.relpath(path, ROOT)
 
 
 def cpu_baseline(cfg, inp, target_s):
@@ -200,14 +219,21 @@ def main():
     elif bound == "hbm":
         ach = work / avg_s / 1e9
         roof.update(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS, traffic=None)
+    elif bound == "alu":
+        ach = work / avg_s / 1e12
+        roof.update(bound="alu", achieved=ach, peak=EXP_PEAK_T, unit="Texp/s", frac=ach / EXP_PEAK_T, traffic=None)
     else:
         roof.update(bound=bound, achieved=None, peak=None, unit=None, frac=None, traffic=None)
+    roof["traffic"], roof["traffic_source"] = measured_traffic(cfg, dom)
     # per-kernel rates for the attention kernels
     rates = {}
-    for n in ("attn_fwd_kernel", "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"):
-        if n in kstats:
+    peaks = {"mfma": (MFMA_BF16_PEAK_TFLOPS, 1e12, "TFLOP/s"), "hbm": (HBM_PEAK_GBS, 1e9, "GB/s"),
+             "alu": (EXP_PEAK_T, 1e12, "Texp/s")}
+    for n, (bnd, work) in units.items():
+        if n in kstats and work:
             s = kstats[n][1] / kstats[n][0] * 1e-3
-            rates[n] = {"tflops": units[n][1] / s / 1e12, "frac": units[n][1] / s / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+            pk, scale, unit = peaks[bnd]
+            rates[n] = {"bound": bnd, "achieved": work / s / scale, "unit": unit, "frac": work / s / scale / pk}
 
     dense = None
     if not a.no_dense:

@@ -101,7 +101,7 @@ def project(x: np.ndarray, w: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# 2. predicted block mass ([de] §2.A "kritische KV-Paare", §2.B; [es] §2.A-B)
+# 2. predicted block mass ([de] §2.A, §2.B; [es] §2.A-B)
 # --------------------------------------------------------------------------
 
 

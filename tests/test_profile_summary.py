@@ -1,0 +1,53 @@
+"""Host checks of the rocprofv3 summariser and of how bench.py picks up measured traffic."""
+import json
+import sqlite3
+
+import bench
+from dynamic_sparse_attention_dsv_amd import profile_summary as ps
+from workloads import get_config
+
+KNAME = "void dsv::attn_fwd_bf16_kernel<128, 128>(unsigned short const*, int)"
+
+
+def _db(path, kernels=None, counter=None, values=None):
+    con = sqlite3.connect(path)
+    con.execute("create table top_kernels (name text, total_calls int, total_duration real, average real, "
+                "percentage real)")
+    con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
+    for row in kernels or []:
+        con.execute("insert into top_kernels values (?,?,?,?,?)", row)
+    for name, v in values or []:
+        con.execute("insert into counters_collection values (?,?,?)", (name, counter, v))
+    con.commit()
+    con.close()
+    return str(path)
+
+
+def test_summary_scales_counters_by_the_calibration_copy(tmp_path):
+    kt = _db(tmp_path / "kt.db", kernels=[(KNAME, 2, 84000.0, 42000.0, 90.0),
+                                          ("__amd_rocclr_copyBuffer", 1, 400.0, 400.0, 1.0)])
+    fe = _db(tmp_path / "fe.db", counter="FETCH_SIZE",
+             values=[("__amd_rocclr_copyBuffer", 524288.0), (KNAME, 1000.0), (KNAME, 3000.0)])
+    wr = _db(tmp_path / "wr.db", counter="WRITE_SIZE", values=[("__amd_rocclr_copyBuffer", 1048576.0), (KNAME, 10.0)])
+    cal, table = ps.summarise(kt, fe, wr)
+    assert cal["fetch_scale"] == 2.0 and cal["write_scale"] == 1.0
+    row = [r for r in table if r["kernel"].startswith("attn_fwd_bf16_kernel")][0]
+    assert row["avg_ms"] == 42.0                      # microseconds -> milliseconds
+    assert row["read_bytes"] == 2000.0 * 2 * 1024     # mean over dispatches, x2, KiB -> bytes
+    assert row["write_bytes"] == 10.0 * 1024
+    rec = ps.to_record(cal, table, "cmd", "w")
+    assert rec["kernels"]["attn_fwd_kernel"]["source_sha256"] == ps.source_hash("attn_fwd_kernel")
+    assert "| attn_fwd_bf16_kernel<128, 128> | 2 | 42.000 |" in ps.to_markdown(cal, table, "cmd", "t")
+
+
+def test_bench_reports_traffic_only_for_an_unchanged_kernel(tmp_path, monkeypatch):
+    cfg = get_config("C5")
+    (tmp_path / "profiles").mkdir()
+    rec = {"kernels": {"attn_fwd_kernel": {"read_bytes": 5.0, "write_bytes": 1.0,
+                                           "source_sha256": ps.source_hash("attn_fwd_kernel")},
+                       "attn_bwd_dq_kernel": {"read_bytes": 5.0, "write_bytes": 1.0, "source_sha256": "0" * 64}}}
+    (tmp_path / "profiles" / "c5_kernel_traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic(cfg, "attn_fwd_kernel")[0] == 6.0
+    assert bench.measured_traffic(cfg, "attn_bwd_dq_kernel") == (None, None)   # sources changed since
+    assert bench.measured_traffic(cfg, "scores_kernel") == (None, None)        # never measured
