@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void csc_emit_kernel(const uint32_t* __restric
 // The two query halves' partial dK/dV are summed through LDS at the end.
 
 template <int D, int BQ>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dvec,
     const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ rows, const int32_t* __restrict__ order,
@@ -272,35 +272,26 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
         dp = mfma32(row_frag<D>(os, arow, dc * 16, lane), vf[dc], dp);
       }
       // register vv holds query qh*32 + (vv/8)*16 + g*8 + vv%8 of the chunk: two runs of 8
-      // consecutive queries, read as vectors
-      float lq[16], dq_[16];
+      // consecutive queries.  Each run's lse2 and D are read as vectors right before use, and its
+      // P and dS feed the dV and dK products at once, so only one run's values are live.
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int q0 = qh * 32 + hh * 16 + g * 8;
+      for (int cc = 0; cc < 2; ++cc) {
+        const int q0 = qh * 32 + cc * 16 + g * 8;
         const f32x4 l0 = *reinterpret_cast<const f32x4*>(&ld[q0]);
         const f32x4 l1 = *reinterpret_cast<const f32x4*>(&ld[q0 + 4]);
         const f32x4 d0 = *reinterpret_cast<const f32x4*>(&ld[QR + q0]);
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(&ld[QR + q0 + 4]);
+        float pv[8], dsv_[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lq[hh * 8 + e] = l0[e];
-          lq[hh * 8 + 4 + e] = l1[e];
-          dq_[hh * 8 + e] = d0[e];
-          dq_[hh * 8 + 4 + e] = d1[e];
+        for (int e = 0; e < 8; ++e) {
+          const int vv = cc * 8 + e;
+          const float lq = e < 4 ? l0[e] : l1[e - 4];
+          const float dd = e < 4 ? d0[e] : d1[e - 4];
+          pv[e] = fast_exp2(fmaf(s[vv], c, -lq));
+          dsv_[e] = pv[e] * (dp[vv] - dd);
         }
-      }
-#pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        const float p = fast_exp2(fmaf(s[vv], c, -lq[vv]));
-        s[vv] = p;
-        dp[vv] = p * (dp[vv] - dq_[vv]);
-      }
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int b0 = cc * 8;
-        const bf16x8 pa = cvt8(s[b0], s[b0 + 1], s[b0 + 2], s[b0 + 3], s[b0 + 4], s[b0 + 5], s[b0 + 6], s[b0 + 7]);
-        const bf16x8 da = cvt8(dp[b0], dp[b0 + 1], dp[b0 + 2], dp[b0 + 3], dp[b0 + 4], dp[b0 + 5], dp[b0 + 6],
-                               dp[b0 + 7]);
+        const bf16x8 pa = cvt8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        const bf16x8 da = cvt8(dsv_[0], dsv_[1], dsv_[2], dsv_[3], dsv_[4], dsv_[5], dsv_[6], dsv_[7]);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           dva[dt] = mfma32(pa, tr_frag<D>(os, qh * 32 + cc * 16, dt * 32, lane), dva[dt]);
