@@ -264,13 +264,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
     };
     const int arow = qh * 32 + sigma(c32);
     auto chunk = [&](const uint16_t* qs, const uint16_t* os, const float* ld) {
-      // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys (A rows in sigma order)
+      // Fragment offsets from two bases (see row_base / tr_base); kept opaque so that they are
+      // recomputed here rather than held in registers for the whole loop.
+      const int rb = opaque(row_base<D>(arow, lane));
+      // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys (A rows in sigma order),
+      // each k-step's operands read one step ahead
       f32x16 s = f32x16{}, dp = f32x16{};
+      bf16x8 qa = row_frag_at<D>(qs, rb, 0), oa = row_frag_at<D>(os, rb, 0);
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        s = mfma32(row_frag<D>(qs, arow, dc * 16, lane), kf[dc], s);
-        dp = mfma32(row_frag<D>(os, arow, dc * 16, lane), vf[dc], dp);
+        bf16x8 qn = qa, on = oa;
+        if (dc + 1 < D / 16) {
+          qn = row_frag_at<D>(qs, rb, dc + 1);
+          on = row_frag_at<D>(os, rb, dc + 1);
+        }
+        s = mfma32(qa, kf[dc], s);
+        dp = mfma32(oa, vf[dc], dp);
+        qa = qn;
+        oa = on;
       }
+      const int tb0 = opaque(tr_base<D>(qh * 32, lane, 0)), tb1 = opaque(tr_base<D>(qh * 32, lane, 1));
       // register vv holds query qh*32 + (vv/8)*16 + g*8 + vv%8 of the chunk: two runs of 8
       // consecutive queries.  Each run's lse2 and D are read as vectors right before use, and its
       // P and dS feed the dV and dK products at once, so only one run's values are live.
@@ -292,10 +305,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
         }
         const bf16x8 pa = cvt8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
         const bf16x8 da = cvt8(dsv_[0], dsv_[1], dsv_[2], dsv_[3], dsv_[4], dsv_[5], dsv_[6], dsv_[7]);
+        // rows cc*16.. of the query half: bases move by 16 rows
+        const int o0 = tb0 + cc * 16 * D, o1 = tb1 + cc * 16 * D;
+        bf16x8 ob = tr_frag_at<D>(os, o0, o1, 0), qb = tr_frag_at<D>(qs, o0, o1, 0);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          dva[dt] = mfma32(pa, tr_frag<D>(os, qh * 32 + cc * 16, dt * 32, lane), dva[dt]);
-          dka[dt] = mfma32(da, tr_frag<D>(qs, qh * 32 + cc * 16, dt * 32, lane), dka[dt]);
+          bf16x8 obn = ob, qbn = qb;
+          if (dt + 1 < D / 32) {
+            obn = tr_frag_at<D>(os, o0, o1, dt + 1);
+            qbn = tr_frag_at<D>(qs, o0, o1, dt + 1);
+          }
+          dva[dt] = mfma32(pa, ob, dva[dt]);
+          dka[dt] = mfma32(da, qb, dka[dt]);
+          ob = obn;
+          qb = qbn;
         }
       }
     };

@@ -47,3 +47,11 @@ def test_bias_makes_keys_heavier_and_cube_order_is_a_permutation():
     t, rem = np.divmod(p[:64], 64)
     y, x = np.divmod(rem, 8)
     assert t.max() < 4 and y.max() < 4 and x.max() < 4
+
+
+def test_threaded_generation_gives_the_same_values():
+    cfg = get_config("C2").with_(heads=3, latent=(1, 32, 32))
+    a = make_inputs(cfg, workers=1)
+    b = make_inputs(cfg, workers=3)
+    for nm in a:
+        assert np.array_equal(a[nm], b[nm]), nm

@@ -168,7 +168,10 @@ def make_inputs(cfg: Config, heads: Optional[Iterable[int]] = None, with_grad: O
     Returns q, k, v (and do) as [B', H', N, d] and wq, wk as [H', d, r], in the
     config's storage dtype: float32 arrays for "f32", uint16 bf16 bit patterns
     for "bf16".  Use :func:`widen` for their exact float64 values.  ``workers``
-    > 1 generates heads in parallel processes (same values).
+    > 1 generates heads on that many threads (same values; NumPy's generators
+    and FFTs release the GIL).  Threads rather than forked processes, so that
+    generation is safe inside processes that already run threads of their own
+    (profilers, GPU runtimes).
     """
     if with_grad is None:
         with_grad = cfg.backward
@@ -182,9 +185,9 @@ def make_inputs(cfg: Config, heads: Optional[Iterable[int]] = None, with_grad: O
     out["wk"] = np.empty((len(hs), d, r), dtype=sdt)
     jobs = [(cfg, b, h, with_grad) for b in bs for h in hs]
     if workers > 1 and len(jobs) > 1:
-        import multiprocessing as mp
-        with mp.get_context("fork").Pool(min(workers, len(jobs))) as pool:
-            results = pool.map(_head_job, jobs, chunksize=1)
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(workers, len(jobs))) as pool:
+            results = list(pool.map(_head_job, jobs))
     else:
         results = map(_head_job, jobs)
     for j, t in enumerate(results):
