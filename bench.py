@@ -158,6 +158,7 @@ def main():
     scores = torch.empty((B, H, cfg.nqb, cfg.nkb), dtype=torch.float32, device=dev)
     idx = torch.empty((B, H, cfg.nqb, cfg.topk), dtype=torch.int32, device=dev)
     o, lse = torch.empty_like(t["q"]), torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    o_lo = torch.empty_like(t["q"])  # the forward's O residual, handed to the backward
     dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
     stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -168,9 +169,10 @@ def main():
         if marks: marks[1].record(stream)
         dsv.select_topk(scores, cfg.topk, out=idx, **kw)
         if marks: marks[2].record(stream)
-        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx, workspace=wsf, out=(o, lse), **kw)
+        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx, workspace=wsf, residual=True, out=(o, lse, o_lo), **kw)
         if marks: marks[3].record(stream)
-        dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, idx, workspace=wsb, out=(dq, dk, dv), **kw)
+        dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, idx, o_lo=o_lo, workspace=wsb, out=(dq, dk, dv),
+                            **kw)
         if marks: marks[4].record(stream)
 
     if a.copy_calibration:
@@ -242,13 +244,14 @@ def main():
         _, wsf_d, wsb_d = dsv.workspace_sizes(t["q"], topk=cfg.nkb, rank=cfg.rank, **kw)
         wsb2 = torch.empty(wsb_d, dtype=torch.uint8, device=dev)
         del wsb
-        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_d, workspace=wsf, out=(o, lse), **kw)
+        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_d, workspace=wsf, residual=True, out=(o, lse, o_lo), **kw)
         torch.cuda.synchronize()
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record(stream)
-        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_d, workspace=wsf, out=(o, lse), **kw)
+        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_d, workspace=wsf, residual=True, out=(o, lse, o_lo), **kw)
         e1.record(stream)
-        dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, idx_d, workspace=wsb2, out=(dq, dk, dv), **kw)
+        dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, idx_d, o_lo=o_lo, workspace=wsb2,
+                            out=(dq, dk, dv), **kw)
         e2.record(stream)
         e2.synchronize()
         dfwd, dbwd = e0.elapsed_time(e1), e1.elapsed_time(e2)

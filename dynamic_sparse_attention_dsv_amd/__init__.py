@@ -9,8 +9,8 @@ tensors are not on a GPU, the calls raise.
 Entry points (same names as the C ABI):
   predict(q, k, wq, wk, ...)          -> block_scores [B, H, N/Bq, N/Bk] float32
   select_topk(block_scores, topk)     -> block_idx    [B, H, N/Bq, k]    int32
-  sparse_attn_fwd(q, k, v, idx, ...)  -> (o, lse)
-  sparse_attn_bwd(q, k, v, o, do, lse, idx, ...) -> (dq, dk, dv)
+  sparse_attn_fwd(q, k, v, idx, ...)  -> (o, lse), or (o, lse, o_lo) with residual=True
+  sparse_attn_bwd(q, k, v, o, do, lse, idx, ..., o_lo=None) -> (dq, dk, dv)
 """
 from __future__ import annotations
 
@@ -69,9 +69,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsv_predict": (ctypes.c_int, [P, V, V, V, V, V, S, V, V]),
         "dsv_select_topk": (ctypes.c_int, [P, V, V, V]),
         "dsv_sparse_attn_fwd_workspace_size": (S, [P]),
-        "dsv_sparse_attn_fwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, S, V]),
+        "dsv_sparse_attn_fwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, S, V]),
         "dsv_sparse_attn_bwd_workspace_size": (S, [P]),
-        "dsv_sparse_attn_bwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, V, V, V, S, V]),
+        "dsv_sparse_attn_bwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, V, V, V, V, S, V]),
         "dsv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dsv_last_error": (ctypes.c_char_p, []),
         "dsv_version": (ctypes.c_int32, []),
@@ -194,9 +194,13 @@ def select_topk(scores: torch.Tensor, topk: int, *, q_block: int, kv_block: int 
 
 
 def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_scale: Optional[float] = None,
-                    workspace: Optional[torch.Tensor] = None,
-                    out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Softmax attention over the selected KV blocks only -> (o [B,H,N,d], lse [B,H,N] float32)."""
+                    residual: bool = False, workspace: Optional[torch.Tensor] = None, out=None):
+    """Softmax attention over the selected KV blocks only -> (o [B,H,N,d], lse [B,H,N] float32).
+
+    With ``residual=True`` (bf16 only) also returns o_lo, the bf16 rounding residual of O; handing it
+    to :func:`sparse_attn_bwd` makes the backward's D = rowsum(dO * O) accurate to fp32.
+    ``out`` may supply (o, lse) or (o, lse, o_lo).
+    """
     lib = load_library()
     dev = _dev(q, k, v, block_idx)
     _contig(q, k, v, block_idx)
@@ -206,32 +210,46 @@ def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_
     prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1], sm_scale=sm_scale)
     if tuple(block_idx.shape) != (b, h, n // q_block, prob.topk):
         raise ValueError("block_idx must be [B, H, N/Bq, k]")
+    if residual and q.dtype != torch.bfloat16:
+        raise ValueError("the O residual exists for bf16 problems only")
     ws = _workspace(int(lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(prob))), dev, workspace)
+    o_lo = None
     if out is not None:
-        o, lse = out
+        o, lse = out[0], out[1]
+        if residual:
+            if len(out) < 3:
+                raise ValueError("out must hold (o, lse, o_lo) when residual=True")
+            o_lo = out[2]
     else:
         o = torch.empty_like(q)
         lse = torch.empty((b, h, n), dtype=torch.float32, device=dev)
+    if residual and o_lo is None:
+        o_lo = torch.empty_like(q)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.dsv_sparse_attn_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(block_idx), _p(o), _p(lse), _p(ws),
-                                   nbytes, _stream(dev)), "dsv_sparse_attn_fwd")
-    return o, lse
+    _check(lib.dsv_sparse_attn_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(block_idx), _p(o), _p(lse),
+                                   _p(o_lo), _p(ws), nbytes, _stream(dev)), "dsv_sparse_attn_fwd")
+    return (o, lse, o_lo) if residual else (o, lse)
 
 
 def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block: int = 64,
-                    sm_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                    sm_scale: Optional[float] = None, o_lo: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
                     out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
-    """Gradients (dq, dk, dv) of the sparse attention."""
+    """Gradients (dq, dk, dv) of the sparse attention; ``o_lo`` is the forward's residual (or None)."""
     lib = load_library()
     dev = _dev(q, k, v, o, dout, lse, block_idx)
     _contig(q, k, v, o, dout, lse, block_idx)
+    if o_lo is not None:
+        _contig(o_lo)
+        if o_lo.shape != o.shape or o_lo.dtype != torch.bfloat16:
+            raise ValueError("o_lo must be a bf16 tensor shaped like o")
     b, h, n, d = q.shape
     prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1], sm_scale=sm_scale)
     ws = _workspace(int(lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(prob))), dev, workspace)
     dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    _check(lib.dsv_sparse_attn_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(o), _p(dout), _p(lse), _p(block_idx),
-                                   _p(dq), _p(dk), _p(dv), _p(ws), ws.numel() * ws.element_size(), _stream(dev)),
-           "dsv_sparse_attn_bwd")
+    _check(lib.dsv_sparse_attn_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(o), _p(o_lo), _p(dout), _p(lse),
+                                   _p(block_idx), _p(dq), _p(dk), _p(dv), _p(ws), ws.numel() * ws.element_size(),
+                                   _stream(dev)), "dsv_sparse_attn_bwd")
     return dq, dk, dv
 
 
@@ -268,15 +286,18 @@ class DSVAttention(torch.autograd.Function):
     def forward(ctx, q, k, v, wq, wk, q_block: int, kv_block: int, topk: int, sm_scale=None, pred_scale=None):
         scores = predict(q, k, wq, wk, q_block=q_block, kv_block=kv_block, pred_scale=pred_scale)
         idx = select_topk(scores, topk, q_block=q_block, kv_block=kv_block)
-        o, lse = sparse_attn_fwd(q, k, v, idx, q_block=q_block, kv_block=kv_block, sm_scale=sm_scale)
-        ctx.save_for_backward(q, k, v, o, lse, idx)
+        res = q.dtype == torch.bfloat16
+        out = sparse_attn_fwd(q, k, v, idx, q_block=q_block, kv_block=kv_block, sm_scale=sm_scale, residual=res)
+        o, lse = out[0], out[1]
+        ctx.save_for_backward(q, k, v, o, lse, idx, *out[2:])
         ctx.cfg = (q_block, kv_block, sm_scale)
         ctx.mark_non_differentiable(idx)
         return o, idx
 
     @staticmethod
     def backward(ctx, do, _didx):
-        q, k, v, o, lse, idx = ctx.saved_tensors
+        q, k, v, o, lse, idx, *o_lo = ctx.saved_tensors
         qb, kb, sm = ctx.cfg
-        dq, dk, dv = sparse_attn_bwd(q, k, v, o, do.contiguous(), lse, idx, q_block=qb, kv_block=kb, sm_scale=sm)
+        dq, dk, dv = sparse_attn_bwd(q, k, v, o, do.contiguous(), lse, idx, q_block=qb, kv_block=kb, sm_scale=sm,
+                                     o_lo=o_lo[0] if o_lo else None)
         return dq, dk, dv, None, None, None, None, None, None, None

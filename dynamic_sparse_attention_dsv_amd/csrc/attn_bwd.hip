@@ -31,6 +31,7 @@ namespace dsv {
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(const uint16_t* __restrict__ o,
+                                                           const uint16_t* __restrict__ o_lo,
                                                            const uint16_t* __restrict__ dout,
                                                            const float* __restrict__ lse, float* __restrict__ dvec,
                                                            float* __restrict__ lse2, int rows) {
@@ -40,10 +41,13 @@ __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(const uint16_t* __res
   float acc = 0.f;
   if (row < rows) {
     const u32x4 a = ld16(o + (size_t)row * D + c * 8), b = ld16(dout + (size_t)row * D + c * 8);
+    const u32x4 r = o_lo ? ld16(o_lo + (size_t)row * D + c * 8) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
-      acc = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), acc);
+    for (int e = 0; e < 4; ++e) {  // O = o + o_lo (the residual is 0 without it)
+      const float olo = __uint_as_float(a[e] << 16) + __uint_as_float(r[e] << 16);
+      const float ohi = __uint_as_float(a[e] & 0xffff0000u) + __uint_as_float(r[e] & 0xffff0000u);
+      acc = fmaf(olo, __uint_as_float(b[e] << 16), acc);
+      acc = fmaf(ohi, __uint_as_float(b[e] & 0xffff0000u), acc);
     }
   }
 #pragma unroll
@@ -422,13 +426,26 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
     // one 32-key tile at a time: S^T, dP^T, dS^T, then its two 16-key chunks of dQ^T += K^T dS^T.
     // dS is split into bf16 hi + lo parts: K's large entries would otherwise amplify dS's bf16
     // rounding into dQ errors comparable to dQ's own bf16 storage rounding.
+    // Fragment offsets come from one base per run (row_base / tr_base), recomputed per block,
+    // and each k-step's operands are read one step ahead.
+    const int rb = opaque(row_base<D>(arow, lane));
+    const int kb0 = opaque(tr_base<D>(0, lane, 0)), kb1 = opaque(tr_base<D>(0, lane, 1));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16 s = f32x16{}, dp = f32x16{};
+      const int rt = rb + t * 32 * D;
+      bf16x8 ka = row_frag_at<D>(Kc, rt, 0), va = row_frag_at<D>(Vc, rt, 0);
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        s = mfma32(row_frag<D>(Kc, t * 32 + arow, dc * 16, lane), qf[dc], s);
-        dp = mfma32(row_frag<D>(Vc, t * 32 + arow, dc * 16, lane), of[dc], dp);
+        bf16x8 kn = ka, vn = va;
+        if (dc + 1 < D / 16) {
+          kn = row_frag_at<D>(Kc, rt, dc + 1);
+          vn = row_frag_at<D>(Vc, rt, dc + 1);
+        }
+        s = mfma32(ka, qf[dc], s);
+        dp = mfma32(va, of[dc], dp);
+        ka = kn;
+        va = vn;
       }
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
@@ -443,11 +460,15 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
         const bf16x8 lo = cvt8(dp[b0] - (float)hi[0], dp[b0 + 1] - (float)hi[1], dp[b0 + 2] - (float)hi[2],
                                dp[b0 + 3] - (float)hi[3], dp[b0 + 4] - (float)hi[4], dp[b0 + 5] - (float)hi[5],
                                dp[b0 + 6] - (float)hi[6], dp[b0 + 7] - (float)hi[7]);
+        const int o0 = kb0 + cc * 16 * D, o1 = kb1 + cc * 16 * D;
+        bf16x8 kt = tr_frag_at<D>(Kc, o0, o1, 0);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16x8 ka = tr_frag<D>(Kc, cc * 16, dt * 32, lane);
-          acc[dt] = mfma32(ka, hi, acc[dt]);
-          acc[dt] = mfma32(ka, lo, acc[dt]);
+          bf16x8 ktn = kt;
+          if (dt + 1 < D / 32) ktn = tr_frag_at<D>(Kc, o0, o1, dt + 1);
+          acc[dt] = mfma32(kt, hi, acc[dt]);
+          acc[dt] = mfma32(kt, lo, acc[dt]);
+          kt = ktn;
         }
       }
     }
@@ -549,13 +570,14 @@ __global__ void attn_bwd_dkdv_f32_kernel(const float* __restrict__ q, const floa
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* dout, const float* lse, float* dvec, float* lse2,
-                               int rows, int d, hipStream_t st) {
+hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* o_lo, const uint16_t* dout, const float* lse,
+                               float* dvec, float* lse2, int rows, int d, hipStream_t st) {
   const int lanes = rows * (d / 8);
   dim3 grid((lanes + 255) / 256);
-  if (d == 64) hipLaunchKernelGGL(bwd_pre_bf16_kernel<64>, grid, dim3(256), 0, st, o, dout, lse, dvec, lse2, rows);
+  if (d == 64)
+    hipLaunchKernelGGL(bwd_pre_bf16_kernel<64>, grid, dim3(256), 0, st, o, o_lo, dout, lse, dvec, lse2, rows);
   else if (d == 128)
-    hipLaunchKernelGGL(bwd_pre_bf16_kernel<128>, grid, dim3(256), 0, st, o, dout, lse, dvec, lse2, rows);
+    hipLaunchKernelGGL(bwd_pre_bf16_kernel<128>, grid, dim3(256), 0, st, o, o_lo, dout, lse, dvec, lse2, rows);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -25,11 +25,14 @@
 
 namespace dsv {
 
-template <int D, int BQ>
+// SPLIT: P enters O += P V as two bf16 parts (hi + lo), carrying O to about 16 bits; chosen
+// when the caller asks for O's rounding residual, i.e. when a backward will use O.
+template <int D, int BQ, bool SPLIT>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse, int n, int topk,
-    int nwg, float c /* sm_scale * log2(e) */) {
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse,
+    uint16_t* __restrict__ o_lo /* optional rounding residual of O */, int n, int topk, int nwg,
+    float c /* sm_scale * log2(e) */) {
   constexpr int WAVES = BQ / 32;
   constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
   // separate arrays per buffer: with one array the compiler cannot tell that the
@@ -74,45 +77,92 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
 
   // one selected KV block: scores from Kc, online softmax, O^T += V^T P^T from Vc
   auto block = [&](const uint16_t* Kc, const uint16_t* Vc) {
-    // S^T = K Q^T: two 32-key tiles, K rows read in sigma order
+    // fragment offsets from one base per run (row_base / tr_base), recomputed per block
+    const int rb = opaque(row_base<D>(arow, lane));
+    // S^T = K Q^T: two 32-key tiles (rows t*32 + sigma order: base + t*32*D), each k-step's
+    // K operand read one step ahead
     f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = f32x16{};
+      bf16x8 ka = row_frag_at<D>(Kc, rb + t * 32 * D, 0);
 #pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) s[t] = mfma32(row_frag<D>(Kc, t * 32 + arow, dc * 16, lane), qf[dc], s[t]);
+      for (int dc = 0; dc < D / 16; ++dc) {
+        bf16x8 kn = ka;
+        if (dc + 1 < D / 16) kn = row_frag_at<D>(Kc, rb + t * 32 * D, dc + 1);
+        s[t] = mfma32(ka, qf[dc], s[t]);
+        ka = kn;
+      }
     }
-    // online softmax (log2 domain); lane owns one query, 32 of the block's 64 keys
-    float mx = s[0][0];
+    // online softmax (log2 domain); lane owns one query, 32 of the block's 64 keys.
+    // Row maximum by a tree over the 32 values.
+    float mx8[8];
 #pragma unroll
-    for (int vv = 1; vv < 16; ++vv) mx = fmaxf(mx, s[0][vv]);
+    for (int e = 0; e < 8; ++e)
+      mx8[e] = fmaxf(fmaxf(s[0][e], s[0][e + 8]), fmaxf(s[1][e], s[1][e + 8]));
 #pragma unroll
-    for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[1][vv]);
-    mx = max_xor32(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+      for (int e = 0; e < w; ++e) mx8[e] = fmaxf(mx8[e], mx8[e + w]);
+    const float mx = max_xor32(mx8[0]) * c;
+    // Lazy rescaling: the running shift m_run only moves when the block's maximum exceeds it by
+    // more than 8 (log2 units), so exponentials stay below 2^8 and the accumulator and row sum
+    // are rescaled rarely.  Any shift gives the same O = acc / l; the choice only moves rounding.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        s[t][vv] = fast_exp2(fmaf(s[t][vv], c, -m_new));
+        s[t][vv] = fast_exp2(fmaf(s[t][vv], c, -m_run));
         psum += s[t][vv];
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-    // O^T += V^T P^T: V^T operands by transposed reads of the row-major V tile;
-    // P^T chunk cc = registers (cc%2)*8.. of tile cc/2
+    l_run += psum;
+    // O^T += V^T P^T: V^T operands by transposed reads of the row-major V tile (rows cc*16..:
+    // bases + cc*16*D); P^T chunk cc = registers (cc%2)*8.. of tile cc/2.  With SPLIT, P enters
+    // as two bf16 parts: hi = P with its low 16 bits cleared (exact), lo = bf16(P - hi), so the
+    // product carries P to about 16 bits.  A single bf16 rounding of P puts errors of up to
+    // 2^-9 P into O -- fine for O itself, too coarse for the backward's D = rowsum(dO * O),
+    // which the dQ product multiplies by K.
+    const int vb0 = opaque(tr_base<D>(0, lane, 0)), vb1 = opaque(tr_base<D>(0, lane, 1));
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const f32x16& st = s[cc >> 1];
       const int b0 = (cc & 1) * 8;
-      const bf16x8 pb = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
-                             st[b0 + 7]);
+      bf16x8 ph, pl;
+      if constexpr (SPLIT) {
+        float lo[8];
+        u32x4 hw;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(tr_frag<D>(Vc, cc * 16, dt * 32, lane), pb, oacc[dt]);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t u0 = __float_as_uint(st[b0 + 2 * e]) & 0xffff0000u;
+          const uint32_t u1 = __float_as_uint(st[b0 + 2 * e + 1]) & 0xffff0000u;
+          hw[e] = (u0 >> 16) | u1;
+          lo[2 * e] = st[b0 + 2 * e] - __uint_as_float(u0);
+          lo[2 * e + 1] = st[b0 + 2 * e + 1] - __uint_as_float(u1);
+        }
+        ph = as_bf16x8(hw);
+        pl = cvt8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+      } else {
+        ph = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6], st[b0 + 7]);
+      }
+      const int o0 = vb0 + cc * 16 * D, o1 = vb1 + cc * 16 * D;
+      bf16x8 va = tr_frag_at<D>(Vc, o0, o1, 0);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        bf16x8 vn = va;
+        if (dt + 1 < D / 32) vn = tr_frag_at<D>(Vc, o0, o1, dt + 1);
+        oacc[dt] = mfma32(va, ph, oacc[dt]);
+        if constexpr (SPLIT) oacc[dt] = mfma32(va, pl, oacc[dt]);
+        va = vn;
+      }
     }
   };
 
@@ -131,14 +181,22 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   const float l = l_run + xor32(l_run);
   const float inv = 1.f / l;
   uint16_t* orow = o + head + (size_t)qrow * D;
+  uint16_t* lrow = SPLIT ? o_lo + head + (size_t)qrow * D : nullptr;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int vq = 0; vq < 4; ++vq) {
       const int d0 = dt * 32 + vq * 8 + g * 4;
-      u32x2 pk = {pack_bf16x2(oacc[dt][vq * 4] * inv, oacc[dt][vq * 4 + 1] * inv),
-                  pack_bf16x2(oacc[dt][vq * 4 + 2] * inv, oacc[dt][vq * 4 + 3] * inv)};
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = oacc[dt][vq * 4 + e] * inv;
+      const u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
       *reinterpret_cast<u32x2*>(orow + d0) = pk;
+      if constexpr (SPLIT) {  // residual x - bf16(x), itself rounded to bf16
+        const u32x2 rk = {pack_bf16x2(x[0] - __uint_as_float(pk[0] << 16), x[1] - __uint_as_float(pk[0] & 0xffff0000u)),
+                          pack_bf16x2(x[2] - __uint_as_float(pk[1] << 16), x[3] - __uint_as_float(pk[1] & 0xffff0000u))};
+        *reinterpret_cast<u32x2*>(lrow + d0) = rk;
+      }
     }
   if (g == 0) lse[(size_t)bh * n + qrow] = (m_run + fast_log2(l)) * kLn2;
 }
@@ -184,14 +242,18 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restric
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                                uint16_t* o, float* lse, int bh, int n, int d, int bq, int topk, float sm_scale,
-                                hipStream_t st) {
+                                uint16_t* o, float* lse, uint16_t* o_lo, int bh, int n, int d, int bq, int topk,
+                                float sm_scale, hipStream_t st) {
   const int nwg = bh * (n / bq);
   const float c = sm_scale * kLog2e;
 #define FWD(D_, BQ_)                                                                                      \
   if (d == D_ && bq == BQ_) {                                                                             \
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, idx, o,  \
-                       lse, n, topk, nwg, c);                                                             \
+    if (o_lo)                                                                                             \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, true>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, idx, \
+                         o, lse, o_lo, n, topk, nwg, c);                                                  \
+    else                                                                                                  \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, false>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, \
+                         idx, o, lse, o_lo, n, topk, nwg, c);                                             \
     return hipGetLastError();                                                                             \
   }
   FWD(64, 64) FWD(64, 128) FWD(128, 64) FWD(128, 128)

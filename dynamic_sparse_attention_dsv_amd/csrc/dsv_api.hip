@@ -91,6 +91,13 @@ dsv_status check_ptr(const void* p, const char* name, size_t align = 16) {
   return DSV_OK;
 }
 
+// The optional rounding residual of O: bf16 problems only, 16-byte aligned when given.
+dsv_status check_residual(const Prob& o, const void* o_lo) {
+  if (!o_lo) return DSV_OK;
+  if (o.dtype != DSV_BF16) return fail(DSV_ERR_INVALID_ARGUMENT, "o_lo must be NULL for float32 problems");
+  return check_ptr(o_lo, "o_lo");
+}
+
 dsv_status hip_status(hipError_t e, const char* where) {
   if (e == hipSuccess) return DSV_OK;
   return fail(DSV_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
@@ -303,7 +310,7 @@ size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p) {
 }
 
 dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
-                               const int32_t* block_idx, void* o_ptr, float* lse, void* workspace,
+                               const int32_t* block_idx, void* o_ptr, float* lse, void* o_lo, void* workspace,
                                size_t workspace_bytes, void* stream) {
   g_err.clear();
   Prob o;
@@ -316,6 +323,7 @@ dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* 
   TRY(check_ptr(block_idx, "block_idx", 4));
   TRY(check_ptr(o_ptr, "o"));
   TRY(check_ptr(lse, "lse"));
+  TRY(check_residual(o, o_lo));
   const size_t need = fwd_ws_bytes(o);
   if (need) {
     TRY(check_ptr(workspace, "workspace", kWsAlign));
@@ -326,7 +334,8 @@ dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* 
   if (o.dtype == DSV_BF16) {
     TRY_HIP(dsv::launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                       static_cast<const uint16_t*>(v), block_idx,
-                                      static_cast<uint16_t*>(o_ptr), lse, o.bh(), o.n, o.d, o.bq, o.k, o.sm, st),
+                                      static_cast<uint16_t*>(o_ptr), lse, static_cast<uint16_t*>(o_lo), o.bh(), o.n,
+                                      o.d, o.bq, o.k, o.sm, st),
             "attn_fwd_kernel");
   } else {
     TRY_HIP(dsv::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
@@ -343,7 +352,7 @@ size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p) {
 }
 
 dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v, const void* o_ptr,
-                               const void* dout, const float* lse, const int32_t* block_idx, void* dq, void* dk,
+                               const void* o_lo, const void* dout, const float* lse, const int32_t* block_idx, void* dq, void* dk,
                                void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   Prob o;
@@ -354,6 +363,7 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
   const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
   for (int i = 0; i < 9; ++i) TRY(check_ptr(ptrs[i], names[i]));
   TRY(check_ptr(block_idx, "block_idx", 4));
+  TRY(check_residual(o, o_lo));
   TRY(check_ptr(workspace, "workspace", kWsAlign));
   const BwdWs w = bwd_ws(o);
   if (workspace_bytes < w.total)
@@ -371,8 +381,8 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
     const uint16_t* do16 = static_cast<const uint16_t*>(dout);
     float* lse2 = at<float>(workspace, w.lse2);
-    TRY_HIP(dsv::launch_bwd_pre_bf16(static_cast<const uint16_t*>(o_ptr), do16, lse, dvec, lse2, o.bh() * o.n, o.d,
-                                     st), "bwd_pre_kernel");
+    TRY_HIP(dsv::launch_bwd_pre_bf16(static_cast<const uint16_t*>(o_ptr), static_cast<const uint16_t*>(o_lo), do16,
+                                     lse, dvec, lse2, o.bh() * o.n, o.d, st), "bwd_pre_kernel");
     TRY_HIP(dsv::launch_bwd_dkdv_bf16(q16, k16, v16, do16, lse2, dvec, col_ptr, rows, order,
                                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), o.bh(), o.n, o.d, o.bq,
                                       o.k, o.sm, st), "attn_bwd_dkdv_kernel");

@@ -26,14 +26,14 @@ hipError_t launch_select_topk(const float* scores, int32_t* idx, int rows, int n
 
 // forward
 hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                                uint16_t* o, float* lse, int bh, int n, int d, int bq, int topk, float sm_scale,
+                                uint16_t* o, float* lse, uint16_t* o_lo, int bh, int n, int d, int bq, int topk, float sm_scale,
                                 hipStream_t st);
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* idx, float* o,
                                float* lse, int bh, int n, int d, int bq, int bk, int topk, float sm_scale,
                                hipStream_t st);
 
 // backward and helpers
-hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* dout, const float* lse, float* dvec, float* lse2,
+hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* o_lo, const uint16_t* dout, const float* lse, float* dvec, float* lse2,
                                int rows, int d, hipStream_t st);
 hipError_t launch_bwd_pre_f32(const float* o, const float* dout, float* dvec, int rows, int d, hipStream_t st);
 hipError_t launch_csc(const int32_t* idx, uint32_t* bitmap, int32_t* counts, int32_t* col_ptr, int32_t* rows,

@@ -5,7 +5,7 @@
 // §2.A) train per-head low-rank matrices W^Q_lr, W^K_lr whose product
 // approximates Q K^T, and use them to find the critical KV pairs -- those that
 // carry most of the attention score -- without materialising the full matrix
-// (§2.B "Fused MM & Top-K": no O(S^2) intermediate in HBM).  The quantity
+// (§2.B, the fused matmul and top-k: no O(S^2) intermediate in HBM).  The quantity
 // computed here is the predicted softmax mass of each query block on each KV
 // block, summed over the block's rows:
 //   score[qb, kb] = sum_{i in qb} sum_{j in kb} exp(l_ij - LSE_i),

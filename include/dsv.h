@@ -65,7 +65,7 @@ typedef enum { DSV_F32 = 0, DSV_BF16 = 1 } dsv_dtype;
  * The problem.  Sizes follow the pages' statement: per attention head
  * ([es] §2.A: the predictor approximates Q K^T of each head independently),
  * queries grouped into blocks of consecutive tokens that share one selection
- * ([de] §2.B / [es] §2.B "Query Grouping"), keys grouped into KV blocks that are
+ * ([de] §2.B; [es] §2.B, query grouping), keys grouped into KV blocks that are
  * the unit of selection, and k blocks kept per query block ([de] §2.B top-k).
  *
  *   batch, heads        B, H >= 1
@@ -104,8 +104,8 @@ typedef struct {
 size_t dsv_predict_workspace_size(const dsv_problem* p);
 
 /*
- * dsv_predict -- low-rank sparsity predictor ([es] §2.A "Estimadores de Baja
- * Rango"; [de] §2.A stage 2, §2.B "Fused MM & Top-K"; [de] §2.B query grouping).
+ * dsv_predict -- low-rank sparsity predictor ([es] §2.A; [de] §2.A;
+ * [de] §2.B, the fused matmul and top-k; [de] §2.B query grouping).
  *
  *   Q_lr = round(Q Wq[h]),  K_lr = round(K Wk[h])        (round = to dtype, RNE)
  *   l_ij = pred_scale * <Q_lr_i, K_lr_j>                  (all j: no causal mask)
@@ -127,7 +127,7 @@ dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const
                        float* block_scores, void* stream);
 
 /*
- * dsv_select_topk -- critical-KV selection ([de] §2.B "Top-k-Selektion";
+ * dsv_select_topk -- critical-KV selection ([de] §2.B, top-k selection;
  * [es] §2.B).  For every (b, h, qb) the k KV blocks with the largest
  * block_scores, ties broken toward the smaller block index, written ascending
  * (distinct indices).  Scores are compared as IEEE floats; a NaN sorts above +inf.
@@ -144,8 +144,8 @@ size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);
 
 /*
  * dsv_sparse_attn_fwd -- exact softmax attention over the selected KV blocks
- * only ([es] §3 "kernels ... para estimación y atención dispersa"; [de] §2.A
- * stage 2 sparse training).  For each query row i of block qb, with
+ * only (the sparse attention kernels of [es] §2.B and [de] §2.B, used for
+ * sparse training, [de] §2.A stage 2).  For each query row i of block qb, with
  * J = the keys of the blocks in block_idx[b,h,qb]:
  *   s_ij = sm_scale <q_i, k_j>,  O_i = sum_{j in J} softmax_J(s_i)_j v_j,
  *   lse_i = log sum_{j in J} exp(s_ij)   (natural log)
@@ -156,10 +156,19 @@ size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);
  *
  *   q, k, v     [B, H, N, d] inputs;  block_idx [B, H, N/Bq, k]
  *   o           [B, H, N, d] output (dtype);  lse [B, H, N] float32 output
- *   workspace   >= dsv_sparse_attn_fwd_workspace_size(p) bytes (holds V^T)
+ *   o_lo        optional [B, H, N, d] bf16 output, or NULL.  DSV_BF16 only (must
+ *               be NULL for DSV_F32).  When given, the forward computes P V
+ *               with P split into two bf16 parts (O to about 16 bits, at the
+ *               cost of extra matrix work) and writes the rounding residual
+ *               bf16(O - o) here, so that o + o_lo carries O to ~16 bits.
+ *               Passing it on to dsv_sparse_attn_bwd makes the backward's row
+ *               term D = rowsum(dO o O) accurate instead of limited by bf16
+ *               rounding, which otherwise dominates dQ's error.  Pass it for
+ *               training; an inference forward leaves it NULL.
+ *   workspace   >= dsv_sparse_attn_fwd_workspace_size(p) bytes (currently 0)
  */
 dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
-                               const int32_t* block_idx, void* o, float* lse, void* workspace,
+                               const int32_t* block_idx, void* o, float* lse, void* o_lo, void* workspace,
                                size_t workspace_bytes, void* stream);
 
 /* Workspace bytes dsv_sparse_attn_bwd needs (0 if the problem is invalid). */
@@ -167,7 +176,7 @@ size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p);
 
 /*
  * dsv_sparse_attn_bwd -- gradients of the sparse attention (the method trains
- * with it: [de] §2.A stage 2; [es] §2.A fase 2).  With P the sparse softmax of
+ * with it: [de] §2.A stage 2; [es] §2.A phase 2).  With P the sparse softmax of
  * the forward and dO = dout:
  *   dV_J += P^T dO,  dP = dO V_J^T,  dS = P o (dP - D),  D_i = sum_c dO_ic O_ic,
  *   dQ = sm_scale dS K_J,  dK_J += sm_scale dS^T Q.
@@ -175,11 +184,13 @@ size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p);
  * No gradient flows to the predictor or to block_idx.
  *
  *   q, k, v, o, dout  [B, H, N, d];  lse [B, H, N];  block_idx [B, H, N/Bq, k]
+ *   o_lo              the forward's o_lo output, or NULL (then D uses o alone).
+ *                     DSV_BF16 only; must be NULL for DSV_F32.
  *   dq, dk, dv        [B, H, N, d] outputs (dtype), fully overwritten
  *   workspace         >= dsv_sparse_attn_bwd_workspace_size(p) bytes
  */
 dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
-                               const void* o, const void* dout, const float* lse,
+                               const void* o, const void* o_lo, const void* dout, const float* lse,
                                const int32_t* block_idx, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, void* stream);
 

@@ -17,13 +17,13 @@ The path, in the pages' order:
   1. per-head low-rank predictor matrices W^Q_lr, W^K_lr whose product
      approximates Q K^T of that head ([es] §2.A; [de] §2.A);
   2. the predicted attention mass of each (query group, KV block) pair, computed
-     without keeping the full N x N matrix ([de] §2.A, §2.B "Fused MM & Top-K";
+     without keeping the full N x N matrix ([de] §2.A; §2.B, the fused matmul and top-k;
      [es] §2.B);
   3. top-k selection of the critical KV blocks per query group ([de] §2.B;
-     [es] §2.B); neighbouring queries form one group ([es] §2.B "Query
-     Grouping"; [de] §2.B);
+     [es] §2.B); neighbouring queries form one group ([es] §2.B, query
+     grouping; [de] §2.B);
   4. exact softmax attention restricted to the selected KV blocks, forward and
-     backward, because the method trains with it ([es] §3; [de] §2.A "Stufe 2").
+     backward, because the method trains with it ([es] §3; [de] §2.A, stage 2).
 
 Readings where the pages are silent (each is listed again in the design doc):
   R1 the predictor acts on each head's Q and K: Q_lr = Q W^Q_lr, K_lr = K W^K_lr
@@ -153,7 +153,7 @@ def predict(q, k, wq, wk, bq: int, bk: int, pred_scale: float, dtype: str):
 
 def representative_scores_head(q_lr: np.ndarray, k_lr: np.ndarray, bq: int, bk: int, pred_scale: float,
                                rep: int = 0) -> np.ndarray:
-    """Representative-row variant ([de] §2.B "Query Grouping"): the group's estimate is the
+    """Representative-row variant ([de] §2.B, query grouping): the group's estimate is the
     predicted softmax mass of its row ``rep`` alone -> [nqb, nkb] (each row sums to 1)."""
     n = q_lr.shape[0]
     _check_blocks(n, bq, bk)
@@ -162,7 +162,7 @@ def representative_scores_head(q_lr: np.ndarray, k_lr: np.ndarray, bq: int, bk: 
 
 
 # --------------------------------------------------------------------------
-# 3. top-k selection ([de] §2.B "Top-k-Selektion"; [es] §2.B)
+# 3. top-k selection ([de] §2.B, top-k selection; [es] §2.B)
 # --------------------------------------------------------------------------
 
 
@@ -194,7 +194,7 @@ def topk_gap(scores: np.ndarray, k: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# 4. sparse attention over the selected blocks ([es] §3; [de] §2.A "Stufe 2")
+# 4. sparse attention over the selected blocks ([es] §3; [de] §2.A, stage 2)
 # --------------------------------------------------------------------------
 
 

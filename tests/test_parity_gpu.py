@@ -30,20 +30,25 @@ def _scale(d):
     return 1.0 / np.sqrt(d)
 
 
-def _run_gpu_path(cfg, inp, idx_fed=None):
-    """predict -> select (GPU); forward/backward with `idx_fed` (or the GPU's own selection)."""
+def _run_gpu_path(cfg, inp, idx_fed=None, residual=True):
+    """predict -> select (GPU); forward/backward with `idx_fed` (or the GPU's own selection).
+
+    bf16 runs hand the forward's O residual to the backward unless residual=False."""
     t = {k: to_dev(v) for k, v in inp.items()}
     scores, qlr, klr = dsv.predict(t["q"], t["k"], t["wq"], t["wk"], q_block=cfg.q_block, kv_block=cfg.kv_block,
                                    return_projections=True)
     idx = dsv.select_topk(scores, cfg.topk, q_block=cfg.q_block, kv_block=cfg.kv_block)
     use = idx if idx_fed is None else to_dev(idx_fed)
-    o, lse = dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], use, q_block=cfg.q_block, kv_block=cfg.kv_block)
+    res = residual and cfg.dtype == "bf16"
+    out = dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], use, q_block=cfg.q_block, kv_block=cfg.kv_block, residual=res)
+    o, lse = out[0], out[1]
+    o_lo = out[2] if res else None
     grads = None
     if "do" in t:
         grads = dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, use, q_block=cfg.q_block,
-                                    kv_block=cfg.kv_block)
+                                    kv_block=cfg.kv_block, o_lo=o_lo)
     torch.cuda.synchronize()
-    return dict(t=t, scores=scores, qlr=qlr, klr=klr, idx=idx, o=o, lse=lse, grads=grads)
+    return dict(t=t, scores=scores, qlr=qlr, klr=klr, idx=idx, o=o, lse=lse, o_lo=o_lo, grads=grads)
 
 
 # ------------------------------------------------------------------ C1: tiny fp32, full path
@@ -149,6 +154,42 @@ def test_c2_bf16_all_heads():
 
 def test_c3_bf16_sampled_heads():
     _bf16_config_check("C3", [0, 23])
+
+
+def test_o_residual_and_backward_without_it():
+    # Asked for O's residual, the forward carries O to ~16 bits: o + o_lo is closer to the oracle's
+    # O than the plain forward's o.  The two forwards share the softmax statistics (lse is
+    # identical), so the two backwards differ only through D = rowsum(dO * O):
+    # dD_i = sum_c dO_ic ((o + o_lo) - o_plain)_ic.  dV does not depend on D, and since the sparse
+    # softmax row P_i sums to 1, dQ moves by at most sm_scale * |dD_i| * max_{j selected} |K_jc|
+    # (+ one bf16 ulp of each stored result).
+    cfg = get_config("C2").with_(heads=4)
+    log("[parity] O residual and backward without it (C2, 4 heads)")
+    inp = make_inputs(cfg)
+    x = {k: widen(v) for k, v in inp.items()}
+    sc = _scale(cfg.head_dim)
+    scores_o, _, _ = O.predict(x["q"], x["k"], x["wq"], x["wk"], cfg.q_block, cfg.kv_block, sc, "bf16")
+    idx_o = O.select_topk(scores_o, cfg.topk)
+    r = _run_gpu_path(cfg, inp, idx_fed=idx_o, residual=True)
+    n = _run_gpu_path(cfg, inp, idx_fed=idx_o, residual=False)
+    assert torch.equal(r["lse"], n["lse"])
+    o_o, _ = O.sparse_attn_fwd(x["q"], x["k"], x["v"], idx_o, cfg.q_block, cfg.kv_block, sc)
+    o_hi, o_lo, o_nr = to_f64(r["o"]), to_f64(r["o_lo"]), to_f64(n["o"])
+    assert np.all(np.abs(o_lo) <= 0.5 * bf16_ulp(np.abs(o_hi)) * 1.0001)
+    e_plain, e_full = np.abs(o_nr - o_o).max(), np.abs(o_hi + o_lo - o_o).max()
+    log(f"[parity] O max-abs error: plain forward {e_plain:.3e}, o + o_lo {e_full:.3e}")
+    assert e_full < 0.25 * e_plain
+    assert np.abs(o_hi - o_o).max() <= FWD_BF16_MAXABS
+    assert torch.equal(r["grads"][2], n["grads"][2])  # dV
+    dd = (x["do"] * (o_hi + o_lo - o_nr)).sum(-1)  # [B, H, N]
+    kmax = np.zeros_like(x["q"])
+    for h in range(cfg.heads):
+        for qb in range(cfg.nqb):
+            keys = O.selected_keys(idx_o[0, h, qb], cfg.kv_block)
+            kmax[0, h, qb * cfg.q_block:(qb + 1) * cfg.q_block] = np.abs(x["k"][0, h][keys]).max(0)
+    a, b = to_f64(r["grads"][0]), to_f64(n["grads"][0])
+    bound = sc * (np.abs(dd)[..., None] + 1e-5) * kmax + bf16_ulp(np.maximum(np.abs(a), np.abs(b)))
+    assert np.all(np.abs(a - b) <= bound)
 
 
 # ------------------------------------------------------------------ small shapes: batch > 1, every instance, k = all

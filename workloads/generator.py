@@ -4,7 +4,7 @@ What the inputs stand in for: the DSV explainer pages (gist.science/de/paper/
 2502.07590, "Technische Zusammenfassung" §1 and §3; Spanish version §1) state
 that attention in video DiTs is dominated by a small, dynamic, non-local set
 of critical key-value pairs, and that tokens adjacent in the 3D latent grid
-tend to share them (§2.B "Query Grouping").  No activations of a trained model
+tend to share them (§2.B, query grouping).  No activations of a trained model
 are available, so the recipe below builds tensors with that structure from
 seeded Gaussian noise:
 
