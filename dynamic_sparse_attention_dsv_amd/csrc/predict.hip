@@ -13,14 +13,14 @@
 //
 // gfx950 design (bf16):
 //  * projection: one MFMA 16x16x32 GEMM per 16-row tile, W^T held in registers;
-//  * scores: persistent workgroups of 4 waves; each work item is 128 query rows
-//    of one head.  Each wave sweeps every KV block once: a 32x32x16 MFMA
-//    produces 32 rows x 64 keys of logits, the lane-local block max, exp2 and
-//    sum give the block's log-mass t_i,kb (log2 domain), and an online
-//    log-sum-exp over blocks gives LSE_i.  t_i,kb goes to a per-workgroup
-//    scratch of nkb x 128 floats (never N x N); after the sweep the same
-//    workgroup turns it into block scores.  The sweep is bound by the vector
-//    ALU (one exp2 per logit), not by MFMA or memory.
+//  * scores: persistent workgroups of 4 waves; each work item is 256 query rows
+//    of one head, 64 per wave.  Each wave sweeps every KV block once: 32x32x16
+//    MFMAs with the scale folded into the query operand produce the logits in
+//    log2 units, and 2^l summed over the block's 64 keys gives the row's block
+//    mass.  Block masses go to a per-workgroup scratch of nkb x 256 floats
+//    (never N x N); the row totals are their sums, and after the sweep the same
+//    workgroup divides and sums them into block scores.  The sweep is bound by
+//    the vector ALU (one exp2 and one add per logit), not by MFMA or memory.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -100,9 +100,17 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
   // scores: [BH, n/BQ, nkb].  pc = pred_scale * log2(e).
   // Each wave owns 64 query rows (two 32-row halves): every K_lr fragment it loads feeds
   // two MFMA tiles, halving the K_lr traffic per logit.
+  //
+  // The scale pc is folded into the MFMA: the query operand is pc * Q_lr as two bf16 parts
+  // (hi = bf16(pc q), lo = bf16(pc q - hi); together exact to ~2^-18), so each MFMA result is
+  // already a logit in log2 units.  The fast sweep then takes 2^logit with no shift and sums
+  // block masses linearly: one exp and one add per logit.  That is exact (up to rounding) for
+  // rows whose total mass T = sum_j 2^l_ij lies in [2^-100, fp32 max]; an item holding any
+  // other row is redone with a per-block maximum in the log domain.
   static_assert(kScoreRows % BQ == 0 && BQ % 64 == 0, "BQ must be 64 or 128");
   constexpr int NC = R / 16;
-  __shared__ float lse2_s[kScoreRows];
+  constexpr float kTinyMass = 7.888609052210118e-31f;  // 2^-100
+  __shared__ float row_s[kScoreRows];  // 1/T (fast path) or log2 T (exact path) per row
   __shared__ float part_s[4][64];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
@@ -113,13 +121,26 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
     const int bh = item / items_per_head;
     const int row0 = (item % items_per_head) * kScoreRows;
     const uint16_t* kh = klr + (size_t)bh * n * R;
-    // B operands = Q_lr^T for the wave's two 32-row halves: lane holds its query row, 8 consecutive r
-    bf16x8 qf[2][NC];
+    // B operands = (pc Q_lr)^T as hi and lo parts for the wave's two 32-row halves: lane holds
+    // its query row, 8 consecutive r per chunk
+    bf16x8 qh[2][NC], ql[2][NC];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint16_t* qrow = qlr + ((size_t)bh * n + row0 + wave * 64 + h * 32 + c32) * R;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) qf[h][c] = as_bf16x8(ld16(qrow + c * 16 + g * 8));
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 raw = ld16(qrow + c * 16 + g * 8);
+        float y[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[2 * e] = __uint_as_float(raw[e] << 16) * pc;
+          y[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u) * pc;
+        }
+        qh[h][c] = cvt8(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = y[e] - (float)qh[h][c][e];
+        ql[h][c] = cvt8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+      }
     }
     // A operands (K_lr rows, 8 consecutive r) of one KV block: 2 tiles x NC chunks
     auto load_k = [&](int kb, u32x4 (&ka)[2][NC]) {
@@ -129,6 +150,7 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
 #pragma unroll
         for (int c = 0; c < NC; ++c) ka[t][c] = ld16(kp + (size_t)(t * 32 + c32) * R + c * 16 + g * 8);
     };
+    // logits in log2 units: lane holds query c32 of half h, registers hold 16 of each tile's keys
     auto logits = [&](const u32x4 (&ka)[2][NC], f32x16 (&acc)[2][2]) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -136,109 +158,96 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
         for (int t = 0; t < 2; ++t) {
           acc[h][t] = f32x16{};
 #pragma unroll
-          for (int c = 0; c < NC; ++c) acc[h][t] = mfma32(as_bf16x8(ka[t][c]), qf[h][c], acc[h][t]);
+          for (int c = 0; c < NC; ++c) {
+            acc[h][t] = mfma32(as_bf16x8(ka[t][c]), qh[h][c], acc[h][t]);
+            acc[h][t] = mfma32(as_bf16x8(ka[t][c]), ql[h][c], acc[h][t]);
+          }
         }
     };
-    float run_m[2], run_s[2];
-    auto fold = [&](int h, float t2) {  // online log-sum-exp over blocks
-      const float nm = fmaxf(run_m[h], t2);
-      run_s[h] = run_s[h] * fast_exp2(run_m[h] - nm) + fast_exp2(t2 - nm);
-      run_m[h] = nm;
-    };
-    // block mass of half h with shift sh (log2 units): t = sh + log2 sum_j 2^(pc a_ij - sh)
-    auto block_t2 = [&](const f32x16 (&acc)[2], float sh) {
-      float s0 = 0.f, s1 = 0.f;
+    // the block's mass for this lane's query of half h: 2^l summed over its 64 keys (two lanes)
+    auto block_mass = [&](const f32x16 (&acc)[2]) {
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s0 += fast_exp2(fmaf(acc[0][v], pc, -sh));
-        s1 += fast_exp2(fmaf(acc[1][v], pc, -sh));
+      for (int v = 0; v < 16; v += 2) {
+        s0 += fast_exp2(acc[0][v]);
+        s1 += fast_exp2(acc[0][v + 1]);
+        s2 += fast_exp2(acc[1][v]);
+        s3 += fast_exp2(acc[1][v + 1]);
       }
-      return sh + fast_log2(sum_xor32(s0 + s1));
+      return sum_xor32((s0 + s1) + (s2 + s3));
     };
-    auto own_max = [&](const f32x16 (&acc)[2]) {  // the block's largest logit, log2 units
-      float m0 = acc[0][0], m1 = acc[1][0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) {
-        m0 = fmaxf(m0, acc[0][v]);
-        m1 = fmaxf(m1, acc[1][v]);
-      }
-      return max_xor32(fmaxf(m0, m1)) * pc;
+    // lanes g = 0 store half 0's rows, lanes g = 1 half 1's: one 256-byte row of the slot per wave
+    auto store = [&](int kb, float v) { slot[(size_t)kb * kScoreRows + wave * 64 + g * 32 + c32] = v; };
+
+    // Fast sweep, software-pipelined and branch-free: two blocks per trip in alternating
+    // accumulators (nkb is even), the next block's K_lr loads and MFMAs issued before the current
+    // block's exponentials.  The prefetch index is clamped, so the last trip recomputes block
+    // nkb - 1 into an accumulator nobody reads.
+    u32x4 ka[2][NC];
+    f32x16 A[2][2], B[2][2], cur[2][2];
+    float tot0 = 0.f, tot1 = 0.f;
+    auto finish = [&](int kb, const f32x16 (&acc)[2][2]) {
+      const float b0 = block_mass(acc[0]), b1 = block_mass(acc[1]);
+      store(kb, g ? b1 : b0);
+      tot0 += b0;
+      tot1 += b1;
     };
-    auto store = [&](int kb, int h, float t2) {
-      if (g == 0) slot[(size_t)kb * kScoreRows + wave * 64 + h * 32 + c32] = t2;
-    };
-    // Fast sweep.  Block 0 is shifted by its own max; every later block by the row's running
-    // log-mass bound one block back (>= each earlier logit, up to +6), so no per-block max is
-    // needed and consecutive blocks stay independent.  A logit more than 127 above that bound
-    // would overflow; this is detected once per item below and the item is redone exactly.
-    u32x4 ka[2][NC], kn[2][NC];
-    f32x16 cur[2][2], nxt[2][2];
-    float lag[2];
     load_k(0, ka);
-    if (nkb > 1) load_k(1, kn);
-    logits(ka, cur);
-    if (nkb > 1) logits(kn, nxt);
-    if (nkb > 2) load_k(2, kn);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float t0 = block_t2(cur[h], own_max(cur[h]));
-      store(0, h, t0);
-      run_m[h] = t0;
-      run_s[h] = 1.f;
-      lag[h] = t0;
+    logits(ka, A);
+    load_k(1, ka);
+    for (int kb = 0; kb < nkb; kb += 2) {
+      logits(ka, B);  // block kb + 1
+      load_k(min(kb + 2, nkb - 1), ka);
+      finish(kb, A);
+      logits(ka, A);  // block kb + 2
+      load_k(min(kb + 3, nkb - 1), ka);
+      finish(kb + 1, B);
     }
-    // steady state without branches: issue block kb+1, prefetch kb+2 (clamped), finish kb
-    for (int kb = 1; kb + 1 < nkb; ++kb) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        cur[h][0] = nxt[h][0];
-        cur[h][1] = nxt[h][1];
+    const bool exact = __syncthreads_or(!(tot0 < INFINITY) || !(tot0 >= kTinyMass) || !(tot1 < INFINITY) ||
+                                        !(tot1 >= kTinyMass));
+    if (!exact) {
+      if (g == 0) {
+        row_s[wave * 64 + c32] = 1.f / tot0;
+        row_s[wave * 64 + 32 + c32] = 1.f / tot1;
       }
-      logits(kn, nxt);
-      load_k(min(kb + 2, nkb - 1), kn);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float t2 = block_t2(cur[h], lag[h]);
-        store(kb, h, t2);
-        lag[h] = run_m[h];
-        fold(h, t2);
-      }
-    }
-    if (nkb > 1) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float t2 = block_t2(nxt[h], lag[h]);
-        store(nkb - 1, h, t2);
-        fold(h, t2);
-      }
-    }
-    // an overflowed row redoes the item with a per-block max (the exact path)
-    if (__syncthreads_or(!(run_m[0] + fast_log2(run_s[0]) < INFINITY) ||
-                         !(run_m[1] + fast_log2(run_s[1]) < INFINITY))) {
+    } else {
+      // exact path: block log-masses t = m + log2 sum_j 2^(l_ij - m) with m the block's own
+      // maximum, and an online log-sum-exp over blocks for log2 T
+      float run_m[2], run_s[2];
       for (int kb = 0; kb < nkb; ++kb) {
         load_k(kb, ka);
         logits(ka, cur);
+        float t2[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float t2 = block_t2(cur[h], own_max(cur[h]));
-          store(kb, h, t2);
+          float m = cur[h][0][0];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) m = fmaxf(m, fmaxf(cur[h][0][v], cur[h][1][v]));
+          m = max_xor32(m);
+          float sm = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sm += fast_exp2(cur[h][0][v] - m) + fast_exp2(cur[h][1][v] - m);
+          t2[h] = m + fast_log2(sum_xor32(sm));
           if (kb == 0) {
-            run_m[h] = t2;
+            run_m[h] = t2[h];
             run_s[h] = 1.f;
           } else {
-            fold(h, t2);
+            const float nm = fmaxf(run_m[h], t2[h]);
+            run_s[h] = run_s[h] * fast_exp2(run_m[h] - nm) + fast_exp2(t2[h] - nm);
+            run_m[h] = nm;
           }
         }
+        store(kb, g ? t2[1] : t2[0]);
       }
-    }
-    if (g == 0) {
-      lse2_s[wave * 64 + c32] = run_m[0] + fast_log2(run_s[0]);
-      lse2_s[wave * 64 + 32 + c32] = run_m[1] + fast_log2(run_s[1]);
+      if (g == 0) {
+        row_s[wave * 64 + c32] = run_m[0] + fast_log2(run_s[0]);
+        row_s[wave * 64 + 32 + c32] = run_m[1] + fast_log2(run_s[1]);
+      }
     }
     __threadfence_block();
     __syncthreads();
 
-    // finalize: score[qb, kb] = sum_{i in qb} 2^(t2[kb][i] - lse2[i]).
+    // finalize: score[qb, kb] = sum_{i in qb} mass[kb][i] / T_i  (log domain on the exact path).
     // chunks of 64 KV blocks: lane <-> kb, wave w sums its rows [64w, 64w+64).
     float* sc_head = scores + (size_t)bh * (n / BQ) * nkb;
     const int qb0 = row0 / BQ;
@@ -247,12 +256,21 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
       float acc0 = 0.f, acc1 = 0.f;
       if (kb < nkb) {
         const float* src = slot + (size_t)kb * kScoreRows + wave * 64;
-        const float* ls = lse2_s + wave * 64;
+        const float* rs = row_s + wave * 64;
+        if (!exact) {
 #pragma unroll
-        for (int i = 0; i < 64; i += 4) {
-          const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
-          acc0 += fast_exp2(tv[0] - ls[i]) + fast_exp2(tv[1] - ls[i + 1]);
-          acc1 += fast_exp2(tv[2] - ls[i + 2]) + fast_exp2(tv[3] - ls[i + 3]);
+          for (int i = 0; i < 64; i += 4) {
+            const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
+            acc0 = fmaf(tv[0], rs[i], fmaf(tv[1], rs[i + 1], acc0));
+            acc1 = fmaf(tv[2], rs[i + 2], fmaf(tv[3], rs[i + 3], acc1));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 64; i += 4) {
+            const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
+            acc0 += fast_exp2(tv[0] - rs[i]) + fast_exp2(tv[1] - rs[i + 1]);
+            acc1 += fast_exp2(tv[2] - rs[i + 2]) + fast_exp2(tv[3] - rs[i + 3]);
+          }
         }
       }
       part_s[wave][lane] = acc0 + acc1;

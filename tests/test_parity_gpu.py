@@ -289,17 +289,24 @@ def test_full_size_sampled(name):
             log(f"[parity] {name} h={h} kb={kb} dK/dV ok")
 
 
-def test_predictor_extreme_logits_use_the_exact_fallback():
-    # With W = [I; 0], Q_lr and K_lr are the first r columns of Q and K.  Block 0's keys are 0
-    # (its logits are 0), block 5's keys give logits ~150 (log2 units) above block 0's bound:
-    # the fast sweep's shifted exponentials overflow and the item must be redone exactly.
+@pytest.mark.parametrize("case", ["overflow", "tiny"])
+def test_predictor_extreme_logits_use_the_exact_fallback(case):
+    # With W = [I; 0], Q_lr and K_lr are the first r columns of Q and K, and every logit is
+    # pred_scale * 16 * q * k (q = 1).  The fast sweep sums 2^logit without a shift; it is redone
+    # with a per-block maximum when a row's total mass leaves [2^-100, fp32 max]:
+    #  * overflow: block 5's keys give logits ~138 (log2), 2^138 overflows;
+    #  * tiny: every key gives a logit <= ~-138 (log2), the total falls below 2^-100.
     n, d, r, bq, bk = 1024, 64, 16, 64, 64
     rng = np.random.default_rng(21)
     q = rng.standard_normal((1, 1, n, d)).astype(np.float32) * 0.1
     k = rng.standard_normal((1, 1, n, d)).astype(np.float32) * 0.1
     q[..., :r] = 1.0
-    k[0, 0, 0:64, :r] = 0.0
-    k[0, 0, 5 * 64:6 * 64, :r] = 48.0
+    if case == "overflow":
+        k[0, 0, 0:64, :r] = 0.0
+        k[0, 0, 5 * 64:6 * 64, :r] = 48.0
+    else:
+        k[0, 0, :, :r] = -48.0 - np.abs(k[0, 0, :, :r]) * 200
+        k[0, 0, 5 * 64:6 * 64, :r] = -48.0
     w = np.zeros((1, d, r), np.float32)
     w[0, :r, :r] = np.eye(r)
     from workloads.generator import bf16_bits_from_f32
