@@ -51,13 +51,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   const int nkb = n / 64;
   // out-of-range block indices are clamped: wrong results, but no access outside the tensors
   auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };
-  // gather KV block `blk` into LDS buffer `buf` (asynchronous; visible after the next barrier)
-  auto issue = [&](int blk, uint16_t* kd, uint16_t* vd) {
-    for (int i = wave; i < NI; i += WAVES) {
-      const bool isv = i >= NI / 2;
-      const int ii = isv ? i - NI / 2 : i;
-      lds_load_rows<D>((isv ? v : k) + head + (size_t)blk * 64 * D, isv ? vd : kd, ii, lane);
-    }
+  // gather the K (or V) tile of KV block `blk` into an LDS buffer (asynchronous; visible after
+  // the next barrier)
+  static_assert((NI / 2) % WAVES == 0, "each wave issues the same number of copies");
+  auto issue = [&](const uint16_t* src, int blk, uint16_t* dst) {
+#pragma unroll
+    for (int m = 0; m < NI / 2 / WAVES; ++m)
+      lds_load_rows<D>(src + head + (size_t)blk * 64 * D, dst, wave + m * WAVES, lane);
   };
 
   // Q^T as the B operand of S^T = K Q^T: lane holds its query row, 8 consecutive d per 16-wide chunk
@@ -66,8 +66,6 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) qf[dc] = as_bf16x8(ld16(q + head + (size_t)qrow * D + dc * 16 + g * 8));
 
-  issue(blk_at(0), K0, V0);
-  __syncthreads();
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -75,13 +73,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   const int arow = sigma(c32);
 
-  // one selected KV block: scores from Kc, online softmax, O^T += V^T P^T from Vc
-  auto block = [&](const uint16_t* Kc, const uint16_t* Vc) {
-    // fragment offsets from one base per run (row_base / tr_base), recomputed per block
+  // S^T = K Q^T for one KV block (two 32-key tiles, K rows in sigma order: base + t*32*D), each
+  // k-step's K operand read one step ahead; fragment offsets from one base, recomputed per block
+  auto scores = [&](const uint16_t* Kc, f32x16 (&s)[2]) {
     const int rb = opaque(row_base<D>(arow, lane));
-    // S^T = K Q^T: two 32-key tiles (rows t*32 + sigma order: base + t*32*D), each k-step's
-    // K operand read one step ahead
-    f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = f32x16{};
@@ -94,6 +89,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
         ka = kn;
       }
     }
+  };
+  // online softmax of one block's scores, part 1: the row maximum and the (rare) rescaling
+  auto rescale = [&](const f32x16 (&s)[2]) {
     // online softmax (log2 domain); lane owns one query, 32 of the block's 64 keys.
     // Row maximum by a tree over the 32 values.
     float mx8[8];
@@ -116,6 +114,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
     }
+  };
+  // part 2: exponentials, row sum and O^T += V^T P^T from Vc
+  auto exp_pv = [&](f32x16 (&s)[2], const uint16_t* Vc) {
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -166,16 +167,41 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     }
   };
 
-  // two blocks per trip so that each buffer is a distinct array (see the declarations)
-  for (int j = 0; j < topk; j += 2) {
-    if (j + 1 < topk) issue(blk_at(j + 1), K1, V1);
-    block(K0, V0);
+  // Pipelined over blocks: the scores of block j+1 are issued between the row maximum and the
+  // exponentials of block j, in one straight-line region with block j's PV product, so the matrix
+  // pipe works while the vector ALU runs the softmax.  K runs one block ahead of V: in step j
+  // (after the barrier that ends step j-1) K_{j+2} goes into the buffer of K_j, whose scores were
+  // computed in step j-1, and V_{j+1} into the buffer of V_{j-1}.  Prefetch indices are clamped
+  // (a redundant copy lands in a free buffer) and the scores computed past the last block are
+  // never used.  Two steps per trip so that each buffer is a distinct array.
+  f32x16 sa[2], sb[2];
+  const int last = topk - 1;
+  issue(k, blk_at(0), K0);
+  issue(k, blk_at(min(1, last)), K1);
+  issue(v, blk_at(0), V0);
+  __syncthreads();
+  scores(K0, sa);
+  __syncthreads();  // every wave has read K0 before step 0 refills it
+  int j = 0;
+  for (; j + 1 < topk; j += 2) {
+    // step j: sa = S_j, K1 = K_{j+1}, V0 = V_j
+    issue(k, blk_at(min(j + 2, last)), K0);
+    issue(v, blk_at(j + 1), V1);
+    rescale(sa);
+    scores(K1, sb);
+    exp_pv(sa, V0);
     __syncthreads();
-    if (j + 1 < topk) {
-      if (j + 2 < topk) issue(blk_at(j + 2), K0, V0);
-      block(K1, V1);
-      __syncthreads();
-    }
+    // step j+1: sb = S_{j+1}, K0 = K_{j+2}, V1 = V_{j+1}
+    issue(k, blk_at(min(j + 3, last)), K1);
+    issue(v, blk_at(min(j + 2, last)), V0);
+    rescale(sb);
+    scores(K0, sa);
+    exp_pv(sb, V1);
+    __syncthreads();
+  }
+  if (j < topk) {  // odd k: the last block (sa = S_last, V0 = V_last)
+    rescale(sa);
+    exp_pv(sa, V0);
   }
 
   const float l = l_run + xor32(l_run);
