@@ -41,7 +41,13 @@ Readings where the pages are silent (each is listed again in the design doc):
      is emitted ascending and duplicate-free; no block is forced in;
   R7 the sparse softmax is renormalised over the selected keys only; LSE is a
      natural log of the scaled logits;
-  R8 N must be a multiple of Bq and of Bk, and Bq a multiple of Bk.
+  R8 N must be a multiple of Bq and of Bk, and Bq a multiple of Bk;
+  R9 mass-threshold selection (the pages' own rule: keep the critical KV blocks that
+     carry ~90% of the score, [de] §2.A, [es] §2.A): per query block, the smallest
+     set of KV blocks, taken by descending score (ties to the smaller index), whose
+     scores sum to at least tau times the row's total score; capped at kmax blocks,
+     never empty.  Lists are ascending and padded with -1 to kmax; a negative entry
+     of any block list means "no block".
 """
 from __future__ import annotations
 
@@ -193,14 +199,62 @@ def topk_gap(scores: np.ndarray, k: int) -> np.ndarray:
     return gap.reshape(scores.shape[:-1])
 
 
+def select_mass_row(scores_row: np.ndarray, tau: float, kmax: int) -> np.ndarray:
+    """Mass-threshold selection of one query block (R9): the smallest descending-score prefix
+    (ties to the smaller index) whose sum reaches tau * sum(scores_row), at most kmax blocks and
+    at least one; returned ascending."""
+    n = scores_row.shape[0]
+    if not 1 <= kmax <= n:
+        raise ValueError(f"kmax={kmax} out of range [1, {n}]")
+    s = np.asarray(scores_row, np.float64)
+    order = np.lexsort((np.arange(n), -s))
+    csum = np.cumsum(s[order])
+    reached = np.nonzero(csum >= tau * s.sum())[0]
+    m = int(reached[0]) + 1 if reached.size else n
+    m = max(1, min(m, kmax))
+    return np.sort(order[:m]).astype(np.int32)
+
+
+def select_mass(scores: np.ndarray, tau: float, kmax: int) -> Tuple[np.ndarray, np.ndarray]:
+    """[..., nkb] scores -> ([..., kmax] int32 ascending lists padded with -1, [...] int32 counts)."""
+    flat = scores.reshape(-1, scores.shape[-1])
+    idx = np.full((flat.shape[0], kmax), -1, np.int32)
+    cnt = np.zeros(flat.shape[0], np.int32)
+    for i, r in enumerate(flat):
+        sel = select_mass_row(r, tau, kmax)
+        idx[i, :sel.size] = sel
+        cnt[i] = sel.size
+    return idx.reshape(scores.shape[:-1] + (kmax,)), cnt.reshape(scores.shape[:-1])
+
+
+def mass_margin(scores: np.ndarray, tau: float) -> np.ndarray:
+    """How far the uncapped cut of each row is from being decided otherwise: with c_m the sum of
+    the m largest scores and m the selected count, min(c_m - T, T - c_{m-1}) for the target
+    T = tau * row total (c_0 = -inf).  A cut with a small margin can legitimately move by one
+    block when the sums are formed in another precision or order."""
+    flat = np.asarray(scores, np.float64).reshape(-1, scores.shape[-1])
+    out = np.empty(flat.shape[0])
+    for i, r in enumerate(flat):
+        t = tau * r.sum()
+        c = np.cumsum(np.sort(r)[::-1])
+        reached = np.nonzero(c >= t)[0]
+        m = int(reached[0]) + 1 if reached.size else r.size
+        above = c[m - 1] - t if reached.size else np.inf
+        below = t - c[m - 2] if m >= 2 else np.inf
+        out[i] = min(above, below)
+    return out.reshape(scores.shape[:-1])
+
+
 # --------------------------------------------------------------------------
 # 4. sparse attention over the selected blocks ([es] §3; [de] §2.A, stage 2)
 # --------------------------------------------------------------------------
 
 
 def selected_keys(idx_row: np.ndarray, bk: int) -> np.ndarray:
-    """Token indices of the selected KV blocks, block by block in list order."""
+    """Token indices of the selected KV blocks, block by block in list order (negative
+    entries pad a ragged list and select nothing, R9)."""
     idx_row = np.asarray(idx_row, np.int64)
+    idx_row = idx_row[idx_row >= 0]
     return (idx_row[:, None] * bk + np.arange(bk)[None, :]).reshape(-1)
 
 

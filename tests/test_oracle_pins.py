@@ -362,3 +362,64 @@ def test_rejects_bad_block_sizes():
     z = np.zeros((1, 1, 100, 4))
     with pytest.raises(ValueError):
         O.sparse_attn_fwd(z, z, z, np.zeros((1, 1, 1, 1), np.int32), 64, 64, 1.0)
+
+
+# ------------------------------------------------------------------ mass-threshold selection (R9)
+
+
+def _greedy_mass_python(scores, tau, kmax):
+    """Independent statement of R9 with Python's sort and a running sum."""
+    order = sorted(range(len(scores)), key=lambda i: (-scores[i], i))
+    target, acc, chosen = tau * sum(scores), 0.0, []
+    for i in order:
+        if len(chosen) == kmax or (chosen and acc >= target):
+            break
+        chosen.append(i)
+        acc += scores[i]
+    return sorted(chosen)
+
+
+def test_mass_selection_is_the_smallest_set_reaching_the_target():
+    import itertools
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        n = int(rng.integers(1, 9))
+        s = rng.integers(0, 6, n).astype(np.float64)  # small integers: exact sums, many ties
+        if s.sum() == 0:
+            s[0] = 1.0
+        tau = float(rng.choice([0.01, 0.3, 0.5, 0.75, 0.9, 1.0]))
+        sel = O.select_mass_row(s, tau, n)
+        target = tau * s.sum()
+        assert s[sel].sum() >= target
+        best = min(m for m in range(1, n + 1)
+                   if any(s[list(c)].sum() >= target for c in itertools.combinations(range(n), m)))
+        assert sel.size == best, (s, tau, sel)
+        assert list(sel) == _greedy_mass_python(list(s), tau, n)
+        kmax = int(rng.integers(1, n + 1))
+        assert list(O.select_mass_row(s, tau, kmax)) == _greedy_mass_python(list(s), tau, kmax)
+
+
+def test_mass_selection_special_cases():
+    s = np.array([2.0, 7.0, 7.0, 0.0, 1.0, 3.0])
+    assert list(O.select_mass_row(s, 1e-6, 6)) == [1]              # one block: the top, ties to smaller index
+    assert list(O.select_mass_row(s, 1.0, 6)) == [0, 1, 2, 4, 5]   # every nonzero block, the empty one left out
+    for k in range(1, 6):                                         # capped below the 5 needed: the top-k rule
+        assert np.array_equal(O.select_mass_row(s, 1.0, k), O.select_topk_row(s, k))
+    idx, cnt = O.select_mass(np.stack([s, s[::-1]])[None], 0.5, 4)
+    assert idx.shape == (1, 2, 4) and list(cnt[0]) == [2, 2]
+    assert list(idx[0, 0]) == [1, 2, -1, -1] and list(idx[0, 1]) == [3, 4, -1, -1]
+    # the cut at 0.5 * 20 = 10: c_1 = 7 < 10 <= c_2 = 14 -> margin min(14 - 10, 10 - 7) = 3
+    assert O.mass_margin(s[None], 0.5)[0] == 3.0
+
+
+def test_padded_block_lists_select_nothing_extra():
+    rng = np.random.default_rng(3)
+    n, d, bq, bk = 256, 16, 64, 64
+    q, k, v, do = (rng.standard_normal((1, 1, n, d)) for _ in range(4))
+    full = np.array([[[[2, 0], [1, 3], [3, 2], [0, 1]]]], np.int32)
+    padded = np.concatenate([full, np.full((1, 1, 4, 2), -1, np.int32)], axis=-1)
+    o1, l1 = O.sparse_attn_fwd(q, k, v, full, bq, bk, 0.25)
+    o2, l2 = O.sparse_attn_fwd(q, k, v, padded, bq, bk, 0.25)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    for a, b in zip(O.sparse_attn_bwd(q, k, v, do, full, bq, bk, 0.25), O.sparse_attn_bwd(q, k, v, do, padded, bq, bk, 0.25)):
+        assert np.array_equal(a, b)
