@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense (k = N/Bk) comparator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
+    ap.add_argument("--no-mass", action="store_true", help="skip the mass-threshold selection leg")
+    ap.add_argument("--mass-tau", type=float, default=0.1,
+                    help="tau of the mass-threshold leg (kmax = 2k); with the random-init predictor's near-uniform "
+                         "scores, 0.1 selects about the headline density")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a reference for HBM byte counters)")
     return ap.parse_args()
@@ -67,6 +71,7 @@ def kernel_units(cfg):
         # predictor sweep: one exponential per predicted logit, B*H*N^2 of them
         "scores_kernel": ("alu", float(cfg.batch * cfg.heads) * cfg.seq_len * cfg.seq_len),
         "select_topk_kernel": ("hbm", 4.0 * cfg.batch * cfg.heads * cfg.nqb * (cfg.nkb + cfg.topk)),
+        "select_mass_kernel": ("hbm", 4.0 * cfg.batch * cfg.heads * cfg.nqb * (cfg.nkb + min(2 * cfg.topk, cfg.nkb) + 1)),
         # projection of one tensor: read [B,H,N,d] bf16, write [B,H,N,r] bf16
         "proj_kernel(q)": ("hbm", 2.0 * elems + 2.0 * cfg.batch * cfg.heads * cfg.seq_len * cfg.rank),
         "bwd_pre_kernel": ("hbm", 2.0 * 2 * elems + 12.0 * cfg.batch * cfg.heads * cfg.seq_len),
@@ -260,6 +265,39 @@ def main():
                  "speedup_attn": (dfwd + dbwd) / attn_ms, "ideal_speedup": cfg.nkb / cfg.topk}
         log(f"[bench] dense fwd {dfwd:.1f} ms bwd {dbwd:.1f} ms")
 
+    mass = None
+    if not a.no_mass:
+        # mass-threshold selection and attention over the resulting ragged lists, same inputs
+        kmax = min(2 * cfg.topk, cfg.nkb)
+        log(f"[bench] mass-threshold leg (tau={a.mass_tau}, kmax={kmax})")
+        idx_m = torch.empty((B, H, cfg.nqb, kmax), dtype=torch.int32, device=dev)
+        cnt_m = torch.empty((B, H, cfg.nqb), dtype=torch.int32, device=dev)
+        _, _, wsb_m = dsv.workspace_sizes(t["q"], topk=kmax, rank=cfg.rank, **kw)
+        wsb3 = torch.empty(wsb_m, dtype=torch.uint8, device=dev)
+        dsv.predict(t["q"], t["k"], t["wq"], t["wk"], workspace=wsp, out=scores, **kw)
+        evm = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for rep in range(2):  # the first pass warms up
+            evm[0].record(stream)
+            dsv.select_mass(scores, a.mass_tau, kmax, out=(idx_m, cnt_m), **kw)
+            evm[1].record(stream)
+            dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_m, block_counts=cnt_m, workspace=wsf, residual=True,
+                                out=(o, lse, o_lo), **kw)
+            evm[2].record(stream)
+            dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, idx_m, block_counts=cnt_m, o_lo=o_lo,
+                                workspace=wsb3, out=(dq, dk, dv), **kw)
+            evm[3].record(stream)
+            evm[3].synchronize()
+        ms = [evm[j].elapsed_time(evm[j + 1]) for j in range(3)]
+        pairs_m = int(cnt_m.sum().item())
+        flops_m = 14.0 * pairs_m * cfg.q_block * cfg.kv_block * cfg.head_dim
+        mass = {"tau": a.mass_tau, "kmax": kmax, "mean_count": pairs_m / (B * H * cfg.nqb),
+                "min_count": int(cnt_m.min().item()), "max_count": int(cnt_m.max().item()),
+                "select_ms": ms[0], "fwd_ms": ms[1], "bwd_ms": ms[2],
+                "attn_tflops": flops_m / ((ms[1] + ms[2]) * 1e-3) / 1e12}
+        log(f"[bench] mass leg: mean count {mass['mean_count']:.1f}, select {ms[0]:.2f} ms, fwd {ms[1]:.1f} ms, "
+            f"bwd {ms[2]:.1f} ms")
+        del wsb3
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] CPU oracle baseline (bounded sample)")
@@ -280,7 +318,7 @@ def main():
         "attn_fwd_bwd": {"ms": attn_ms, "tflops": attn_tflops, "frac_of_peak": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
                          "tokens_per_s": B * N / (attn_ms * 1e-3)},
         "phases_ms": {"predict": phases[0], "select": phases[1], "fwd": phases[2], "bwd": phases[3]},
-        "kernels": kern, "kernel_rates": rates, "dense": dense,
+        "kernels": kern, "kernel_rates": rates, "dense": dense, "mass_selection": mass,
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

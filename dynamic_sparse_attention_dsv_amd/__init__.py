@@ -9,6 +9,7 @@ tensors are not on a GPU, the calls raise.
 Entry points (same names as the C ABI):
   predict(q, k, wq, wk, ...)          -> block_scores [B, H, N/Bq, N/Bk] float32
   select_topk(block_scores, topk)     -> block_idx    [B, H, N/Bq, k]    int32
+  select_mass(block_scores, tau, kmax) -> (block_idx [B, H, N/Bq, kmax] padded with -1, block_counts)
   sparse_attn_fwd(q, k, v, idx, ...)  -> (o, lse), or (o, lse, o_lo) with residual=True
   sparse_attn_bwd(q, k, v, o, do, lse, idx, ..., o_lo=None) -> (dq, dk, dv)
 """
@@ -27,7 +28,8 @@ DSV_F32, DSV_BF16 = 0, 1
 STATUS = {0: "DSV_OK", 1: "DSV_ERR_INVALID_ARGUMENT", 2: "DSV_ERR_UNSUPPORTED", 3: "DSV_ERR_WORKSPACE_TOO_SMALL",
           4: "DSV_ERR_HIP"}
 
-EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_select_topk", "dsv_sparse_attn_fwd_workspace_size",
+EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_select_topk", "dsv_select_mass",
+            "dsv_sparse_attn_fwd_workspace_size",
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd_workspace_size", "dsv_sparse_attn_bwd", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_timing_begin", "dsv_timing_end")
 
@@ -68,10 +70,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsv_predict_workspace_size": (S, [P]),
         "dsv_predict": (ctypes.c_int, [P, V, V, V, V, V, S, V, V]),
         "dsv_select_topk": (ctypes.c_int, [P, V, V, V]),
+        "dsv_select_mass": (ctypes.c_int, [P, V, ctypes.c_float, V, V, V]),
         "dsv_sparse_attn_fwd_workspace_size": (S, [P]),
-        "dsv_sparse_attn_fwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, S, V]),
+        "dsv_sparse_attn_fwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, V, S, V]),
         "dsv_sparse_attn_bwd_workspace_size": (S, [P]),
-        "dsv_sparse_attn_bwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, V, V, V, V, S, V]),
+        "dsv_sparse_attn_bwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, V, V, V, V, V, S, V]),
         "dsv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dsv_last_error": (ctypes.c_char_p, []),
         "dsv_version": (ctypes.c_int32, []),
@@ -110,6 +113,14 @@ def _dev(*ts: torch.Tensor) -> torch.device:
 
 def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_counts(cnt: Optional[torch.Tensor], idx: torch.Tensor) -> None:
+    if cnt is None:
+        return
+    _contig(cnt)
+    if cnt.dtype != torch.int32 or tuple(cnt.shape) != tuple(idx.shape[:-1]) or cnt.device != idx.device:
+        raise ValueError("block_counts must be int32 [B, H, N/Bq] on the block_idx device")
 
 
 def _stream(dev: torch.device):
@@ -193,13 +204,39 @@ def select_topk(scores: torch.Tensor, topk: int, *, q_block: int, kv_block: int 
     return idx
 
 
+def select_mass(scores: torch.Tensor, tau: float, kmax: int, *, q_block: int, kv_block: int = 64,
+                out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The fewest KV blocks (by descending score) carrying a fraction tau of each query block's
+    score, at most kmax -> (block_idx ascending then -1 padding, block_counts)."""
+    lib = load_library()
+    dev = _dev(scores)
+    _contig(scores)
+    if scores.dtype != torch.float32 or scores.dim() != 4:
+        raise TypeError("scores must be float32 [B, H, N/Bq, N/Bk]")
+    b, h, nqb, nkb = scores.shape
+    n = nkb * kv_block
+    if nqb * q_block != n:
+        raise ValueError("scores shape does not match the block sizes")
+    prob = Problem(b, h, n, 64, q_block, kv_block, kmax, 1, DSV_F32, 0.0, 0.0)
+    if out is not None:
+        idx, cnt = out
+    else:
+        idx = torch.empty((b, h, nqb, kmax), dtype=torch.int32, device=dev)
+        cnt = torch.empty((b, h, nqb), dtype=torch.int32, device=dev)
+    _check(lib.dsv_select_mass(ctypes.byref(prob), _p(scores), ctypes.c_float(tau), _p(idx), _p(cnt), _stream(dev)),
+           "dsv_select_mass")
+    return idx, cnt
+
+
 def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_scale: Optional[float] = None,
-                    residual: bool = False, workspace: Optional[torch.Tensor] = None, out=None):
+                    block_counts: Optional[torch.Tensor] = None, residual: bool = False,
+                    workspace: Optional[torch.Tensor] = None, out=None):
     """Softmax attention over the selected KV blocks only -> (o [B,H,N,d], lse [B,H,N] float32).
 
     With ``residual=True`` (bf16 only) also returns o_lo, the bf16 rounding residual of O; handing it
     to :func:`sparse_attn_bwd` makes the backward's D = rowsum(dO * O) accurate to fp32.
-    ``out`` may supply (o, lse) or (o, lse, o_lo).
+    ``out`` may supply (o, lse) or (o, lse, o_lo).  ``block_counts`` ([B, H, N/Bq] int32, e.g. from
+    :func:`select_mass`) limits each query block to the first entries of its list.
     """
     lib = load_library()
     dev = _dev(q, k, v, block_idx)
@@ -226,14 +263,15 @@ def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_
     if residual and o_lo is None:
         o_lo = torch.empty_like(q)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.dsv_sparse_attn_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(block_idx), _p(o), _p(lse),
-                                   _p(o_lo), _p(ws), nbytes, _stream(dev)), "dsv_sparse_attn_fwd")
+    _check_counts(block_counts, block_idx)
+    _check(lib.dsv_sparse_attn_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(block_idx), _p(block_counts), _p(o),
+                                   _p(lse), _p(o_lo), _p(ws), nbytes, _stream(dev)), "dsv_sparse_attn_fwd")
     return (o, lse, o_lo) if residual else (o, lse)
 
 
 def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block: int = 64,
                     sm_scale: Optional[float] = None, o_lo: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None,
+                    block_counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                     out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """Gradients (dq, dk, dv) of the sparse attention; ``o_lo`` is the forward's residual (or None)."""
     lib = load_library()
@@ -247,9 +285,10 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block:
     prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1], sm_scale=sm_scale)
     ws = _workspace(int(lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(prob))), dev, workspace)
     dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    _check_counts(block_counts, block_idx)
     _check(lib.dsv_sparse_attn_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(o), _p(o_lo), _p(dout), _p(lse),
-                                   _p(block_idx), _p(dq), _p(dk), _p(dv), _p(ws), ws.numel() * ws.element_size(),
-                                   _stream(dev)), "dsv_sparse_attn_bwd")
+                                   _p(block_idx), _p(block_counts), _p(dq), _p(dk), _p(dv), _p(ws),
+                                   ws.numel() * ws.element_size(), _stream(dev)), "dsv_sparse_attn_bwd")
     return dq, dk, dv
 
 

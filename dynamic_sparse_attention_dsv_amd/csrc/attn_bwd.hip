@@ -74,11 +74,12 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) 
     p[i] = v;
 }
 
-__global__ void csc_mark_kernel(const int32_t* __restrict__ idx, uint32_t* __restrict__ bitmap, int nqb, int nkb,
-                                int topk, int words, size_t total) {
+__global__ void csc_mark_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts,
+                                uint32_t* __restrict__ bitmap, int nqb, int nkb, int topk, int words, size_t total) {
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= total) return;
   const size_t row = t / topk;  // bh * nqb + qb
+  if ((int)(t % topk) >= list_len(cnts, row, topk)) return;  // past the row's count
   const int qb = (int)(row % nqb);
   const size_t bh = row / nqb;
   const int kb = idx[t];
@@ -381,7 +382,8 @@ template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dvec,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ dq, int n, int topk, int nwg, float c, float sm_scale) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ dq, int n, int topk,
+    int nwg, float c, float sm_scale) {
   constexpr int WAVES = BQ / 32;
   constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
   // one array per buffer, so the compiler can see that the asynchronous copy into
@@ -396,6 +398,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
   const int g = lane >> 5, c32 = lane & 31;
   const size_t head = (size_t)bh * n * D;
   const int32_t* blocks = idx + ((size_t)bh * nqb + qb) * topk;
+  const int kq = list_len(cnts, (size_t)bh * nqb + qb, topk);  // blocks in this query block's list
   const int qrow = qb * BQ + wave * 32 + c32;
   const int nkb = n / 64;
   auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };  // clamp out-of-range indices
@@ -473,13 +476,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
       }
     }
   };
-  // two blocks per trip so that each buffer is a distinct array
-  for (int j = 0; j < topk; j += 2) {
-    if (j + 1 < topk) issue(blk_at(j + 1), K1, V1);
+  // two blocks per trip so that each buffer is a distinct array (an empty list leaves dQ = 0)
+  for (int j = 0; j < kq; j += 2) {
+    if (j + 1 < kq) issue(blk_at(j + 1), K1, V1);
     block(K0, V0);
     __syncthreads();
-    if (j + 1 < topk) {
-      if (j + 2 < topk) issue(blk_at(j + 2), K0, V0);
+    if (j + 1 < kq) {
+      if (j + 2 < kq) issue(blk_at(j + 2), K0, V0);
       block(K1, V1);
       __syncthreads();
     }
@@ -501,8 +504,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
 __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                        const float* __restrict__ v, const float* __restrict__ dout,
                                        const float* __restrict__ lse, const float* __restrict__ dvec,
-                                       const int32_t* __restrict__ idx, float* __restrict__ dq, int n, int d, int bq,
-                                       int bk, int topk, float scale) {
+                                       const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts,
+                                       float* __restrict__ dq, int n, int d, int bq, int bk, int topk, float scale) {
   // one thread per query row and output column c: grid (ceil(n*d/256), BH)
   const int bh = blockIdx.y;
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -512,9 +515,11 @@ __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ q, const float*
   const float* qi = q + head + (size_t)i * d;
   const float* gi = dout + head + (size_t)i * d;
   const float li = lse[(size_t)bh * n + i], di = dvec[(size_t)bh * n + i];
-  const int32_t* blocks = idx + ((size_t)bh * (n / bq) + i / bq) * topk;
+  const size_t qrow = (size_t)bh * (n / bq) + i / bq;
+  const int32_t* blocks = idx + qrow * topk;
+  const int kq = list_len(cnts, qrow, topk);
   float acc = 0.f;
-  for (int jb = 0; jb < topk; ++jb) {
+  for (int jb = 0; jb < kq; ++jb) {
     const int kb = min(max(blocks[jb], 0), n / bk - 1);  // clamp out-of-range indices
     for (int j = kb * bk; j < (kb + 1) * bk; ++j) {
       const float* kj = k + head + (size_t)j * d;
@@ -587,8 +592,8 @@ hipError_t launch_bwd_pre_f32(const float* o, const float* dout, float* dvec, in
   return hipGetLastError();
 }
 
-hipError_t launch_csc(const int32_t* idx, uint32_t* bitmap, int32_t* counts, int32_t* col_ptr, int32_t* rows,
-                      int32_t* order, int bh, int nqb, int nkb, int topk, hipStream_t st) {
+hipError_t launch_csc(const int32_t* idx, const int32_t* cnts, uint32_t* bitmap, int32_t* counts, int32_t* col_ptr,
+                      int32_t* rows, int32_t* order, int bh, int nqb, int nkb, int topk, hipStream_t st) {
   const int words = (nqb + 31) / 32;
   const size_t nbits = (size_t)bh * nkb * words;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<size_t>((nbits + 255) / 256, 65535)), dim3(256), 0,
@@ -596,8 +601,8 @@ hipError_t launch_csc(const int32_t* idx, uint32_t* bitmap, int32_t* counts, int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t total = (size_t)bh * nqb * topk;
-  hipLaunchKernelGGL(csc_mark_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, idx, bitmap, nqb,
-                     nkb, topk, words, total);
+  hipLaunchKernelGGL(csc_mark_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, idx, cnts, bitmap,
+                     nqb, nkb, topk, words, total);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int cols = bh * nkb;
   hipLaunchKernelGGL(csc_count_kernel, dim3((cols + 3) / 4), dim3(256), 0, st, bitmap, counts, cols, words);
@@ -632,14 +637,14 @@ hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint
 }
 
 hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                              const float* lse2, const float* dvec, const int32_t* idx, uint16_t* dq, int bh, int n,
-                              int d, int bq, int topk, float sm_scale, hipStream_t st) {
+                              const float* lse2, const float* dvec, const int32_t* idx, const int32_t* cnts,
+                              uint16_t* dq, int bh, int n, int d, int bq, int topk, float sm_scale, hipStream_t st) {
   const int nwg = bh * (n / bq);
   const float c = sm_scale * kLog2e;
 #define DQ(D_, BQ_)                                                                                          \
   if (d == D_ && bq == BQ_) {                                                                                \
     hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, dout, lse2, \
-                       dvec, idx, dq, n, topk, nwg, c, sm_scale);                                            \
+                       dvec, idx, cnts, dq, n, topk, nwg, c, sm_scale);                                      \
     return hipGetLastError();                                                                                \
   }
   DQ(64, 64) DQ(64, 128) DQ(128, 64) DQ(128, 128)
@@ -648,12 +653,12 @@ hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16
 }
 
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dout, const float* lse,
-                          const float* dvec, const int32_t* idx, const int32_t* col_ptr, const int32_t* rows,
-                          float* dq, float* dk, float* dv, int bh, int n, int d, int bq, int bk, int topk,
-                          float sm_scale, hipStream_t st) {
+                          const float* dvec, const int32_t* idx, const int32_t* cnts, const int32_t* col_ptr,
+                          const int32_t* rows, float* dq, float* dk, float* dv, int bh, int n, int d, int bq, int bk,
+                          int topk, float sm_scale, hipStream_t st) {
   dim3 grid((unsigned)(((size_t)n * d + 255) / 256), bh);
-  hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, grid, dim3(256), 0, st, q, k, v, dout, lse, dvec, idx, dq, n, d, bq, bk,
-                     topk, sm_scale);
+  hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, grid, dim3(256), 0, st, q, k, v, dout, lse, dvec, idx, cnts, dq, n, d,
+                     bq, bk, topk, sm_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, grid, dim3(256), 0, st, q, k, v, dout, lse, dvec, col_ptr, rows, dk,

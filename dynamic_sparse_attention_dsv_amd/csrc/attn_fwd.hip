@@ -30,8 +30,8 @@ namespace dsv {
 template <int D, int BQ, bool SPLIT>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse,
-    uint16_t* __restrict__ o_lo /* optional rounding residual of O */, int n, int topk, int nwg,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ o,
+    float* __restrict__ lse, uint16_t* __restrict__ o_lo /* optional rounding residual of O */, int n, int topk, int nwg,
     float c /* sm_scale * log2(e) */) {
   constexpr int WAVES = BQ / 32;
   constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
@@ -48,6 +48,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   const int g = lane >> 5, c32 = lane & 31;
   const size_t head = (size_t)bh * n * D;
   const int32_t* blocks = idx + ((size_t)bh * nqb + qb) * topk;
+  const int kq = list_len(cnts, (size_t)bh * nqb + qb, topk);  // blocks in this query block's list
   const int nkb = n / 64;
   // out-of-range block indices are clamped: wrong results, but no access outside the tensors
   auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };
@@ -62,6 +63,18 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
 
   // Q^T as the B operand of S^T = K Q^T: lane holds its query row, 8 consecutive d per 16-wide chunk
   const int qrow = qb * BQ + wave * 32 + c32;
+  if (kq == 0) {  // an empty block list: O = 0, lse = -inf (uniform over the workgroup)
+    uint16_t* orow = o + head + (size_t)qrow * D;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) st16(orow + dc * 16 + g * 8, u32x4{0, 0, 0, 0});
+    if constexpr (SPLIT) {
+      uint16_t* lrow = o_lo + head + (size_t)qrow * D;
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) st16(lrow + dc * 16 + g * 8, u32x4{0, 0, 0, 0});
+    }
+    if (g == 0) lse[(size_t)bh * n + qrow] = -INFINITY;
+    return;
+  }
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) qf[dc] = as_bf16x8(ld16(q + head + (size_t)qrow * D + dc * 16 + g * 8));
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   // (a redundant copy lands in a free buffer) and the scores computed past the last block are
   // never used.  Two steps per trip so that each buffer is a distinct array.
   f32x16 sa[2], sb[2];
-  const int last = topk - 1;
+  const int last = kq - 1;
   issue(k, blk_at(0), K0);
   issue(k, blk_at(min(1, last)), K1);
   issue(v, blk_at(0), V0);
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   scores(K0, sa);
   __syncthreads();  // every wave has read K0 before step 0 refills it
   int j = 0;
-  for (; j + 1 < topk; j += 2) {
+  for (; j + 1 < kq; j += 2) {
     // step j: sa = S_j, K1 = K_{j+1}, V0 = V_j
     issue(k, blk_at(min(j + 2, last)), K0);
     issue(v, blk_at(j + 1), V1);
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     exp_pv(sb, V1);
     __syncthreads();
   }
-  if (j < topk) {  // odd k: the last block (sa = S_last, V0 = V_last)
+  if (j < kq) {  // odd length: the last block (sa = S_last, V0 = V_last)
     rescale(sa);
     exp_pv(sa, V0);
   }
@@ -232,7 +245,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
 template <int D>
 __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                           const float* __restrict__ v,
-                                                          const int32_t* __restrict__ idx, float* __restrict__ o,
+                                                          const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ cnts, float* __restrict__ o,
                                                           float* __restrict__ lse, int n, int d, int bq, int bk,
                                                           int topk, float scale) {
   // one thread per query row; grid (ceil(n/64), BH)
@@ -243,9 +257,11 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restric
   const float* qi = q + head + (size_t)i * d;
   float qv[D], acc[D];
   for (int c = 0; c < d; ++c) { qv[c] = qi[c]; acc[c] = 0.f; }
-  const int32_t* blocks = idx + ((size_t)bh * (n / bq) + i / bq) * topk;
+  const size_t qrow = (size_t)bh * (n / bq) + i / bq;
+  const int32_t* blocks = idx + qrow * topk;
+  const int kq = list_len(cnts, qrow, topk);
   float m = -INFINITY, l = 0.f;
-  for (int jb = 0; jb < topk; ++jb) {
+  for (int jb = 0; jb < kq; ++jb) {
     const int kb = min(max(blocks[jb], 0), n / bk - 1);  // clamp out-of-range indices
     for (int j = kb * bk; j < (kb + 1) * bk; ++j) {
       const float* kj = k + head + (size_t)j * d;
@@ -261,14 +277,15 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restric
     }
   }
   float* oi = o + head + (size_t)i * d;
-  for (int c = 0; c < d; ++c) oi[c] = acc[c] / l;
-  lse[(size_t)bh * n + i] = m + logf(l);
+  const float inv = l > 0.f ? 1.f / l : 0.f;  // an empty block list gives O = 0, lse = -inf
+  for (int c = 0; c < d; ++c) oi[c] = acc[c] * inv;
+  lse[(size_t)bh * n + i] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                                uint16_t* o, float* lse, uint16_t* o_lo, int bh, int n, int d, int bq, int topk,
+                                const int32_t* cnts, uint16_t* o, float* lse, uint16_t* o_lo, int bh, int n, int d, int bq, int topk,
                                 float sm_scale, hipStream_t st) {
   const int nwg = bh * (n / bq);
   const float c = sm_scale * kLog2e;
@@ -276,10 +293,10 @@ hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint
   if (d == D_ && bq == BQ_) {                                                                             \
     if (o_lo)                                                                                             \
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, true>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, idx, \
-                         o, lse, o_lo, n, topk, nwg, c);                                                  \
+                         cnts, o, lse, o_lo, n, topk, nwg, c);                                            \
     else                                                                                                  \
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, false>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, \
-                         idx, o, lse, o_lo, n, topk, nwg, c);                                             \
+                         idx, cnts, o, lse, o_lo, n, topk, nwg, c);                                       \
     return hipGetLastError();                                                                             \
   }
   FWD(64, 64) FWD(64, 128) FWD(128, 64) FWD(128, 128)
@@ -287,14 +304,14 @@ hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* idx, float* o,
-                               float* lse, int bh, int n, int d, int bq, int bk, int topk, float sm_scale,
-                               hipStream_t st) {
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* idx,
+                               const int32_t* cnts, float* o, float* lse, int bh, int n, int d, int bq, int bk, int topk,
+                               float sm_scale, hipStream_t st) {
   dim3 grid((n + 63) / 64, bh);
 #define FF(D_)                                                                                            \
   if (d <= D_) {                                                                                          \
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D_>), grid, dim3(64), 0, st, q, k, v, idx, o, lse, n, d, bq, bk, \
-                       topk, sm_scale);                                                                   \
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D_>), grid, dim3(64), 0, st, q, k, v, idx, cnts, o, lse, n, d, bq, \
+                       bk, topk, sm_scale);                                                               \
     return hipGetLastError();                                                                             \
   }
   FF(32) FF(64) FF(128)

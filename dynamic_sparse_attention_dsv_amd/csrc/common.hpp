@@ -208,6 +208,12 @@ __device__ __forceinline__ void lds_load_rows(const uint16_t* src, uint16_t* dst
   __builtin_amdgcn_global_load_lds(src + (size_t)row * D + c * 8, dst + i * 512, 16, 0, 0);
 }
 
+// Length of query-block row `row`'s block list: its count when per-row counts are given
+// (clamped to [0, k]), else k.
+__device__ __forceinline__ int list_len(const int32_t* cnts, size_t row, int k) {
+  return cnts ? min(max(cnts[row], 0), k) : k;
+}
+
 // Map a workgroup id so that consecutive logical ids run on the same XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); with this
 // remap XCD x processes the contiguous logical range [x*per, (x+1)*per), so the

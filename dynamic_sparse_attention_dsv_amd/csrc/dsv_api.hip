@@ -303,6 +303,21 @@ dsv_status dsv_select_topk(const dsv_problem* p, const float* block_scores, int3
   return DSV_OK;
 }
 
+dsv_status dsv_select_mass(const dsv_problem* p, const float* block_scores, float tau, int32_t* block_idx,
+                           int32_t* block_counts, void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, false));
+  TRY(check_ptr(block_scores, "block_scores", 4));
+  TRY(check_ptr(block_idx, "block_idx", 4));
+  TRY(check_ptr(block_counts, "block_counts", 4));
+  if (!(tau > 0.f && tau <= 1.f)) return fail(DSV_ERR_INVALID_ARGUMENT, "tau must lie in (0, 1]");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY_HIP(dsv::launch_select_mass(block_scores, block_idx, block_counts, o.bh() * o.nqb(), o.nkb(), o.k, tau, st),
+          "select_mass_kernel");
+  return DSV_OK;
+}
+
 size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p) {
   Prob o;
   if (to_prob(p, o, false) != DSV_OK) return 0;
@@ -310,8 +325,8 @@ size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p) {
 }
 
 dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
-                               const int32_t* block_idx, void* o_ptr, float* lse, void* o_lo, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               const int32_t* block_idx, const int32_t* block_counts, void* o_ptr, float* lse,
+                               void* o_lo, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   Prob o;
   TRY(to_prob(p, o, false));
@@ -321,6 +336,7 @@ dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* 
   TRY(check_ptr(k, "k"));
   TRY(check_ptr(v, "v"));
   TRY(check_ptr(block_idx, "block_idx", 4));
+  if (block_counts) TRY(check_ptr(block_counts, "block_counts", 4));
   TRY(check_ptr(o_ptr, "o"));
   TRY(check_ptr(lse, "lse"));
   TRY(check_residual(o, o_lo));
@@ -333,13 +349,14 @@ dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (o.dtype == DSV_BF16) {
     TRY_HIP(dsv::launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                      static_cast<const uint16_t*>(v), block_idx,
+                                      static_cast<const uint16_t*>(v), block_idx, block_counts,
                                       static_cast<uint16_t*>(o_ptr), lse, static_cast<uint16_t*>(o_lo), o.bh(), o.n,
                                       o.d, o.bq, o.k, o.sm, st),
             "attn_fwd_kernel");
   } else {
     TRY_HIP(dsv::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                                     static_cast<const float*>(v), block_idx, static_cast<float*>(o_ptr), lse, o.bh(),
+                                     static_cast<const float*>(v), block_idx, block_counts,
+                                     static_cast<float*>(o_ptr), lse, o.bh(),
                                      o.n, o.d, o.bq, o.bk, o.k, o.sm, st), "attn_fwd_kernel");
   }
   return DSV_OK;
@@ -352,7 +369,8 @@ size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p) {
 }
 
 dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v, const void* o_ptr,
-                               const void* o_lo, const void* dout, const float* lse, const int32_t* block_idx, void* dq, void* dk,
+                               const void* o_lo, const void* dout, const float* lse, const int32_t* block_idx,
+                               const int32_t* block_counts, void* dq, void* dk,
                                void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   Prob o;
@@ -363,6 +381,7 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
   const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
   for (int i = 0; i < 9; ++i) TRY(check_ptr(ptrs[i], names[i]));
   TRY(check_ptr(block_idx, "block_idx", 4));
+  if (block_counts) TRY(check_ptr(block_counts, "block_counts", 4));
   TRY(check_residual(o, o_lo));
   TRY(check_ptr(workspace, "workspace", kWsAlign));
   const BwdWs w = bwd_ws(o);
@@ -372,8 +391,8 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
   int32_t* col_ptr = at<int32_t>(workspace, w.col_ptr);
   int32_t* rows = at<int32_t>(workspace, w.rows);
   int32_t* order = o.dtype == DSV_BF16 ? at<int32_t>(workspace, w.order) : nullptr;
-  TRY_HIP(dsv::launch_csc(block_idx, at<uint32_t>(workspace, w.bitmap), at<int32_t>(workspace, w.counts), col_ptr,
-                          rows, order, o.bh(), o.nqb(), o.nkb(), o.k, st), "csc_kernels");
+  TRY_HIP(dsv::launch_csc(block_idx, block_counts, at<uint32_t>(workspace, w.bitmap), at<int32_t>(workspace, w.counts),
+                          col_ptr, rows, order, o.bh(), o.nqb(), o.nkb(), o.k, st), "csc_kernels");
   float* dvec = at<float>(workspace, w.dvec);
   if (o.dtype == DSV_BF16) {
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
@@ -386,13 +405,14 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
     TRY_HIP(dsv::launch_bwd_dkdv_bf16(q16, k16, v16, do16, lse2, dvec, col_ptr, rows, order,
                                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), o.bh(), o.n, o.d, o.bq,
                                       o.k, o.sm, st), "attn_bwd_dkdv_kernel");
-    TRY_HIP(dsv::launch_bwd_dq_bf16(q16, k16, v16, do16, lse2, dvec, block_idx, static_cast<uint16_t*>(dq), o.bh(),
-                                    o.n, o.d, o.bq, o.k, o.sm, st), "attn_bwd_dq_kernel");
+    TRY_HIP(dsv::launch_bwd_dq_bf16(q16, k16, v16, do16, lse2, dvec, block_idx, block_counts,
+                                    static_cast<uint16_t*>(dq), o.bh(), o.n, o.d, o.bq, o.k, o.sm, st),
+            "attn_bwd_dq_kernel");
   } else {
     TRY_HIP(dsv::launch_bwd_pre_f32(static_cast<const float*>(o_ptr), static_cast<const float*>(dout), dvec,
                                     o.bh() * o.n, o.d, st), "bwd_pre_kernel");
     TRY_HIP(dsv::launch_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-                                static_cast<const float*>(dout), lse, dvec, block_idx, col_ptr, rows,
+                                static_cast<const float*>(dout), lse, dvec, block_idx, block_counts, col_ptr, rows,
                                 static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), o.bh(), o.n,
                                 o.d, o.bq, o.bk, o.k, o.sm, st), "attn_bwd_f32_kernels");
   }

@@ -23,31 +23,33 @@ hipError_t launch_scores_f32(const float* qlr, const float* klr, float* lse, flo
 
 // selection
 hipError_t launch_select_topk(const float* scores, int32_t* idx, int rows, int nkb, int k, hipStream_t st);
+hipError_t launch_select_mass(const float* scores, int32_t* idx, int32_t* cnts, int rows, int nkb, int kmax,
+                              float tau, hipStream_t st);
 
-// forward
+// forward (cnts: optional per-query-block list lengths, NULL = topk)
 hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                                uint16_t* o, float* lse, uint16_t* o_lo, int bh, int n, int d, int bq, int topk, float sm_scale,
-                                hipStream_t st);
-hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* idx, float* o,
-                               float* lse, int bh, int n, int d, int bq, int bk, int topk, float sm_scale,
-                               hipStream_t st);
+                                const int32_t* cnts, uint16_t* o, float* lse, uint16_t* o_lo, int bh, int n, int d,
+                                int bq, int topk, float sm_scale, hipStream_t st);
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* idx,
+                               const int32_t* cnts, float* o, float* lse, int bh, int n, int d, int bq, int bk,
+                               int topk, float sm_scale, hipStream_t st);
 
 // backward and helpers
-hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* o_lo, const uint16_t* dout, const float* lse, float* dvec, float* lse2,
-                               int rows, int d, hipStream_t st);
+hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* o_lo, const uint16_t* dout, const float* lse,
+                               float* dvec, float* lse2, int rows, int d, hipStream_t st);
 hipError_t launch_bwd_pre_f32(const float* o, const float* dout, float* dvec, int rows, int d, hipStream_t st);
-hipError_t launch_csc(const int32_t* idx, uint32_t* bitmap, int32_t* counts, int32_t* col_ptr, int32_t* rows,
-                      int32_t* order, int bh, int nqb, int nkb, int topk, hipStream_t st);
+hipError_t launch_csc(const int32_t* idx, const int32_t* cnts, uint32_t* bitmap, int32_t* counts, int32_t* col_ptr,
+                      int32_t* rows, int32_t* order, int bh, int nqb, int nkb, int topk, hipStream_t st);
 hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                                 const float* lse2, const float* dvec, const int32_t* col_ptr, const int32_t* rows,
                                 const int32_t* order, uint16_t* dk, uint16_t* dv, int bh, int n, int d, int bq,
                                 int topk, float sm_scale, hipStream_t st);
 hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                              const float* lse2, const float* dvec, const int32_t* idx, uint16_t* dq, int bh, int n,
-                              int d, int bq, int topk, float sm_scale, hipStream_t st);
+                              const float* lse2, const float* dvec, const int32_t* idx, const int32_t* cnts,
+                              uint16_t* dq, int bh, int n, int d, int bq, int topk, float sm_scale, hipStream_t st);
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dout, const float* lse,
-                          const float* dvec, const int32_t* idx, const int32_t* col_ptr, const int32_t* rows,
-                          float* dq, float* dk, float* dv, int bh, int n, int d, int bq, int bk, int topk,
-                          float sm_scale, hipStream_t st);
+                          const float* dvec, const int32_t* idx, const int32_t* cnts, const int32_t* col_ptr,
+                          const int32_t* rows, float* dq, float* dk, float* dv, int bh, int n, int d, int bq, int bk,
+                          int topk, float sm_scale, hipStream_t st);
 
 }  // namespace dsv

@@ -71,6 +71,107 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
   }
 }
 
+// ---------------------------------------------------------------- mass-threshold selection
+//
+// The pages keep the critical KV blocks that carry most (~90%) of the attention score ([de]
+// §2.A, [es] §2.A).  Per query block: the smallest set of KV blocks, taken by descending score
+// with ties to the smaller index, whose scores sum to at least tau times the row's total;
+// at most kmax blocks, never empty.  Output: ascending indices padded with -1 to kmax, and
+// the count.
+//
+// One wave64 per query block, lane l holding blocks e*64 + l.  Each block gets a unique key
+// (score key << 12 | (4095 - kb)), so descending key order is descending score with ties to
+// the smaller index, and the chosen set is {key >= T} for one threshold T.  T is the largest
+// key whose suffix mass S(T) = sum_{key >= T} score reaches the target, found by an MSB-first
+// bisection; every S is a per-lane sum in block order followed by a fixed butterfly, so the
+// result is deterministic.  A set larger than kmax is cut to its kmax largest keys by a second
+// bisection on counts.
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void select_mass_kernel(const float* __restrict__ scores,
+                                                          int32_t* __restrict__ idx, int32_t* __restrict__ cnts,
+                                                          int rows, int nkb, int kmax, float tau) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wave exits together
+  const float* src = scores + (size_t)row * nkb;
+  float val[NPL];
+  uint64_t key[NPL];
+  uint64_t kmaxkey = 0;
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) {
+    const int kb = e * 64 + lane;
+    val[e] = kb < nkb ? src[kb] : 0.f;
+    // padding keys are 0; valid keys are >= 1
+    key[e] = kb < nkb ? ((uint64_t)max(order_key(val[e]), 1u) << 12) | (uint64_t)(4095 - kb) : 0ull;
+    kmaxkey = key[e] > kmaxkey ? key[e] : kmaxkey;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = __shfl_xor(kmaxkey, off);
+    kmaxkey = o > kmaxkey ? o : kmaxkey;
+  }
+  auto suffix_mass = [&](uint64_t t) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) acc += key[e] >= t ? val[e] : 0.f;
+    return wave_sum(acc);
+  };
+  auto count_ge = [&](uint64_t t) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) c += popc64(__ballot(key[e] >= t));
+    return c;
+  };
+  const float target = tau * suffix_mass(1ull);
+  uint64_t T = 0;
+  for (int bit = 43; bit >= 0; --bit) {
+    const uint64_t cand = T | (1ull << bit);
+    if (cand <= kmaxkey && suffix_mass(cand) >= target) T = cand;
+  }
+  int m = count_ge(T);
+  if (m > kmax) {  // keep the kmax largest keys
+    T = 0;
+    for (int bit = 43; bit >= 0; --bit) {
+      const uint64_t cand = T | (1ull << bit);
+      if (count_ge(cand) >= kmax) T = cand;
+    }
+    m = kmax;
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t* dst = idx + (size_t)row * kmax;
+  int taken = 0;
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) {
+    const bool sel = key[e] >= T && key[e] != 0ull;
+    const uint64_t sel_m = __ballot(sel);
+    if (sel) dst[taken + popc64(sel_m & lt_mask)] = e * 64 + lane;
+    taken += popc64(sel_m);
+  }
+  for (int p = m + lane; p < kmax; p += 64) dst[p] = -1;
+  if (lane == 0) cnts[row] = m;
+}
+
+hipError_t launch_select_mass(const float* scores, int32_t* idx, int32_t* cnts, int rows, int nkb, int kmax,
+                              float tau, hipStream_t st) {
+  const dim3 grid((rows + 3) / 4), block(256);
+  const int npl = (nkb + 63) / 64;
+#define SEL(N_)                                                                                          \
+  if (npl <= N_) {                                                                                       \
+    hipLaunchKernelGGL((select_mass_kernel<N_>), grid, block, 0, st, scores, idx, cnts, rows, nkb, kmax, tau); \
+    return hipGetLastError();                                                                            \
+  }
+  SEL(1) SEL(2) SEL(4) SEL(8) SEL(16) SEL(32) SEL(64)
+#undef SEL
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_select_topk(const float* scores, int32_t* idx, int rows, int nkb, int k, hipStream_t st) {
   const dim3 grid((rows + 3) / 4), block(256);
   const int npl = (nkb + 63) / 64;

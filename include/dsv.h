@@ -13,6 +13,7 @@
  * The four compute calls, in pipeline order:
  *   dsv_predict          predicted attention mass per (query block, KV block)
  *   dsv_select_topk      the k most important KV blocks of each query block
+ *   dsv_select_mass      (alternative) the fewest blocks carrying a fraction tau of the score
  *   dsv_sparse_attn_fwd  softmax attention restricted to the selected blocks
  *   dsv_sparse_attn_bwd  its gradients with respect to Q, K and V
  *
@@ -138,6 +139,24 @@ dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const
 dsv_status dsv_select_topk(const dsv_problem* p, const float* block_scores, int32_t* block_idx,
                            void* stream);
 
+/*
+ * dsv_select_mass -- mass-threshold selection: keep the critical KV blocks that carry most of
+ * the predicted score ([de] §2.A and [es] §2.A: ~90% of the attention score lies in few KV
+ * pairs).  For every (b, h, qb): the smallest set of KV blocks, taken by descending
+ * block_scores with ties toward the smaller block index, whose scores sum to at least
+ * tau * (the row's total score); at most k = problem.topk blocks, never empty.
+ *
+ *   block_scores  [B, H, N/Bq, N/Bk] float32 input (dsv_predict's output)
+ *   tau           target fraction, 0 < tau <= 1
+ *   block_idx     [B, H, N/Bq, k] int32 output: the chosen blocks ascending, then -1 padding
+ *   block_counts  [B, H, N/Bq] int32 output: number of chosen blocks (1 .. k)
+ * Pass block_idx and block_counts on to the attention calls.  The count is an integer
+ * decided by a float32 sum; where the cumulative score at the cut lies within rounding of
+ * the target, it may differ by one from a sum formed in another order or precision.
+ */
+dsv_status dsv_select_mass(const dsv_problem* p, const float* block_scores, float tau, int32_t* block_idx,
+                           int32_t* block_counts, void* stream);
+
 /* Workspace bytes dsv_sparse_attn_fwd needs (0 if none is needed or the problem is
    invalid; with 0, `workspace` may be NULL). */
 size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);
@@ -155,6 +174,10 @@ size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);
  * but no memory outside the tensors is touched); duplicates count twice.
  *
  *   q, k, v     [B, H, N, d] inputs;  block_idx [B, H, N/Bq, k]
+ *   block_counts  optional [B, H, N/Bq] int32, or NULL: query block qb uses the first
+ *               block_counts[qb] entries of its block_idx row (clamped to [0, k]; the
+ *               rest are never read).  NULL means all k.  A query block with an empty
+ *               list gets O = 0 and lse = -inf.
  *   o           [B, H, N, d] output (dtype);  lse [B, H, N] float32 output
  *   o_lo        optional [B, H, N, d] bf16 output, or NULL.  DSV_BF16 only (must
  *               be NULL for DSV_F32).  When given, the forward computes P V
@@ -168,8 +191,8 @@ size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);
  *   workspace   >= dsv_sparse_attn_fwd_workspace_size(p) bytes (currently 0)
  */
 dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
-                               const int32_t* block_idx, void* o, float* lse, void* o_lo, void* workspace,
-                               size_t workspace_bytes, void* stream);
+                               const int32_t* block_idx, const int32_t* block_counts, void* o, float* lse,
+                               void* o_lo, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes dsv_sparse_attn_bwd needs (0 if the problem is invalid). */
 size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p);
@@ -184,6 +207,7 @@ size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p);
  * No gradient flows to the predictor or to block_idx.
  *
  *   q, k, v, o, dout  [B, H, N, d];  lse [B, H, N];  block_idx [B, H, N/Bq, k]
+ *   block_counts      the forward's block_counts, or NULL (all k)
  *   o_lo              the forward's o_lo output, or NULL (then D uses o alone).
  *                     DSV_BF16 only; must be NULL for DSV_F32.
  *   dq, dk, dv        [B, H, N, d] outputs (dtype), fully overwritten
@@ -191,8 +215,8 @@ size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p);
  */
 dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
                                const void* o, const void* o_lo, const void* dout, const float* lse,
-                               const int32_t* block_idx, void* dq, void* dk, void* dv,
-                               void* workspace, size_t workspace_bytes, void* stream);
+                               const int32_t* block_idx, const int32_t* block_counts, void* dq, void* dk,
+                               void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static English name of a status code. */
 const char* dsv_status_string(dsv_status s);

@@ -47,7 +47,8 @@ Readings where the pages are silent (each is listed again in the design doc):
      set of KV blocks, taken by descending score (ties to the smaller index), whose
      scores sum to at least tau times the row's total score; capped at kmax blocks,
      never empty.  Lists are ascending and padded with -1 to kmax; a negative entry
-     of any block list means "no block".
+     of any block list means "no block", and a query block whose list is empty has
+     O = 0, LSE = -inf and no gradient.
 """
 from __future__ import annotations
 
@@ -261,9 +262,12 @@ def selected_keys(idx_row: np.ndarray, bk: int) -> np.ndarray:
 def attn_fwd_qblock(q_blk, k, v, idx_row, bk: int, sm_scale: float) -> Tuple[np.ndarray, np.ndarray]:
     """Softmax attention of one query block over its selected keys only (R7).
 
-    Returns (O [Bq, d], LSE [Bq]) with LSE_i = log sum_j exp(sm_scale <q_i, k_j>).
+    Returns (O [Bq, d], LSE [Bq]) with LSE_i = log sum_j exp(sm_scale <q_i, k_j>).  An empty
+    list (R9) defines O = 0 and LSE = -inf.
     """
     keys = selected_keys(idx_row, bk)
+    if keys.size == 0:
+        return np.zeros((np.shape(q_blk)[0], np.shape(v)[-1])), np.full(np.shape(q_blk)[0], -np.inf)
     s = sm_scale * (np.asarray(q_blk, np.float64) @ np.asarray(k, np.float64)[keys].T)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
@@ -294,9 +298,12 @@ def attn_bwd_qblock(q_blk, k, v, do_blk, idx_row, bk: int, sm_scale: float):
     With S = sm_scale Q K_J^T, P = softmax_row(S), O = P V_J (J = selected keys):
       dV_J = P^T dO,   dP = dO V_J^T,   dS = P o (dP - rowsum(P o dP)),
       dQ = sm_scale dS K_J,   dK_J = sm_scale dS^T Q.
-    Returns (dQ [Bq, d], dK_J [|J|, d], dV_J [|J|, d], J).
+    Returns (dQ [Bq, d], dK_J [|J|, d], dV_J [|J|, d], J); an empty list has no gradient.
     """
     keys = selected_keys(idx_row, bk)
+    if keys.size == 0:
+        dq = np.zeros(np.shape(q_blk))
+        return dq, np.zeros((0, np.shape(k)[-1])), np.zeros((0, np.shape(v)[-1])), keys
     q_blk = np.asarray(q_blk, np.float64)
     kj = np.asarray(k, np.float64)[keys]
     vj = np.asarray(v, np.float64)[keys]
@@ -348,7 +355,7 @@ def attn_bwd_kvblock(q, k, v, do, idx, kb: int, bq: int, bk: int, sm_scale: floa
             continue
         rows = slice(qb * bq, (qb + 1) * bq)
         _, g_k, g_v, _ = attn_bwd_qblock(q[rows], k, v, do[rows], row, bk, sm_scale)
-        pos = int(hit[0])
+        pos = int(np.sum(row[:hit[0]] >= 0))  # position among the list's valid entries
         dk += g_k[pos * bk:(pos + 1) * bk]
         dv += g_v[pos * bk:(pos + 1) * bk]
     return dk, dv

@@ -77,7 +77,7 @@ def _prob(**kw):
 ])
 def test_forward_rejects_bad_problems_before_launch(lib, kw, code):
     p = _prob(**kw)
-    st = lib.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    st = lib.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st == code, lib.dsv_last_error()
     assert lib.dsv_last_error().decode()
 
@@ -88,21 +88,24 @@ def test_null_and_misaligned_pointers_are_rejected(lib):
     assert lib.dsv_select_topk(ctypes.byref(p), None, FAKE, None) == 1
     assert lib.dsv_select_topk(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 2), FAKE, None) == 1
     assert "aligned" in lib.dsv_last_error().decode()
-    st = lib.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, ctypes.c_void_p((1 << 20) + 8), FAKE, FAKE, FAKE, FAKE, None,
-                                 FAKE, 1 << 40, None)
+    st = lib.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, ctypes.c_void_p((1 << 20) + 8), FAKE, FAKE, None, FAKE, FAKE,
+                                 None, FAKE, 1 << 40, None)
     assert st == 1
+    st = lib.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 2), FAKE, FAKE,
+                                 None, FAKE, 1 << 40, None)
+    assert st == 1 and "block_counts" in lib.dsv_last_error().decode()
 
 
 def test_o_residual_is_bf16_only_and_aligned(lib):
-    args = lambda prob, olo: (ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, olo, FAKE, 1 << 40, None)
+    args = lambda prob, olo: (ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, olo, FAKE, 1 << 40, None)
     p32 = _prob(dtype=dsv.DSV_F32)
     assert lib.dsv_sparse_attn_fwd(*args(p32, FAKE)) == 1
     assert "o_lo" in lib.dsv_last_error().decode()
     assert lib.dsv_sparse_attn_fwd(*args(_prob(), ctypes.c_void_p((1 << 20) + 4))) == 1
     assert "o_lo" in lib.dsv_last_error().decode()
     nb = lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(p32))
-    st = lib.dsv_sparse_attn_bwd(ctypes.byref(p32), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                 FAKE, nb, None)
+    st = lib.dsv_sparse_attn_bwd(ctypes.byref(p32), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                 FAKE, FAKE, nb, None)
     assert st == 1 and "o_lo" in lib.dsv_last_error().decode()
 
 
@@ -112,8 +115,8 @@ def test_workspace_sizes_and_short_workspace_is_rejected(lib):
     nb = lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(p))
     # bf16 backward: lse2 + D (2 x B*H*N floats), the block-order list, and the transposed block lists
     assert nb >= 2 * 2 * 1024 * 4 + 2 * 16 * 4 + 2 * 16 * 2 * 4
-    st = lib.dsv_sparse_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                 FAKE, nb - 1, None)
+    st = lib.dsv_sparse_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                 FAKE, FAKE, nb - 1, None)
     assert st == 3
     assert lib.dsv_sparse_attn_fwd_workspace_size(None) == 0
     assert lib.dsv_sparse_attn_bwd_workspace_size(None) == 0
@@ -126,3 +129,13 @@ def test_predictor_rejects_unsupported_rank(lib):
     p = _prob(seq_len=64 * 3, q_block=64)  # N % 256 != 0 for the bf16 predictor
     p.topk = 1
     assert lib.dsv_predict(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, FAKE, None) == 2
+
+
+def test_select_mass_validates_tau_and_pointers(lib):
+    p = _prob(topk=4)
+    for tau in (0.0, -0.5, 1.5, float("nan")):
+        assert lib.dsv_select_mass(ctypes.byref(p), FAKE, ctypes.c_float(tau), FAKE, FAKE, None) == 1
+        assert "tau" in lib.dsv_last_error().decode()
+    assert lib.dsv_select_mass(ctypes.byref(p), FAKE, ctypes.c_float(0.9), FAKE, None, None) == 1
+    assert "block_counts" in lib.dsv_last_error().decode()
+    assert lib.dsv_select_mass(ctypes.byref(_prob(topk=17)), FAKE, ctypes.c_float(0.9), FAKE, FAKE, None) == 1

@@ -423,3 +423,18 @@ def test_padded_block_lists_select_nothing_extra():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
     for a, b in zip(O.sparse_attn_bwd(q, k, v, do, full, bq, bk, 0.25), O.sparse_attn_bwd(q, k, v, do, padded, bq, bk, 0.25)):
         assert np.array_equal(a, b)
+
+
+def test_empty_block_list_defines_zero_output_and_gradient():
+    rng = np.random.default_rng(4)
+    n, d, bq, bk = 128, 8, 64, 64
+    q, k, v, do = (rng.standard_normal((1, 1, n, d)) for _ in range(4))
+    idx = np.array([[[[1, -1], [-1, -1]]]], np.int32)  # query block 1 selects nothing
+    o, lse = O.sparse_attn_fwd(q, k, v, idx, bq, bk, 0.3)
+    assert np.all(o[0, 0, 64:] == 0) and np.all(np.isneginf(lse[0, 0, 64:]))
+    o1, _ = O.attn_fwd_qblock(q[0, 0, :64], k[0, 0], v[0, 0], np.array([1]), bk, 0.3)
+    assert np.array_equal(o[0, 0, :64], o1)
+    dq, dk, dv = O.sparse_attn_bwd(q, k, v, do, idx, bq, bk, 0.3)
+    assert np.all(dq[0, 0, 64:] == 0) and np.all(dk[0, 0, :64] == 0) and np.all(dv[0, 0, :64] == 0)
+    gk, gv = O.attn_bwd_kvblock(q[0, 0], k[0, 0], v[0, 0], do[0, 0], idx[0, 0], 1, bq, bk, 0.3)
+    assert np.allclose(gk, dk[0, 0, 64:]) and np.allclose(gv, dv[0, 0, 64:])
