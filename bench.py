@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
     ap.add_argument("--no-mass", action="store_true", help="skip the mass-threshold selection leg")
+    ap.add_argument("--no-rep", action="store_true", help="skip the representative-row predictor leg")
     ap.add_argument("--mass-tau", type=float, default=0.1,
                     help="tau of the mass-threshold leg (kmax = 2k); with the random-init predictor's near-uniform "
                          "scores, 0.1 selects about the headline density")
@@ -298,6 +299,22 @@ def main():
             f"bwd {ms[2]:.1f} ms")
         del wsb3
 
+    rep = None
+    if not a.no_rep:
+        # representative-row predictor (one row per query block) and top-k on its scores
+        log("[bench] representative-row leg (row 0 of each query block)")
+        evr = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for _ in range(2):  # the first pass warms up
+            evr[0].record(stream)
+            dsv.predict(t["q"], t["k"], t["wq"], t["wk"], rep_row=0, workspace=wsp, out=scores, **kw)
+            evr[1].record(stream)
+            dsv.select_topk(scores, cfg.topk, out=idx, **kw)
+            evr[2].record(stream)
+            evr[2].synchronize()
+        rep = {"rep_row": 0, "predict_ms": evr[0].elapsed_time(evr[1]), "select_ms": evr[1].elapsed_time(evr[2]),
+               "logits": float(B * H * cfg.nqb) * N}
+        log(f"[bench] representative leg: predict {rep['predict_ms']:.2f} ms, select {rep['select_ms']:.2f} ms")
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] CPU oracle baseline (bounded sample)")
@@ -318,7 +335,7 @@ def main():
         "attn_fwd_bwd": {"ms": attn_ms, "tflops": attn_tflops, "frac_of_peak": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
                          "tokens_per_s": B * N / (attn_ms * 1e-3)},
         "phases_ms": {"predict": phases[0], "select": phases[1], "fwd": phases[2], "bwd": phases[3]},
-        "kernels": kern, "kernel_rates": rates, "dense": dense, "mass_selection": mass,
+        "kernels": kern, "kernel_rates": rates, "dense": dense, "mass_selection": mass, "representative": rep,
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -7,7 +7,7 @@ library's HIP kernels.  There is no fallback: if the library is missing, or the
 tensors are not on a GPU, the calls raise.
 
 Entry points (same names as the C ABI):
-  predict(q, k, wq, wk, ...)          -> block_scores [B, H, N/Bq, N/Bk] float32
+  predict(q, k, wq, wk, ...)          -> block_scores [B, H, N/Bq, N/Bk] float32 (rep_row=...: one-row masses)
   select_topk(block_scores, topk)     -> block_idx    [B, H, N/Bq, k]    int32
   select_mass(block_scores, tau, kmax) -> (block_idx [B, H, N/Bq, kmax] padded with -1, block_counts)
   sparse_attn_fwd(q, k, v, idx, ...)  -> (o, lse), or (o, lse, o_lo) with residual=True
@@ -28,7 +28,8 @@ DSV_F32, DSV_BF16 = 0, 1
 STATUS = {0: "DSV_OK", 1: "DSV_ERR_INVALID_ARGUMENT", 2: "DSV_ERR_UNSUPPORTED", 3: "DSV_ERR_WORKSPACE_TOO_SMALL",
           4: "DSV_ERR_HIP"}
 
-EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_select_topk", "dsv_select_mass",
+EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_predict_representative", "dsv_select_topk",
+            "dsv_select_mass",
             "dsv_sparse_attn_fwd_workspace_size",
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd_workspace_size", "dsv_sparse_attn_bwd", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_timing_begin", "dsv_timing_end")
@@ -69,6 +70,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "dsv_predict_workspace_size": (S, [P]),
         "dsv_predict": (ctypes.c_int, [P, V, V, V, V, V, S, V, V]),
+        "dsv_predict_representative": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, V, S, V, V]),
         "dsv_select_topk": (ctypes.c_int, [P, V, V, V]),
         "dsv_select_mass": (ctypes.c_int, [P, V, ctypes.c_float, V, V, V]),
         "dsv_sparse_attn_fwd_workspace_size": (S, [P]),
@@ -157,9 +159,12 @@ def predict_workspace_size(prob: Problem) -> int:
 
 
 def predict(q, k, wq, wk, *, q_block: int, kv_block: int = 64, pred_scale: Optional[float] = None,
-            workspace: Optional[torch.Tensor] = None, return_projections: bool = False,
-            out: Optional[torch.Tensor] = None):
-    """Predicted attention mass per (query block, KV block): [B, H, N/Bq, N/Bk] float32."""
+            rep_row: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+            return_projections: bool = False, out: Optional[torch.Tensor] = None):
+    """Predicted attention mass per (query block, KV block): [B, H, N/Bq, N/Bk] float32.
+
+    With ``rep_row`` the representative-row variant: the mass of the single row
+    qb * q_block + rep_row of each query block (rows sum to 1)."""
     lib = load_library()
     dev = _dev(q, k, wq, wk)
     _contig(q, k, wq, wk)
@@ -173,8 +178,13 @@ def predict(q, k, wq, wk, *, q_block: int, kv_block: int = 64, pred_scale: Optio
     ws = _workspace(int(lib.dsv_predict_workspace_size(ctypes.byref(prob))), dev, workspace)
     scores = out if out is not None else torch.empty((b, h, n // q_block, n // kv_block), dtype=torch.float32,
                                                      device=dev)
-    _check(lib.dsv_predict(ctypes.byref(prob), _p(q), _p(k), _p(wq), _p(wk), _p(ws), ws.numel() * ws.element_size(),
-                           _p(scores), _stream(dev)), "dsv_predict")
+    nbytes = ws.numel() * ws.element_size()
+    if rep_row is None:
+        _check(lib.dsv_predict(ctypes.byref(prob), _p(q), _p(k), _p(wq), _p(wk), _p(ws), nbytes, _p(scores),
+                               _stream(dev)), "dsv_predict")
+    else:
+        _check(lib.dsv_predict_representative(ctypes.byref(prob), _p(q), _p(k), _p(wq), _p(wk), int(rep_row), _p(ws),
+                                              nbytes, _p(scores), _stream(dev)), "dsv_predict_representative")
     if return_projections:
         esz = q.element_size()
         lr = b * h * n * r * esz

@@ -248,11 +248,13 @@ size_t dsv_predict_workspace_size(const dsv_problem* p) {
   return predict_ws(o).total;
 }
 
-dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const void* wq, const void* wk,
-                       void* workspace, size_t workspace_bytes, float* block_scores, void* stream) {
-  g_err.clear();
+namespace {
+// shared by dsv_predict (rep < 0) and dsv_predict_representative (rep = the representative row)
+dsv_status predict_impl(const dsv_problem* p, const void* q, const void* k, const void* wq, const void* wk,
+                        void* workspace, size_t workspace_bytes, float* block_scores, int rep, void* stream) {
   Prob o;
   TRY(to_prob(p, o, true));
+  if (rep >= o.bq) return fail(DSV_ERR_INVALID_ARGUMENT, "rep_row must lie in [0, q_block)");
   if (o.dtype == DSV_BF16) {
     if ((o.d != 64 && o.d != 128) || (o.r != 16 && o.r != 32) || (o.bq != 64 && o.bq != 128) || o.bk != 64 ||
         o.n % 256)
@@ -278,7 +280,7 @@ dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const
     TRY_HIP(dsv::launch_proj_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(wk), klr, o.bh(), o.n,
                                   o.h, o.d, o.r, st), "proj_kernel(k)");
     TRY_HIP(dsv::launch_scores_bf16(qlr, klr, at<float>(workspace, w.scratch), block_scores, o.bh(), o.n, o.nkb(),
-                                    o.r, o.bq, o.ps, st), "scores_kernel");
+                                    o.r, o.bq, o.ps, rep, st), "scores_kernel");
   } else {
     float* qlr = at<float>(workspace, w.qlr);
     float* klr = at<float>(workspace, w.klr);
@@ -286,10 +288,29 @@ dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const
                                  o.d, o.r, st), "proj_kernel(q)");
     TRY_HIP(dsv::launch_proj_f32(static_cast<const float*>(k), static_cast<const float*>(wk), klr, o.bh(), o.n, o.h,
                                  o.d, o.r, st), "proj_kernel(k)");
-    TRY_HIP(dsv::launch_scores_f32(qlr, klr, at<float>(workspace, w.lse), block_scores, o.bh(), o.n, o.r, o.bq, o.bk,
-                                   o.ps, st), "scores_kernel");
+    if (rep < 0)
+      TRY_HIP(dsv::launch_scores_f32(qlr, klr, at<float>(workspace, w.lse), block_scores, o.bh(), o.n, o.r, o.bq,
+                                     o.bk, o.ps, st), "scores_kernel");
+    else
+      TRY_HIP(dsv::launch_rep_scores_f32(qlr, klr, at<float>(workspace, w.lse), block_scores, o.bh(), o.n, o.r,
+                                         o.bq, o.bk, o.ps, rep, st), "scores_kernel");
   }
   return DSV_OK;
+}
+}  // namespace
+
+dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const void* wq, const void* wk,
+                       void* workspace, size_t workspace_bytes, float* block_scores, void* stream) {
+  g_err.clear();
+  return predict_impl(p, q, k, wq, wk, workspace, workspace_bytes, block_scores, -1, stream);
+}
+
+dsv_status dsv_predict_representative(const dsv_problem* p, const void* q, const void* k, const void* wq,
+                                      const void* wk, int32_t rep_row, void* workspace, size_t workspace_bytes,
+                                      float* block_scores, void* stream) {
+  g_err.clear();
+  if (rep_row < 0) return fail(DSV_ERR_INVALID_ARGUMENT, "rep_row must lie in [0, q_block)");
+  return predict_impl(p, q, k, wq, wk, workspace, workspace_bytes, block_scores, rep_row, stream);
 }
 
 dsv_status dsv_select_topk(const dsv_problem* p, const float* block_scores, int32_t* block_idx, void* stream) {

@@ -16,8 +16,12 @@ hipError_t launch_proj_f32(const float* x, const float* w, float* out, int bh, i
                            hipStream_t st);
 int score_slots(int items);
 size_t score_scratch_bytes(int items, int nkb);
+int score_items(int bh, int n, int bq, bool representative);
+// rep < 0: block scores (every row of a query block); rep >= 0: the masses of row qb * bq + rep
 hipError_t launch_scores_bf16(const uint16_t* qlr, const uint16_t* klr, float* scratch, float* scores, int bh,
-                              int n, int nkb, int r, int bq, float pred_scale, hipStream_t st);
+                              int n, int nkb, int r, int bq, float pred_scale, int rep, hipStream_t st);
+hipError_t launch_rep_scores_f32(const float* qlr, const float* klr, float* lse, float* scores, int bh, int n,
+                                 int r, int bq, int bk, float pred_scale, int rep, hipStream_t st);
 hipError_t launch_scores_f32(const float* qlr, const float* klr, float* lse, float* scores, int bh, int n, int r,
                              int bq, int bk, float pred_scale, hipStream_t st);
 

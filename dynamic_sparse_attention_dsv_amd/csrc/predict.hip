@@ -90,12 +90,15 @@ __global__ void proj_f32_kernel(const float* __restrict__ x, const float* __rest
 
 constexpr int kScoreRows = 256;  // query rows per work item (4 waves x 64)
 
-template <int R, int BQ>
+// REP = false: work-item rows are 256 consecutive query rows; a score sums its query block's rows.
+// REP = true (representative rows, [de] §2.B query grouping): work-item rows are the rows
+// qb * BQ + rep of 256 consecutive query blocks, and a score is that one row's mass.
+template <int R, int BQ, bool REP>
 __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __restrict__ qlr,
                                                           const uint16_t* __restrict__ klr,
                                                           float* __restrict__ scratch,
                                                           float* __restrict__ scores, int n, int nkb,
-                                                          int items, float pc) {
+                                                          int items, float pc, int rep) {
   // qlr, klr: [BH, n, R] bf16.  scratch: gridDim.x slots of [nkb][256] float.
   // scores: [BH, n/BQ, nkb].  pc = pred_scale * log2(e).
   // Each wave owns 64 query rows (two 32-row halves): every K_lr fragment it loads feeds
@@ -115,18 +118,22 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
   float* slot = scratch + (size_t)blockIdx.x * nkb * kScoreRows;
-  const int items_per_head = n / kScoreRows;
+  const int nqb = n / BQ;
+  const int items_per_head = REP ? (nqb + kScoreRows - 1) / kScoreRows : n / kScoreRows;
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int bh = item / items_per_head;
-    const int row0 = (item % items_per_head) * kScoreRows;
+    const int row0 = (item % items_per_head) * kScoreRows;  // first row, or first query block (REP)
+    // query row of the item's local row i (REP: past the last query block the row is clamped
+    // to a valid one and its scores are never written)
+    auto qrow_of = [&](int i) { return REP ? min(row0 + i, nqb - 1) * BQ + rep : row0 + i; };
     const uint16_t* kh = klr + (size_t)bh * n * R;
     // B operands = (pc Q_lr)^T as hi and lo parts for the wave's two 32-row halves: lane holds
     // its query row, 8 consecutive r per chunk
     bf16x8 qh[2][NC], ql[2][NC];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint16_t* qrow = qlr + ((size_t)bh * n + row0 + wave * 64 + h * 32 + c32) * R;
+      const uint16_t* qrow = qlr + ((size_t)bh * n + qrow_of(wave * 64 + h * 32 + c32)) * R;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const u32x4 raw = ld16(qrow + c * 16 + g * 8);
@@ -247,6 +254,22 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
     __threadfence_block();
     __syncthreads();
 
+    if constexpr (REP) {
+      // finalize: score[qb0 + i, kb] = mass[kb][i] / T_i (log domain on the exact path); each
+      // wave writes its 64 rows, lane <-> kb
+      float* sc_head = scores + (size_t)bh * nqb * nkb;
+      for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
+        const int kb = kb0 + lane;
+        if (kb >= nkb) continue;
+        const float* src = slot + (size_t)kb * kScoreRows;
+        for (int i = wave * 64; i < wave * 64 + 64; ++i) {
+          if (row0 + i >= nqb) break;
+          sc_head[(size_t)(row0 + i) * nkb + kb] = exact ? fast_exp2(src[i] - row_s[i]) : src[i] * row_s[i];
+        }
+      }
+      __syncthreads();  // the slot and row_s are reused by the next item
+      continue;
+    }
     // finalize: score[qb, kb] = sum_{i in qb} mass[kb][i] / T_i  (log domain on the exact path).
     // chunks of 64 KV blocks: lane <-> kb, wave w sums its rows [64w, 64w+64).
     float* sc_head = scores + (size_t)bh * (n / BQ) * nkb;
@@ -338,6 +361,61 @@ __global__ void scores_f32_kernel(const float* __restrict__ qlr, const float* __
   scores[t] = acc;
 }
 
+// representative rows (f32): the log-sum-exp of row qb * bq + rep over all keys, then that
+// row's mass on each KV block
+__global__ void rep_lse_f32_kernel(const float* __restrict__ qlr, const float* __restrict__ klr,
+                                   float* __restrict__ lse, int n, int r, int bq, int rep, float ps, int rows) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;  // bh * nqb + qb
+  if (t >= rows) return;
+  const int nqb = n / bq, bh = t / nqb, qb = t % nqb;
+  const float* q = qlr + ((size_t)bh * n + (size_t)qb * bq + rep) * r;
+  const float* kh = klr + (size_t)bh * n * r;
+  float m = -INFINITY;
+  for (int j = 0; j < n; ++j) {
+    float a = 0.f;
+    for (int c = 0; c < r; ++c) a = fmaf(q[c], kh[(size_t)j * r + c], a);
+    m = fmaxf(m, a * ps);
+  }
+  float sum = 0.f;
+  for (int j = 0; j < n; ++j) {
+    float a = 0.f;
+    for (int c = 0; c < r; ++c) a = fmaf(q[c], kh[(size_t)j * r + c], a);
+    sum += expf(a * ps - m);
+  }
+  lse[t] = m + logf(sum);
+}
+
+__global__ void rep_scores_f32_kernel(const float* __restrict__ qlr, const float* __restrict__ klr,
+                                      const float* __restrict__ lse, float* __restrict__ scores, int n, int r,
+                                      int bq, int bk, int rep, float ps, int total) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;  // (bh * nqb + qb) * nkb + kb
+  if (t >= total) return;
+  const int nkb = n / bk, nqb = n / bq;
+  const int kb = t % nkb, row = t / nkb, bh = row / nqb, qb = row % nqb;
+  const float* q = qlr + ((size_t)bh * n + (size_t)qb * bq + rep) * r;
+  const float* kh = klr + (size_t)bh * n * r;
+  float acc = 0.f;
+  for (int j = kb * bk; j < (kb + 1) * bk; ++j) {
+    float a = 0.f;
+    for (int c = 0; c < r; ++c) a = fmaf(q[c], kh[(size_t)j * r + c], a);
+    acc += expf(a * ps - lse[row]);
+  }
+  scores[t] = acc;
+}
+
+hipError_t launch_rep_scores_f32(const float* qlr, const float* klr, float* lse, float* scores, int bh, int n,
+                                 int r, int bq, int bk, float pred_scale, int rep, hipStream_t st) {
+  const int rows = bh * (n / bq);
+  hipLaunchKernelGGL(rep_lse_f32_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, qlr, klr, lse, n, r, bq, rep,
+                     pred_scale, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int total = rows * (n / bk);
+  hipLaunchKernelGGL(rep_scores_f32_kernel, dim3((total + 255) / 256), dim3(256), 0, st, qlr, klr, lse, scores, n, r,
+                     bq, bk, rep, pred_scale, total);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* w, uint16_t* out, int bh, int n, int heads,
@@ -374,16 +452,25 @@ size_t score_scratch_bytes(int items, int nkb) {
   return (size_t)score_slots(items) * nkb * kScoreRows * sizeof(float);
 }
 
+int score_items(int bh, int n, int bq, bool representative) {
+  return representative ? bh * ((n / bq + kScoreRows - 1) / kScoreRows) : bh * (n / kScoreRows);
+}
+
 hipError_t launch_scores_bf16(const uint16_t* qlr, const uint16_t* klr, float* scratch, float* scores,
-                              int bh, int n, int nkb, int r, int bq, float pred_scale, hipStream_t st) {
-  const int items = bh * (n / kScoreRows);
+                              int bh, int n, int nkb, int r, int bq, float pred_scale, int rep, hipStream_t st) {
+  const bool representative = rep >= 0;
+  const int items = score_items(bh, n, bq, representative);
   const int slots = score_slots(items);
   const float pc = pred_scale * kLog2e;
-#define SC(R_, BQ_)                                                                                    \
-  if (r == R_ && bq == BQ_) {                                                                          \
-    hipLaunchKernelGGL((scores_bf16_kernel<R_, BQ_>), dim3(slots), dim3(256), 0, st, qlr, klr, scratch, \
-                       scores, n, nkb, items, pc);                                                     \
-    return hipGetLastError();                                                                          \
+#define SC(R_, BQ_)                                                                                           \
+  if (r == R_ && bq == BQ_) {                                                                                 \
+    if (representative)                                                                                       \
+      hipLaunchKernelGGL((scores_bf16_kernel<R_, BQ_, true>), dim3(slots), dim3(256), 0, st, qlr, klr, scratch, \
+                         scores, n, nkb, items, pc, rep);                                                     \
+    else                                                                                                      \
+      hipLaunchKernelGGL((scores_bf16_kernel<R_, BQ_, false>), dim3(slots), dim3(256), 0, st, qlr, klr,         \
+                         scratch, scores, n, nkb, items, pc, 0);                                              \
+    return hipGetLastError();                                                                                 \
   }
   SC(16, 64) SC(16, 128) SC(32, 64) SC(32, 128)
 #undef SC

@@ -12,6 +12,7 @@
  *
  * The four compute calls, in pipeline order:
  *   dsv_predict          predicted attention mass per (query block, KV block)
+ *   dsv_predict_representative  (alternative) the mass of one representative row per query block
  *   dsv_select_topk      the k most important KV blocks of each query block
  *   dsv_select_mass      (alternative) the fewest blocks carrying a fraction tau of the score
  *   dsv_sparse_attn_fwd  softmax attention restricted to the selected blocks
@@ -126,6 +127,25 @@ size_t dsv_predict_workspace_size(const dsv_problem* p);
 dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const void* wq,
                        const void* wk, void* workspace, size_t workspace_bytes,
                        float* block_scores, void* stream);
+
+/*
+ * dsv_predict_representative -- the representative-row variant of the predictor ([de] §2.B,
+ * query grouping: the critical pairs of a group of neighbouring queries are estimated for one
+ * representative of the group).  Same inputs, projections and workspace as dsv_predict; the
+ * score of (qb, kb) is the predicted softmax mass that the single query row
+ * qb * Bq + rep_row puts on KV block kb (each score row sums to 1):
+ *   score[qb, kb] = sum_{j in kb} exp(l_ij - LSE_i),   i = qb * Bq + rep_row.
+ * The ranking of a row's blocks equals the ranking of their in-block log-sum-exp of logits,
+ * so top-k on these scores needs no statistics of other rows.  Feed the scores to
+ * dsv_select_topk or dsv_select_mass.  Costs 1/Bq of dsv_predict's logit sweep.
+ *
+ *   rep_row       0 <= rep_row < Bq
+ *   block_scores  [B, H, N/Bq, N/Bk] float32 output
+ * The bf16 instance needs the same sizes as dsv_predict.
+ */
+dsv_status dsv_predict_representative(const dsv_problem* p, const void* q, const void* k, const void* wq,
+                                      const void* wk, int32_t rep_row, void* workspace, size_t workspace_bytes,
+                                      float* block_scores, void* stream);
 
 /*
  * dsv_select_topk -- critical-KV selection ([de] §2.B, top-k selection;

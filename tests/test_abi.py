@@ -139,3 +139,11 @@ def test_select_mass_validates_tau_and_pointers(lib):
     assert lib.dsv_select_mass(ctypes.byref(p), FAKE, ctypes.c_float(0.9), FAKE, None, None) == 1
     assert "block_counts" in lib.dsv_last_error().decode()
     assert lib.dsv_select_mass(ctypes.byref(_prob(topk=17)), FAKE, ctypes.c_float(0.9), FAKE, FAKE, None) == 1
+
+
+def test_representative_predictor_validates_the_row(lib):
+    p = _prob()
+    for rep in (-1, 64):
+        assert lib.dsv_predict_representative(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, rep, FAKE, 1 << 40, FAKE,
+                                              None) == 1
+        assert "rep_row" in lib.dsv_last_error().decode()
