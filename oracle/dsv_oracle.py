@@ -246,6 +246,46 @@ def mass_margin(scores: np.ndarray, tau: float) -> np.ndarray:
     return out.reshape(scores.shape[:-1])
 
 
+def pack_selected(idx: np.ndarray, counts: Optional[np.ndarray], qb_begin: int, qb_end: int, nkb: int):
+    """Sequence-parallel send list ([de] §2.C, [es] §2.C: context parallelism that moves only the
+    KV the selection needs): per (b, h) the union of the KV blocks selected by query blocks
+    [qb_begin, qb_end), ascending.
+
+    idx [B, H, nqb, k], counts [B, H, nqb] or None (all k).  Returns
+      blocks [B, H, nkb]  the union ascending, then -1;   count [B, H];
+      remapped [B, H, qb_end - qb_begin, k]  each list entry's position in the union (-1 past
+      the row's count or for an out-of-range entry)."""
+    b_, h_, nqb, k = idx.shape
+    blocks = np.full((b_, h_, nkb), -1, np.int32)
+    count = np.zeros((b_, h_), np.int32)
+    remapped = np.full((b_, h_, qb_end - qb_begin, k), -1, np.int32)
+    for b in range(b_):
+        for h in range(h_):
+            lens = [k if counts is None else int(np.clip(counts[b, h, qb], 0, k)) for qb in range(nqb)]
+            sel = sorted({int(x) for qb in range(qb_begin, qb_end) for x in idx[b, h, qb, :lens[qb]] if 0 <= x < nkb})
+            blocks[b, h, :len(sel)] = sel
+            count[b, h] = len(sel)
+            where = {kb: u for u, kb in enumerate(sel)}
+            for qb in range(qb_begin, qb_end):
+                for j in range(lens[qb]):
+                    x = int(idx[b, h, qb, j])
+                    if 0 <= x < nkb:
+                        remapped[b, h, qb - qb_begin, j] = where[x]
+    return blocks, count, remapped
+
+
+def pack_rows(x: np.ndarray, blocks: np.ndarray, count: np.ndarray, bk: int) -> np.ndarray:
+    """[B, H, N, d] rows of the packed KV blocks: rows [u*bk, (u+1)*bk) of the result hold block
+    blocks[b, h, u] of x, for u < count; later rows are left zero."""
+    out = np.zeros_like(x)
+    for b in range(x.shape[0]):
+        for h in range(x.shape[1]):
+            for u in range(int(count[b, h])):
+                kb = int(blocks[b, h, u])
+                out[b, h, u * bk:(u + 1) * bk] = x[b, h, kb * bk:(kb + 1) * bk]
+    return out
+
+
 # --------------------------------------------------------------------------
 # 4. sparse attention over the selected blocks ([es] §3; [de] §2.A, stage 2)
 # --------------------------------------------------------------------------

@@ -438,3 +438,33 @@ def test_empty_block_list_defines_zero_output_and_gradient():
     assert np.all(dq[0, 0, 64:] == 0) and np.all(dk[0, 0, :64] == 0) and np.all(dv[0, 0, :64] == 0)
     gk, gv = O.attn_bwd_kvblock(q[0, 0], k[0, 0], v[0, 0], do[0, 0], idx[0, 0], 1, bq, bk, 0.3)
     assert np.allclose(gk, dk[0, 0, 64:]) and np.allclose(gv, dv[0, 0, 64:])
+
+
+# ------------------------------------------------------------------ packing for sequence sharding
+
+
+def test_packing_moves_exactly_the_union_and_attention_is_unchanged():
+    rng = np.random.default_rng(11)
+    n, d, bq, bk, k = 512, 8, 64, 32, 4
+    nqb, nkb = n // bq, n // bk
+    q, kk, v = (rng.standard_normal((1, 2, n, d)) for _ in range(3))
+    idx = np.stack([np.stack([np.sort(rng.choice(nkb, k, replace=False)) for _ in range(nqb)]) for _ in range(2)])[None]
+    counts = rng.integers(0, k + 1, (1, 2, nqb)).astype(np.int32)
+    qb0, qb1 = 2, 6
+    blocks, count, remapped = O.pack_selected(idx, counts, qb0, qb1, nkb)
+    for h in range(2):
+        want = set()
+        for qb in range(qb0, qb1):
+            want |= set(int(x) for x in idx[0, h, qb, :counts[0, h, qb]])
+        assert list(blocks[0, h, :count[0, h]]) == sorted(want) and np.all(blocks[0, h, count[0, h]:] == -1)
+        for qb in range(qb0, qb1):
+            c = counts[0, h, qb]
+            assert np.array_equal(blocks[0, h][remapped[0, h, qb - qb0, :c]], idx[0, h, qb, :c])
+            assert np.all(remapped[0, h, qb - qb0, c:] == -1)
+    kp, vp = O.pack_rows(kk, blocks, count, bk), O.pack_rows(v, blocks, count, bk)
+    # attention of the shard's query blocks over the packed buffer equals the original
+    rows = slice(qb0 * bq, qb1 * bq)
+    shard_idx = np.where(np.arange(k)[None, None, None, :] < counts[:, :, qb0:qb1, None], idx[:, :, qb0:qb1], -1)
+    o_ref, l_ref = O.sparse_attn_fwd(q[:, :, rows], kk, v, shard_idx, bq, bk, 0.3)
+    o_p, l_p = O.sparse_attn_fwd(q[:, :, rows], kp, vp, remapped, bq, bk, 0.3)
+    assert np.array_equal(o_ref, o_p) and np.array_equal(l_ref, l_p)
