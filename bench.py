@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
     ap.add_argument("--no-mass", action="store_true", help="skip the mass-threshold selection leg")
     ap.add_argument("--no-rep", action="store_true", help="skip the representative-row predictor leg")
+    ap.add_argument("--no-pack", action="store_true", help="skip the KV-packing (sequence-sharding) leg")
     ap.add_argument("--mass-tau", type=float, default=0.1,
                     help="tau of the mass-threshold leg (kmax = 2k); with the random-init predictor's near-uniform "
                          "scores, 0.1 selects about the headline density")
@@ -315,6 +316,27 @@ def main():
                "logits": float(B * H * cfg.nqb) * N}
         log(f"[bench] representative leg: predict {rep['predict_ms']:.2f} ms, select {rep['select_ms']:.2f} ms")
 
+    pack = None
+    if not a.no_pack:
+        # KV packing for one eighth of the query blocks (one GPU's share under 8-way sequence
+        # sharding), with the top-k lists of the timed steps
+        qb1 = cfg.nqb // 8
+        log(f"[bench] KV packing leg (query blocks [0, {qb1}))")
+        evp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(2):  # the first pass warms up
+            evp[0].record(stream)
+            kp, vp, pblocks, pcounts, _ = dsv.pack_kv(t["k"], t["v"], idx, 0, qb1, **kw)
+            evp[1].record(stream)
+            evp[1].synchronize()
+        ms_p = evp[0].elapsed_time(evp[1])
+        units = int(pcounts.sum().item())
+        moved = 2.0 * 2 * units * cfg.kv_block * D * t["k"].element_size()  # K and V, read + write
+        pack = {"query_blocks": qb1, "mean_union_blocks": units / (B * H), "ms": ms_p, "bytes_moved": moved,
+                "gbs": moved / (ms_p * 1e-3) / 1e9}
+        log(f"[bench] pack leg: union {pack['mean_union_blocks']:.0f} of {cfg.nkb} blocks per head, {ms_p:.2f} ms, "
+            f"{pack['gbs']:.0f} GB/s")
+        del kp, vp
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] CPU oracle baseline (bounded sample)")
@@ -335,7 +357,7 @@ def main():
         "attn_fwd_bwd": {"ms": attn_ms, "tflops": attn_tflops, "frac_of_peak": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
                          "tokens_per_s": B * N / (attn_ms * 1e-3)},
         "phases_ms": {"predict": phases[0], "select": phases[1], "fwd": phases[2], "bwd": phases[3]},
-        "kernels": kern, "kernel_rates": rates, "dense": dense, "mass_selection": mass, "representative": rep,
+        "kernels": kern, "kernel_rates": rates, "dense": dense, "mass_selection": mass, "representative": rep, "pack": pack,
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

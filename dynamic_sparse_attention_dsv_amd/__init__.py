@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   select_mass(block_scores, tau, kmax) -> (block_idx [B, H, N/Bq, kmax] padded with -1, block_counts)
   sparse_attn_fwd(q, k, v, idx, ...)  -> (o, lse), or (o, lse, o_lo) with residual=True
   sparse_attn_bwd(q, k, v, o, do, lse, idx, ..., o_lo=None) -> (dq, dk, dv)
+  pack_kv(k, v, idx, qb_begin, qb_end, ...) -> (k_packed, v_packed, packed_blocks, packed_counts, packed_idx)
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ STATUS = {0: "DSV_OK", 1: "DSV_ERR_INVALID_ARGUMENT", 2: "DSV_ERR_UNSUPPORTED", 
           4: "DSV_ERR_HIP"}
 
 EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_predict_representative", "dsv_select_topk",
-            "dsv_select_mass",
+            "dsv_select_mass", "dsv_pack_kv_workspace_size", "dsv_pack_kv",
             "dsv_sparse_attn_fwd_workspace_size",
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd_workspace_size", "dsv_sparse_attn_bwd", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_timing_begin", "dsv_timing_end")
@@ -73,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsv_predict_representative": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, V, S, V, V]),
         "dsv_select_topk": (ctypes.c_int, [P, V, V, V]),
         "dsv_select_mass": (ctypes.c_int, [P, V, ctypes.c_float, V, V, V]),
+        "dsv_pack_kv_workspace_size": (S, [P]),
+        "dsv_pack_kv": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, ctypes.c_int32, V, V, V, V, V, V, S, V]),
         "dsv_sparse_attn_fwd_workspace_size": (S, [P]),
         "dsv_sparse_attn_fwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, V, S, V]),
         "dsv_sparse_attn_bwd_workspace_size": (S, [P]),
@@ -300,6 +303,28 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block:
                                    _p(block_idx), _p(block_counts), _p(dq), _p(dk), _p(dv), _p(ws),
                                    ws.numel() * ws.element_size(), _stream(dev)), "dsv_sparse_attn_bwd")
     return dq, dk, dv
+
+
+def pack_kv(k, v, block_idx, qb_begin: int, qb_end: int, *, q_block: int, kv_block: int = 64,
+            block_counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Pack the KV blocks selected by query blocks [qb_begin, qb_end) for sequence sharding ->
+    (k_packed, v_packed [B,H,N,d], packed_blocks [B,H,N/Bk], packed_counts [B,H],
+    packed_idx [B,H,qb_end-qb_begin,k])."""
+    lib = load_library()
+    dev = _dev(k, v, block_idx)
+    _contig(k, v, block_idx)
+    b, h, n, d = k.shape
+    prob = make_problem(k, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1])
+    _check_counts(block_counts, block_idx)
+    ws = _workspace(int(lib.dsv_pack_kv_workspace_size(ctypes.byref(prob))), dev, workspace)
+    kp, vp = torch.empty_like(k), torch.empty_like(v)
+    blocks = torch.empty((b, h, n // kv_block), dtype=torch.int32, device=dev)
+    counts = torch.empty((b, h), dtype=torch.int32, device=dev)
+    pidx = torch.empty((b, h, max(qb_end - qb_begin, 0), block_idx.shape[-1]), dtype=torch.int32, device=dev)
+    _check(lib.dsv_pack_kv(ctypes.byref(prob), _p(k), _p(v), _p(block_idx), _p(block_counts), int(qb_begin),
+                           int(qb_end), _p(kp), _p(vp), _p(blocks), _p(counts), _p(pidx) if pidx.numel() else None,
+                           _p(ws), ws.numel() * ws.element_size(), _stream(dev)), "dsv_pack_kv")
+    return kp, vp, blocks, counts, pidx
 
 
 def workspace_sizes(q: torch.Tensor, *, q_block: int, kv_block: int, topk: int, rank: int):

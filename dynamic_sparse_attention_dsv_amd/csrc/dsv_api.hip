@@ -339,6 +339,42 @@ dsv_status dsv_select_mass(const dsv_problem* p, const float* block_scores, floa
   return DSV_OK;
 }
 
+size_t dsv_pack_kv_workspace_size(const dsv_problem* p) {
+  Prob o;
+  if (to_prob(p, o, false) != DSV_OK) return 0;
+  return 2 * align_up((size_t)o.bh() * o.nkb() * 4);
+}
+
+dsv_status dsv_pack_kv(const dsv_problem* p, const void* k, const void* v, const int32_t* block_idx,
+                       const int32_t* block_counts, int32_t qb_begin, int32_t qb_end, void* k_packed, void* v_packed,
+                       int32_t* packed_blocks, int32_t* packed_counts, int32_t* packed_idx, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, false));
+  if (qb_begin < 0 || qb_end > o.nqb() || qb_begin > qb_end)
+    return fail(DSV_ERR_INVALID_ARGUMENT, "need 0 <= qb_begin <= qb_end <= N/Bq");
+  const void* ptrs[] = {k, v, k_packed, v_packed};
+  const char* names[] = {"k", "v", "k_packed", "v_packed"};
+  for (int i = 0; i < 4; ++i) TRY(check_ptr(ptrs[i], names[i]));
+  TRY(check_ptr(block_idx, "block_idx", 4));
+  if (block_counts) TRY(check_ptr(block_counts, "block_counts", 4));
+  TRY(check_ptr(packed_blocks, "packed_blocks", 4));
+  TRY(check_ptr(packed_counts, "packed_counts", 4));
+  if (qb_end > qb_begin) TRY(check_ptr(packed_idx, "packed_idx", 4));
+  TRY(check_ptr(workspace, "workspace", kWsAlign));
+  const size_t half = align_up((size_t)o.bh() * o.nkb() * 4);
+  if (workspace_bytes < 2 * half)
+    return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "pack workspace needs " + std::to_string(2 * half) + " bytes");
+  if (o.bk != 64) return fail(DSV_ERR_UNSUPPORTED, "packing needs Bk = 64");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY_HIP(dsv::launch_pack_kv(k, v, block_idx, block_counts, k_packed, v_packed, packed_blocks, packed_counts,
+                              packed_idx, at<int32_t>(workspace, 0), at<int32_t>(workspace, half), o.bh(), o.n,
+                              (int)(o.d * o.esize()), o.nqb(), o.nkb(), o.k, qb_begin, qb_end, st),
+          "pack_kernels");
+  return DSV_OK;
+}
+
 size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p) {
   Prob o;
   if (to_prob(p, o, false) != DSV_OK) return 0;

@@ -56,4 +56,9 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
                           const int32_t* rows, float* dq, float* dk, float* dv, int bh, int n, int d, int bq, int bk,
                           int topk, float sm_scale, hipStream_t st);
 
+// packing of selected KV blocks (sequence sharding)
+hipError_t launch_pack_kv(const void* k, const void* v, const int32_t* idx, const int32_t* cnts, void* kp, void* vp,
+                          int32_t* blocks, int32_t* count, int32_t* packed_idx, int32_t* flags, int32_t* pos, int bh,
+                          int n, int row_bytes, int nqb, int nkb, int topk, int qb0, int qb1, hipStream_t st);
+
 }  // namespace dsv

@@ -177,6 +177,29 @@ dsv_status dsv_select_topk(const dsv_problem* p, const float* block_scores, int3
 dsv_status dsv_select_mass(const dsv_problem* p, const float* block_scores, float tau, int32_t* block_idx,
                            int32_t* block_counts, void* stream);
 
+/* Workspace bytes dsv_pack_kv needs (0 if the problem is invalid). */
+size_t dsv_pack_kv_workspace_size(const dsv_problem* p);
+
+/*
+ * dsv_pack_kv -- the one-GPU share of sequence-sharded context parallelism ([de] §2.C,
+ * [es] §2.C: shard long sequences over GPUs and move only the KV that the sparsity needs).
+ * For the receiver's query blocks [qb_begin, qb_end): per (b, h) the union of the KV blocks
+ * their lists select (block_counts as in dsv_sparse_attn_fwd; out-of-range entries ignored),
+ * ascending, and its K and V rows copied contiguously:
+ *   packed_blocks [B, H, N/Bk] int32  the union ascending, then -1 padding
+ *   packed_counts [B, H] int32        its size U
+ *   k_packed, v_packed [B, H, N, d]   rows [u*Bk, (u+1)*Bk) hold block packed_blocks[u] of
+ *                                     k, v for u < U (later rows are not written)
+ *   packed_idx [B, H, qb_end - qb_begin, k] int32  the shard's lists rewritten to positions in
+ *                                     the union (-1 past a row's count or for an ignored entry)
+ * The receiver's forward is dsv_sparse_attn_fwd on (its Q rows, k_packed, v_packed,
+ * packed_idx), which equals the forward over the original k, v for those rows.  Bk must be 64.
+ */
+dsv_status dsv_pack_kv(const dsv_problem* p, const void* k, const void* v, const int32_t* block_idx,
+                       const int32_t* block_counts, int32_t qb_begin, int32_t qb_end, void* k_packed,
+                       void* v_packed, int32_t* packed_blocks, int32_t* packed_counts, int32_t* packed_idx,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes dsv_sparse_attn_fwd needs (0 if none is needed or the problem is
    invalid; with 0, `workspace` may be NULL). */
 size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);

@@ -147,3 +147,14 @@ def test_representative_predictor_validates_the_row(lib):
         assert lib.dsv_predict_representative(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, rep, FAKE, 1 << 40, FAKE,
                                               None) == 1
         assert "rep_row" in lib.dsv_last_error().decode()
+
+
+def test_pack_validates_range_and_workspace(lib):
+    p = _prob(topk=4)
+    nb = lib.dsv_pack_kv_workspace_size(ctypes.byref(p))
+    assert nb >= 2 * 2 * 16 * 4
+    args = lambda b, e, ws: (ctypes.byref(p), FAKE, FAKE, FAKE, None, b, e, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    for b, e in ((-1, 2), (3, 2), (0, 17)):
+        assert lib.dsv_pack_kv(*args(b, e, nb)) == 1
+        assert "qb_begin" in lib.dsv_last_error().decode()
+    assert lib.dsv_pack_kv(*args(0, 4, nb - 1)) == 3
