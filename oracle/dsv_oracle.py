@@ -246,6 +246,27 @@ def mass_margin(scores: np.ndarray, tau: float) -> np.ndarray:
     return out.reshape(scores.shape[:-1])
 
 
+def block_recall(q, k, idx, bq: int, bk: int, sm_scale: float) -> np.ndarray:
+    """True attention mass captured by the selected blocks ([de] §2.A: the critical KV carry most of
+    the score; the profiler's question is how much): per query block, the mean over its rows of
+    sum_{j selected} softmax(sm_scale q_i K^T)_j, with the softmax over ALL keys.
+    q, k [B, H, N, d]; idx [B, H, nqb, k] (negative entries select nothing) -> [B, H, nqb]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    b_, h_, n, _ = q.shape
+    nqb = n // bq
+    out = np.zeros((b_, h_, nqb))
+    for b in range(b_):
+        for h in range(h_):
+            for qb in range(nqb):
+                s = sm_scale * (q[b, h, qb * bq:(qb + 1) * bq] @ k[b, h].T)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                keys = selected_keys(idx[b, h, qb], bk)
+                out[b, h, qb] = p[:, keys].sum(axis=1).mean()
+    return out
+
+
 def pack_selected(idx: np.ndarray, counts: Optional[np.ndarray], qb_begin: int, qb_end: int, nkb: int):
     """Sequence-parallel send list ([de] §2.C, [es] §2.C: context parallelism that moves only the
     KV the selection needs): per (b, h) the union of the KV blocks selected by query blocks

@@ -468,3 +468,27 @@ def test_packing_moves_exactly_the_union_and_attention_is_unchanged():
     o_ref, l_ref = O.sparse_attn_fwd(q[:, :, rows], kk, v, shard_idx, bq, bk, 0.3)
     o_p, l_p = O.sparse_attn_fwd(q[:, :, rows], kp, vp, remapped, bq, bk, 0.3)
     assert np.array_equal(o_ref, o_p) and np.array_equal(l_ref, l_p)
+
+
+# ------------------------------------------------------------------ recall of a selection
+
+
+def test_block_recall_special_cases_and_identity_predictor():
+    rng = np.random.default_rng(21)
+    n, d, bq, bk = 256, 8, 64, 32
+    q, k = (rng.standard_normal((1, 1, n, d)) for _ in range(2))
+    nqb, nkb = n // bq, n // bk
+    everything = np.tile(np.arange(nkb, dtype=np.int32), (1, 1, nqb, 1))
+    np.testing.assert_allclose(O.block_recall(q, k, everything, bq, bk, 0.4), 1.0, rtol=1e-14)
+    # one block: the true block mass from the identity predictor (r = d, W = I), per row
+    true_mass = O.block_scores_head(q[0, 0], k[0, 0], bq, bk, 0.4)  # sums over the Bq rows
+    for kb in (0, 5):
+        one = np.full((1, 1, nqb, 1), kb, np.int32)
+        np.testing.assert_allclose(O.block_recall(q, k, one, bq, bk, 0.4)[0, 0], true_mass[:, kb] / bq, rtol=1e-12)
+    # additivity over disjoint lists, and nothing selected gives 0
+    a = np.tile(np.array([1, 6], np.int32), (1, 1, nqb, 1))
+    b = np.tile(np.array([0, 3], np.int32), (1, 1, nqb, 1))
+    both = np.concatenate([a, b], axis=-1)
+    np.testing.assert_allclose(O.block_recall(q, k, both, bq, bk, 0.4),
+                               O.block_recall(q, k, a, bq, bk, 0.4) + O.block_recall(q, k, b, bq, bk, 0.4), rtol=1e-12)
+    assert np.all(O.block_recall(q, k, np.full((1, 1, nqb, 1), -1, np.int32), bq, bk, 0.4) == 0)
