@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="C5")
+    ap.add_argument("--generator", choices=("g1", "g2"), default=None,
+                    help="override the config's input generator (g2: smooth Q field and 3D-cube token order)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense (k = N/Bk) comparator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
@@ -131,7 +133,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path; "
-              "the sharding design is described in DESIGN.md", file=sys.stderr)
+              "the sharding design is documented with the library", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -143,6 +145,8 @@ def main():
         sys.exit(1)
     dsv.load_library()
     cfg = get_config(a.config)
+    if a.generator:
+        cfg = cfg.with_(generator=a.generator)
     dev = torch.device("cuda:0")
     log(f"[bench] {cfg.name}: B={cfg.batch} H={cfg.heads} N={cfg.seq_len} d={cfg.head_dim} r={cfg.rank} "
         f"Bq={cfg.q_block} Bk={cfg.kv_block} k={cfg.topk}/{cfg.nkb}; generating inputs")
@@ -251,6 +255,7 @@ def main():
         _, wsf_d, wsb_d = dsv.workspace_sizes(t["q"], topk=cfg.nkb, rank=cfg.rank, **kw)
         wsb2 = torch.empty(wsb_d, dtype=torch.uint8, device=dev)
         del wsb
+        lse_sel = lse.clone()  # the top-k step's lse, for the recall of its selection
         dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_d, workspace=wsf, residual=True, out=(o, lse, o_lo), **kw)
         torch.cuda.synchronize()
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
@@ -263,9 +268,16 @@ def main():
         e2.synchronize()
         dfwd, dbwd = e0.elapsed_time(e1), e1.elapsed_time(e2)
         dense_flops = 3.5 * 4.0 * B * H * N * N * D
+        # the dense forward's lse (every block selected) gives the true mass the top-k lists capture
+        dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_d, workspace=wsf, residual=True, out=(o, lse, o_lo), **kw)
+        rec = dsv.block_recall(lse_sel, lse, q_block=cfg.q_block).double()
+        torch.cuda.synchronize()
         dense = {"fwd_ms": dfwd, "bwd_ms": dbwd, "tflops": dense_flops / ((dfwd + dbwd) * 1e-3) / 1e12,
-                 "speedup_attn": (dfwd + dbwd) / attn_ms, "ideal_speedup": cfg.nkb / cfg.topk}
-        log(f"[bench] dense fwd {dfwd:.1f} ms bwd {dbwd:.1f} ms")
+                 "speedup_attn": (dfwd + dbwd) / attn_ms, "ideal_speedup": cfg.nkb / cfg.topk,
+                 "recall_mean": float(rec.mean()), "recall_p05": float(torch.quantile(rec.flatten()[:1 << 24], 0.05)),
+                 "recall_min": float(rec.min())}
+        log(f"[bench] dense fwd {dfwd:.1f} ms bwd {dbwd:.1f} ms; top-k recall mean {dense['recall_mean']:.4f} "
+            f"p05 {dense['recall_p05']:.4f} min {dense['recall_min']:.4f}")
 
     mass = None
     if not a.no_mass:

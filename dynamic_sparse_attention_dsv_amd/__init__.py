@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   select_mass(block_scores, tau, kmax) -> (block_idx [B, H, N/Bq, kmax] padded with -1, block_counts)
   sparse_attn_fwd(q, k, v, idx, ...)  -> (o, lse), or (o, lse, o_lo) with residual=True
   sparse_attn_bwd(q, k, v, o, do, lse, idx, ..., o_lo=None) -> (dq, dk, dv)
+  block_recall(lse_selected, lse_all, q_block) -> recall [B, H, N/Bq] (true mass captured)
   pack_kv(k, v, idx, qb_begin, qb_end, ...) -> (k_packed, v_packed, packed_blocks, packed_counts, packed_idx)
 """
 from __future__ import annotations
@@ -30,7 +31,7 @@ STATUS = {0: "DSV_OK", 1: "DSV_ERR_INVALID_ARGUMENT", 2: "DSV_ERR_UNSUPPORTED", 
           4: "DSV_ERR_HIP"}
 
 EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_predict_representative", "dsv_select_topk",
-            "dsv_select_mass", "dsv_pack_kv_workspace_size", "dsv_pack_kv",
+            "dsv_select_mass", "dsv_block_recall", "dsv_pack_kv_workspace_size", "dsv_pack_kv",
             "dsv_sparse_attn_fwd_workspace_size",
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd_workspace_size", "dsv_sparse_attn_bwd", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_timing_begin", "dsv_timing_end")
@@ -74,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsv_predict_representative": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, V, S, V, V]),
         "dsv_select_topk": (ctypes.c_int, [P, V, V, V]),
         "dsv_select_mass": (ctypes.c_int, [P, V, ctypes.c_float, V, V, V]),
+        "dsv_block_recall": (ctypes.c_int, [P, V, V, V, V]),
         "dsv_pack_kv_workspace_size": (S, [P]),
         "dsv_pack_kv": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, ctypes.c_int32, V, V, V, V, V, V, S, V]),
         "dsv_sparse_attn_fwd_workspace_size": (S, [P]),
@@ -303,6 +305,23 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block:
                                    _p(block_idx), _p(block_counts), _p(dq), _p(dk), _p(dv), _p(ws),
                                    ws.numel() * ws.element_size(), _stream(dev)), "dsv_sparse_attn_bwd")
     return dq, dk, dv
+
+
+def block_recall(lse_selected: torch.Tensor, lse_all: torch.Tensor, *, q_block: int,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Mean over each query block's rows of exp(lse_selected - lse_all): the true attention mass
+    the selection captures (lse_all from the forward with every block selected)."""
+    lib = load_library()
+    dev = _dev(lse_selected, lse_all)
+    _contig(lse_selected, lse_all)
+    if lse_selected.shape != lse_all.shape or lse_selected.dim() != 3 or lse_selected.dtype != torch.float32:
+        raise ValueError("lse tensors must be float32 [B, H, N] of one shape")
+    b, h, n = lse_selected.shape
+    prob = Problem(b, h, n, 64, q_block, q_block, 1, 1, DSV_F32, 0.0, 0.0)
+    rec = out if out is not None else torch.empty((b, h, n // q_block), dtype=torch.float32, device=dev)
+    _check(lib.dsv_block_recall(ctypes.byref(prob), _p(lse_selected), _p(lse_all), _p(rec), _stream(dev)),
+           "dsv_block_recall")
+    return rec
 
 
 def pack_kv(k, v, block_idx, qb_begin: int, qb_end: int, *, q_block: int, kv_block: int = 64,

@@ -339,6 +339,19 @@ dsv_status dsv_select_mass(const dsv_problem* p, const float* block_scores, floa
   return DSV_OK;
 }
 
+dsv_status dsv_block_recall(const dsv_problem* p, const float* lse_selected, const float* lse_all, float* recall,
+                            void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, false));
+  TRY(check_ptr(lse_selected, "lse_selected", 4));
+  TRY(check_ptr(lse_all, "lse_all", 4));
+  TRY(check_ptr(recall, "recall", 4));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY_HIP(dsv::launch_block_recall(lse_selected, lse_all, recall, o.bh() * o.nqb(), o.bq, st), "block_recall_kernel");
+  return DSV_OK;
+}
+
 size_t dsv_pack_kv_workspace_size(const dsv_problem* p) {
   Prob o;
   if (to_prob(p, o, false) != DSV_OK) return 0;

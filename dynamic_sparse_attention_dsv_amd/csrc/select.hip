@@ -172,6 +172,32 @@ hipError_t launch_select_mass(const float* scores, int32_t* idx, int32_t* cnts, 
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------- recall of a selection
+//
+// The profiler's question ([de] §2.A: the critical KV carry most of the score): how much of a
+// row's true attention mass do its selected blocks capture?  With LSE_J the log-sum-exp of the
+// row's scaled logits over its selected keys (the sparse forward's lse) and LSE_all over all
+// keys (the forward with every block selected), the captured mass is exp(LSE_J - LSE_all).
+// One wave per query block averages it over the block's rows.
+__global__ __launch_bounds__(256) void block_recall_kernel(const float* __restrict__ lse_sel,
+                                                           const float* __restrict__ lse_all,
+                                                           float* __restrict__ recall, int rows, int bq) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // bh * nqb + qb
+  if (row >= rows) return;  // whole wave exits together
+  const size_t base = (size_t)row * bq;
+  float acc = 0.f;
+  for (int i = lane; i < bq; i += 64) acc += expf(lse_sel[base + i] - lse_all[base + i]);
+  acc = wave_sum(acc);
+  if (lane == 0) recall[row] = acc / (float)bq;
+}
+
+hipError_t launch_block_recall(const float* lse_sel, const float* lse_all, float* recall, int rows, int bq,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(block_recall_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, lse_sel, lse_all, recall, rows, bq);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_topk(const float* scores, int32_t* idx, int rows, int nkb, int k, hipStream_t st) {
   const dim3 grid((rows + 3) / 4), block(256);
   const int npl = (nkb + 63) / 64;

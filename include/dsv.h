@@ -177,6 +177,21 @@ dsv_status dsv_select_topk(const dsv_problem* p, const float* block_scores, int3
 dsv_status dsv_select_mass(const dsv_problem* p, const float* block_scores, float tau, int32_t* block_idx,
                            int32_t* block_counts, void* stream);
 
+/*
+ * dsv_block_recall -- sparsity profiler: the true attention mass a selection captures ([de]
+ * §2.A: the critical KV carry most of the attention score).  For query row i with selected
+ * keys J_i, the captured mass is sum_{j in J_i} softmax(s_i)_j over ALL keys
+ * = exp(LSE_J(i) - LSE_all(i)); recall[b, h, qb] is its mean over the rows of query block qb.
+ *
+ *   lse_selected  [B, H, N] float32: dsv_sparse_attn_fwd's lse for the selection
+ *   lse_all       [B, H, N] float32: dsv_sparse_attn_fwd's lse with every block selected
+ *                 (k = N/Bk, block_idx[qb] = 0 .. N/Bk - 1), same q, k and scale
+ *   recall        [B, H, N/Bq] float32 output, in [0, 1]
+ * Only problem.batch, heads, seq_len and q_block are used.
+ */
+dsv_status dsv_block_recall(const dsv_problem* p, const float* lse_selected, const float* lse_all, float* recall,
+                            void* stream);
+
 /* Workspace bytes dsv_pack_kv needs (0 if the problem is invalid). */
 size_t dsv_pack_kv_workspace_size(const dsv_problem* p);
 

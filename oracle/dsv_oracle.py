@@ -25,7 +25,7 @@ The path, in the pages' order:
   4. exact softmax attention restricted to the selected KV blocks, forward and
      backward, because the method trains with it ([es] §3; [de] §2.A, stage 2).
 
-Readings where the pages are silent (each is listed again in the design doc):
+Readings where the pages are silent, ambiguous or garbled:
   R1 the predictor acts on each head's Q and K: Q_lr = Q W^Q_lr, K_lr = K W^K_lr
      with W in R^{d x r};
   R2 predicted logits are pred_scale * <Q_lr_i, K_lr_j> (pred_scale defaults to

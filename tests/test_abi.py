@@ -158,3 +158,10 @@ def test_pack_validates_range_and_workspace(lib):
         assert lib.dsv_pack_kv(*args(b, e, nb)) == 1
         assert "qb_begin" in lib.dsv_last_error().decode()
     assert lib.dsv_pack_kv(*args(0, 4, nb - 1)) == 3
+
+
+def test_block_recall_validates_pointers(lib):
+    p = _prob()
+    assert lib.dsv_block_recall(ctypes.byref(p), FAKE, None, FAKE, None) == 1
+    assert "lse_all" in lib.dsv_last_error().decode()
+    assert lib.dsv_block_recall(None, FAKE, FAKE, FAKE, None) == 1
