@@ -249,7 +249,8 @@ def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_
     """Softmax attention over the selected KV blocks only -> (o [B,H,N,d], lse [B,H,N] float32).
 
     With ``residual=True`` (bf16 only) also returns o_lo, the bf16 rounding residual of O; handing it
-    to :func:`sparse_attn_bwd` makes the backward's D = rowsum(dO * O) accurate to fp32.
+    to :func:`sparse_attn_bwd` makes the backward's D = rowsum(dO * O) accurate.  This training
+    forward needs a workspace (an fp16 copy of V); the inference forward needs none.
     ``out`` may supply (o, lse) or (o, lse, o_lo).  ``block_counts`` ([B, H, N/Bq] int32, e.g. from
     :func:`select_mass`) limits each query block to the first entries of its list.
     """
@@ -264,7 +265,8 @@ def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_
         raise ValueError("block_idx must be [B, H, N/Bq, k]")
     if residual and q.dtype != torch.bfloat16:
         raise ValueError("the O residual exists for bf16 problems only")
-    ws = _workspace(int(lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(prob))), dev, workspace)
+    ws = _workspace(int(lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(prob))) if residual else 0, dev,
+                    workspace)
     o_lo = None
     if out is not None:
         o, lse = out[0], out[1]

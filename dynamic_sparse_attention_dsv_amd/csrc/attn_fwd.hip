@@ -19,19 +19,75 @@
 //    O^T += V^T P^T comes from transposing LDS reads (ds_read_b64_tr_b16);
 //  * S^T's D layout puts one query per lane, so the online-softmax row max and
 //    row sum are lane-local plus one exchange with lane ^ 32; K rows are loaded
-//    in the sigma order so that P^T feeds O^T += V^T P^T directly from registers.
+//    in the sigma order so that P^T feeds O^T += V^T P^T directly from registers;
+//  * the training forward (when the caller asks for O's rounding residual) takes
+//    P V in fp16: V is first copied to fp16 with a power-of-two per-head scale
+//    (exact for bf16 values), P is rounded to fp16 (2^-11 relative instead of
+//    bf16's 2^-8) -- one product, O accurate enough for the backward's D.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dsv {
 
-// SPLIT: P enters O += P V as two bf16 parts (hi + lo), carrying O to about 16 bits; chosen
-// when the caller asks for O's rounding residual, i.e. when a backward will use O.
-template <int D, int BQ, bool SPLIT>
+// ---------------------------------------------------------------- V to fp16 (training forward)
+//
+// Per head: the largest |V| (as float bits; |x| orders like its bits), in VMAX_PARTS partial
+// maxima per head, then V16 = fp16(V * 2^s) with s = f16_shift(max), exact for bf16 values
+// (8 significant bits) above 2^-28 of the maximum.  Deterministic, no atomics.
+constexpr int VMAX_PARTS = 32;
+
+__global__ __launch_bounds__(256) void vmax_part_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ part,
+                                                        size_t per_head /* elements, multiple of 8 */) {
+  __shared__ uint32_t red[4];
+  const int bh = blockIdx.y, ch = blockIdx.x;
+  const size_t chunk = (per_head / 8 + VMAX_PARTS - 1) / VMAX_PARTS;  // 16-byte units
+  const size_t u0 = ch * chunk, u1 = min(per_head / 8, u0 + chunk);
+  const uint16_t* src = v + (size_t)bh * per_head;
+  uint32_t m = 0;
+  for (size_t u = u0 + threadIdx.x; u < u1; u += 256) {
+    const u32x4 x = ld16(src + u * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = max(m, max((x[e] & 0x7fffu) << 16, x[e] & 0x7fff0000u));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[bh * VMAX_PARTS + ch] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// grid (ceil(per_head / 2048), BH): 8 elements per thread; block 0 of each head also writes the
+// head's shift for the forward
+__global__ __launch_bounds__(256) void v_to_f16_kernel(const uint16_t* __restrict__ v, const uint32_t* __restrict__ part,
+                                                       uint16_t* __restrict__ v16, int32_t* __restrict__ shift,
+                                                       size_t per_head) {
+  const int bh = blockIdx.y, lane = threadIdx.x & 63;
+  uint32_t m = lane < VMAX_PARTS ? part[bh * VMAX_PARTS + lane] : 0u;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  const int s = f16_shift(m);
+  if (blockIdx.x == 0 && threadIdx.x == 0) shift[bh] = s;
+  const size_t u = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= per_head / 8) return;
+  const u32x4 x = ld16(v + (size_t)bh * per_head + u * 8);
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[2 * e] = ldexpf(__uint_as_float(x[e] << 16), s);
+    y[2 * e + 1] = ldexpf(__uint_as_float(x[e] & 0xffff0000u), s);
+  }
+  const f16x8 h = cvt8h(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
+  st16(v16 + (size_t)bh * per_head + u * 8, __builtin_bit_cast(u32x4, h));
+}
+
+// PV16: the training forward.  v is then the fp16 copy of V scaled by 2^vshift[bh]; P enters
+// O += P V rounded to fp16, and the kernel also writes O's rounding residual o_lo.
+template <int D, int BQ, bool PV16>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ o,
-    float* __restrict__ lse, uint16_t* __restrict__ o_lo /* optional rounding residual of O */, int n, int topk, int nwg,
+    float* __restrict__ lse, uint16_t* __restrict__ o_lo /* rounding residual of O (PV16) */,
+    const int32_t* __restrict__ vshift /* PV16: per-head exponent of V's scale */, int n, int topk, int nwg,
     float c /* sm_scale * log2(e) */) {
   constexpr int WAVES = BQ / 32;
   constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
@@ -67,7 +123,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     uint16_t* orow = o + head + (size_t)qrow * D;
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) st16(orow + dc * 16 + g * 8, u32x4{0, 0, 0, 0});
-    if constexpr (SPLIT) {
+    if constexpr (PV16) {
       uint16_t* lrow = o_lo + head + (size_t)qrow * D;
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) st16(lrow + dc * 16 + g * 8, u32x4{0, 0, 0, 0});
@@ -140,42 +196,37 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
       }
     l_run += psum;
     // O^T += V^T P^T: V^T operands by transposed reads of the row-major V tile (rows cc*16..:
-    // bases + cc*16*D); P^T chunk cc = registers (cc%2)*8.. of tile cc/2.  With SPLIT, P enters
-    // as two bf16 parts: hi = P with its low 16 bits cleared (exact), lo = bf16(P - hi), so the
-    // product carries P to about 16 bits.  A single bf16 rounding of P puts errors of up to
-    // 2^-9 P into O -- fine for O itself, too coarse for the backward's D = rowsum(dO * O),
-    // which the dQ product multiplies by K.
+    // bases + cc*16*D); P^T chunk cc = registers (cc%2)*8.. of tile cc/2.  P <= 2^8 (lazy
+    // rescaling), so fp16 holds it; a bf16 rounding of P (2^-8 relative) would be fine for O
+    // itself but too coarse for the backward's D = rowsum(dO * O), which the dQ product
+    // multiplies by K -- the training forward therefore rounds P to fp16 against fp16 V.
     const int vb0 = opaque(tr_base<D>(0, lane, 0)), vb1 = opaque(tr_base<D>(0, lane, 1));
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const f32x16& st = s[cc >> 1];
       const int b0 = (cc & 1) * 8;
-      bf16x8 ph, pl;
-      if constexpr (SPLIT) {
-        float lo[8];
-        u32x4 hw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t u0 = __float_as_uint(st[b0 + 2 * e]) & 0xffff0000u;
-          const uint32_t u1 = __float_as_uint(st[b0 + 2 * e + 1]) & 0xffff0000u;
-          hw[e] = (u0 >> 16) | u1;
-          lo[2 * e] = st[b0 + 2 * e] - __uint_as_float(u0);
-          lo[2 * e + 1] = st[b0 + 2 * e + 1] - __uint_as_float(u1);
-        }
-        ph = as_bf16x8(hw);
-        pl = cvt8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
-      } else {
-        ph = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6], st[b0 + 7]);
-      }
       const int o0 = vb0 + cc * 16 * D, o1 = vb1 + cc * 16 * D;
       bf16x8 va = tr_frag_at<D>(Vc, o0, o1, 0);
+      if constexpr (PV16) {
+        const f16x8 ph = cvt8h(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
+                               st[b0 + 7]);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        bf16x8 vn = va;
-        if (dt + 1 < D / 32) vn = tr_frag_at<D>(Vc, o0, o1, dt + 1);
-        oacc[dt] = mfma32(va, ph, oacc[dt]);
-        if constexpr (SPLIT) oacc[dt] = mfma32(va, pl, oacc[dt]);
-        va = vn;
+        for (int dt = 0; dt < D / 32; ++dt) {
+          bf16x8 vn = va;
+          if (dt + 1 < D / 32) vn = tr_frag_at<D>(Vc, o0, o1, dt + 1);
+          oacc[dt] = mfma32h(as_f16x8(va), ph, oacc[dt]);
+          va = vn;
+        }
+      } else {
+        const bf16x8 ph = cvt8(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
+                               st[b0 + 7]);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          bf16x8 vn = va;
+          if (dt + 1 < D / 32) vn = tr_frag_at<D>(Vc, o0, o1, dt + 1);
+          oacc[dt] = mfma32(va, ph, oacc[dt]);
+          va = vn;
+        }
       }
     }
   };
@@ -219,8 +270,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
 
   const float l = l_run + xor32(l_run);
   const float inv = 1.f / l;
+  const int unscale = PV16 ? -vshift[bh] : 0;  // O was accumulated against V * 2^vshift
   uint16_t* orow = o + head + (size_t)qrow * D;
-  uint16_t* lrow = SPLIT ? o_lo + head + (size_t)qrow * D : nullptr;
+  uint16_t* lrow = PV16 ? o_lo + head + (size_t)qrow * D : nullptr;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -228,10 +280,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
       const int d0 = dt * 32 + vq * 8 + g * 4;
       float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = oacc[dt][vq * 4 + e] * inv;
+      for (int e = 0; e < 4; ++e) x[e] = PV16 ? ldexpf(oacc[dt][vq * 4 + e] * inv, unscale) : oacc[dt][vq * 4 + e] * inv;
       const u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
       *reinterpret_cast<u32x2*>(orow + d0) = pk;
-      if constexpr (SPLIT) {  // residual x - bf16(x), itself rounded to bf16
+      if constexpr (PV16) {  // residual x - bf16(x), itself rounded to bf16
         const u32x2 rk = {pack_bf16x2(x[0] - __uint_as_float(pk[0] << 16), x[1] - __uint_as_float(pk[0] & 0xffff0000u)),
                           pack_bf16x2(x[2] - __uint_as_float(pk[1] << 16), x[3] - __uint_as_float(pk[1] & 0xffff0000u))};
         *reinterpret_cast<u32x2*>(lrow + d0) = rk;
@@ -284,19 +336,38 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restric
 
 // ---------------------------------------------------------------- launchers
 
+size_t attn_fwd_bf16_ws_bytes(int bh, int n, int d) {
+  return align_ws((size_t)bh * n * d * 2) + align_ws((size_t)bh * VMAX_PARTS * 4) + align_ws((size_t)bh * 4);
+}
+
 hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                                const int32_t* cnts, uint16_t* o, float* lse, uint16_t* o_lo, int bh, int n, int d, int bq, int topk,
-                                float sm_scale, hipStream_t st) {
+                                const int32_t* cnts, uint16_t* o, float* lse, uint16_t* o_lo, void* ws, int bh, int n,
+                                int d, int bq, int topk, float sm_scale, hipStream_t st) {
   const int nwg = bh * (n / bq);
   const float c = sm_scale * kLog2e;
+  uint16_t* v16 = nullptr;
+  int32_t* vshift = nullptr;
+  if (o_lo) {  // training forward: V to fp16 first
+    const size_t per_head = (size_t)n * d;
+    char* w = static_cast<char*>(ws);
+    v16 = reinterpret_cast<uint16_t*>(w);
+    uint32_t* part = reinterpret_cast<uint32_t*>(w + align_ws((size_t)bh * per_head * 2));
+    vshift = reinterpret_cast<int32_t*>(w + align_ws((size_t)bh * per_head * 2) + align_ws((size_t)bh * VMAX_PARTS * 4));
+    hipLaunchKernelGGL(vmax_part_kernel, dim3(VMAX_PARTS, bh), dim3(256), 0, st, v, part, per_head);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(v_to_f16_kernel, dim3((unsigned)((per_head / 8 + 255) / 256), bh), dim3(256), 0, st, v, part,
+                       v16, vshift, per_head);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
 #define FWD(D_, BQ_)                                                                                      \
   if (d == D_ && bq == BQ_) {                                                                             \
     if (o_lo)                                                                                             \
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, true>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, idx, \
-                         cnts, o, lse, o_lo, n, topk, nwg, c);                                            \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, true>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v16, idx, \
+                         cnts, o, lse, o_lo, vshift, n, topk, nwg, c);                                    \
     else                                                                                                  \
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, false>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, \
-                         idx, cnts, o, lse, o_lo, n, topk, nwg, c);                                       \
+                         idx, cnts, o, lse, o_lo, vshift, n, topk, nwg, c);                               \
     return hipGetLastError();                                                                             \
   }
   FWD(64, 64) FWD(64, 128) FWD(128, 64) FWD(128, 128)

@@ -65,6 +65,26 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// fp16 operands: eight floats -> one fp16 MFMA operand (v_cvt_pk_f16_f32, round to nearest even)
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 cvt8h(float a0, float a1, float a2, float a3, float a4, float a5,
+                                       float a6, float a7) {
+  f32x8 f = {a0, a1, a2, a3, a4, a5, a6, a7};
+  return __builtin_convertvector(f, f16x8);
+}
+__device__ __forceinline__ f16x8 as_f16x8(bf16x8 x) { return __builtin_bit_cast(f16x8, x); }
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Power-of-two exponent s such that a maximum magnitude m (float bits, m >= 0) scaled by 2^s lies
+// in [2^14, 2^15): a tensor scaled by 2^s fits fp16's range (largest finite 65504) with its
+// elements' 8 significant bits kept exactly down to 2^-28 of the maximum.  0 for m = 0 or non-finite.
+__device__ __forceinline__ int f16_shift(uint32_t m) {
+  if (m == 0 || m >= 0x7f800000u) return 0;
+  return 14 - ((int)(m >> 23) - 127);
+}
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -207,6 +227,9 @@ __device__ __forceinline__ void lds_load_rows(const uint16_t* src, uint16_t* dst
   const int c = ((lane % (D / 8)) ^ swz<D>(row)) & (D / 8 - 1);
   __builtin_amdgcn_global_load_lds(src + (size_t)row * D + c * 8, dst + i * 512, 16, 0, 0);
 }
+
+// Workspace sub-buffers start on 256-byte boundaries.
+__host__ __device__ inline size_t align_ws(size_t x) { return (x + 255) / 256 * 256; }
 
 // Length of query-block row `row`'s block list: its count when per-row counts are given
 // (clamped to [0, k]), else k.

@@ -178,7 +178,10 @@ BwdWs bwd_ws(const Prob& o) {
   return w;
 }
 
-size_t fwd_ws_bytes(const Prob&) { return 0; }  // the forward needs no scratch
+// the bf16 training forward (o_lo requested) needs scratch; the inference forward and fp32 none
+size_t fwd_ws_bytes(const Prob& o) {
+  return o.dtype == DSV_BF16 ? dsv::attn_fwd_bf16_ws_bytes(o.bh(), o.n, o.d) : 0;
+}
 
 template <typename T>
 T* at(void* base, size_t off) {
@@ -410,7 +413,7 @@ dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* 
   TRY(check_ptr(o_ptr, "o"));
   TRY(check_ptr(lse, "lse"));
   TRY(check_residual(o, o_lo));
-  const size_t need = fwd_ws_bytes(o);
+  const size_t need = o_lo ? fwd_ws_bytes(o) : 0;
   if (need) {
     TRY(check_ptr(workspace, "workspace", kWsAlign));
     if (workspace_bytes < need)
@@ -420,8 +423,8 @@ dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* 
   if (o.dtype == DSV_BF16) {
     TRY_HIP(dsv::launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                       static_cast<const uint16_t*>(v), block_idx, block_counts,
-                                      static_cast<uint16_t*>(o_ptr), lse, static_cast<uint16_t*>(o_lo), o.bh(), o.n,
-                                      o.d, o.bq, o.k, o.sm, st),
+                                      static_cast<uint16_t*>(o_ptr), lse, static_cast<uint16_t*>(o_lo), workspace,
+                                      o.bh(), o.n, o.d, o.bq, o.k, o.sm, st),
             "attn_fwd_kernel");
   } else {
     TRY_HIP(dsv::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),

@@ -33,9 +33,12 @@ hipError_t launch_select_mass(const float* scores, int32_t* idx, int32_t* cnts, 
                               float tau, hipStream_t st);
 
 // forward (cnts: optional per-query-block list lengths, NULL = topk)
+// bytes of the training forward's scratch (fp16 copy of V, its per-head maxima and shifts)
+size_t attn_fwd_bf16_ws_bytes(int bh, int n, int d);
+// o_lo != nullptr selects the training forward, which needs ws of attn_fwd_bf16_ws_bytes bytes
 hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                                const int32_t* cnts, uint16_t* o, float* lse, uint16_t* o_lo, int bh, int n, int d,
-                                int bq, int topk, float sm_scale, hipStream_t st);
+                                const int32_t* cnts, uint16_t* o, float* lse, uint16_t* o_lo, void* ws, int bh, int n,
+                                int d, int bq, int topk, float sm_scale, hipStream_t st);
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* idx,
                                const int32_t* cnts, float* o, float* lse, int bh, int n, int d, int bq, int bk,
                                int topk, float sm_scale, hipStream_t st);

@@ -215,8 +215,9 @@ dsv_status dsv_pack_kv(const dsv_problem* p, const void* k, const void* v, const
                        void* v_packed, int32_t* packed_blocks, int32_t* packed_counts, int32_t* packed_idx,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes dsv_sparse_attn_fwd needs (0 if none is needed or the problem is
-   invalid; with 0, `workspace` may be NULL). */
+/* Workspace bytes dsv_sparse_attn_fwd needs when o_lo is requested (DSV_BF16: an fp16 copy
+   of V plus a few bytes per head); 0 for DSV_F32 or an invalid problem.  A forward without
+   o_lo needs no workspace (`workspace` may then be NULL). */
 size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);
 
 /*
@@ -238,15 +239,18 @@ size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);
  *               list gets O = 0 and lse = -inf.
  *   o           [B, H, N, d] output (dtype);  lse [B, H, N] float32 output
  *   o_lo        optional [B, H, N, d] bf16 output, or NULL.  DSV_BF16 only (must
- *               be NULL for DSV_F32).  When given, the forward computes P V
- *               with P split into two bf16 parts (O to about 16 bits, at the
- *               cost of extra matrix work) and writes the rounding residual
- *               bf16(O - o) here, so that o + o_lo carries O to ~16 bits.
- *               Passing it on to dsv_sparse_attn_bwd makes the backward's row
- *               term D = rowsum(dO o O) accurate instead of limited by bf16
+ *               be NULL for DSV_F32).  When given (the training forward), the
+ *               forward first copies V to fp16 with a power-of-two per-head
+ *               scale (exact for bf16 values) into the workspace, computes P V
+ *               with P rounded to fp16 (2^-11 relative, against bf16's 2^-8),
+ *               and writes the rounding residual bf16(O - o) here, so that
+ *               o + o_lo carries O to ~16 bits.  Passing it on to
+ *               dsv_sparse_attn_bwd makes the backward's row term
+ *               D = rowsum(dO o O) accurate instead of limited by bf16
  *               rounding, which otherwise dominates dQ's error.  Pass it for
  *               training; an inference forward leaves it NULL.
- *   workspace   >= dsv_sparse_attn_fwd_workspace_size(p) bytes (currently 0)
+ *   workspace   >= dsv_sparse_attn_fwd_workspace_size(p) bytes when o_lo is
+ *               given (256-byte aligned); ignored otherwise
  */
 dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
                                const int32_t* block_idx, const int32_t* block_counts, void* o, float* lse,

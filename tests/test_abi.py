@@ -111,7 +111,13 @@ def test_o_residual_is_bf16_only_and_aligned(lib):
 
 def test_workspace_sizes_and_short_workspace_is_rejected(lib):
     p = _prob()
-    assert lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(p)) == 0  # the forward needs no scratch
+    # bf16 training forward (o_lo given): an fp16 copy of V, B*H*N*d*2 bytes, plus per-head words
+    nf = lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(p))
+    assert nf >= 2 * 1024 * 64 * 2
+    assert lib.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, nf - 1,
+                                   None) == 3
+    assert "workspace" in lib.dsv_last_error().decode()
+    assert lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(_prob(dtype=dsv.DSV_F32))) == 0
     nb = lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(p))
     # bf16 backward: lse2 + D (2 x B*H*N floats), the block-order list, and the transposed block lists
     assert nb >= 2 * 2 * 1024 * 4 + 2 * 16 * 4 + 2 * 16 * 2 * 4

@@ -157,8 +157,9 @@ def test_c3_bf16_sampled_heads():
 
 
 def test_o_residual_and_backward_without_it():
-    # Asked for O's residual, the forward carries O to ~16 bits: o + o_lo is closer to the oracle's
-    # O than the plain forward's o.  The two forwards share the softmax statistics (lse is
+    # Asked for O's residual, the forward takes P V with P in fp16 (2^-11 relative instead of
+    # bf16's 2^-8) and returns o_lo: o + o_lo is at least 4x closer to the oracle's O than the
+    # plain forward's o.  The two forwards share the softmax statistics (lse is
     # identical), so the two backwards differ only through D = rowsum(dO * O):
     # dD_i = sum_c dO_ic ((o + o_lo) - o_plain)_ic.  dV does not depend on D, and since the sparse
     # softmax row P_i sums to 1, dQ moves by at most sm_scale * |dD_i| * max_{j selected} |K_jc|
