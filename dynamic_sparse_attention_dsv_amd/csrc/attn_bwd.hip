@@ -372,18 +372,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
   }
 }
 
-// ---------------------------------------------------------------- dQ (bf16, MFMA)
+// ---------------------------------------------------------------- dQ (bf16 inputs, MFMA)
 //
 // One workgroup per query block (Bq/32 waves, 32 rows each) walking its k
 // selected blocks: S^T = K Q^T and dP^T = V dO^T are recomputed, and
 // dQ^T += K^T dS^T takes K^T from transposing reads of the row-major K tile.
+//
+// S and dQ are fp16 products: K comes as an fp16 copy scaled by 2^sK (sK = f16_shift of the
+// head's max |K|; exact for bf16 values), Q is converted in registers with its own head shift sQ,
+// so S is the exact bf16 product scaled by 2^(sQ+sK).  dS is rounded to fp16 (2^-11 relative;
+// a bf16 rounding would let K's large entries amplify dS's error into dQ) after scaling row i by
+// 2^r_i, with r_i from the bound |dS_ij| = P_ij |dP_ij - D_i| <= 2 |dO_i|_1 max|V| (both dP_ij
+// and D_i are dO_i against a row of V or a convex mix of them), which keeps it inside fp16's
+// range at full precision.  dQ is unscaled exactly at the end.  dP stays a bf16 product.
 
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k16, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dvec,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ dq, int n, int topk,
-    int nwg, float c, float sm_scale) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ dq,
+    const uint32_t* __restrict__ absmax /* per head max |.| bits: [0,bh) K, [bh,2bh) Q, [2bh,3bh) V */, int bh_total,
+    int n, int topk, int nwg, float c, float sm_scale) {
   constexpr int WAVES = BQ / 32;
   constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
   // one array per buffer, so the compiler can see that the asynchronous copy into
@@ -406,18 +415,37 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
     for (int i = wave; i < NI; i += WAVES) {
       const bool isv = i >= NI / 2;
       const int ii = isv ? i - NI / 2 : i;
-      lds_load_rows<D>((isv ? v : k) + head + (size_t)blk * 64 * D, isv ? vd : kd, ii, lane);
+      lds_load_rows<D>((isv ? v : k16) + head + (size_t)blk * 64 * D, isv ? vd : kd, ii, lane);
     }
   };
+  const int sK = f16_shift(absmax[bh]), sQ = f16_shift(absmax[bh_total + bh]);
+  const float vmax = __uint_as_float(absmax[2 * bh_total + bh]);
 
-  bf16x8 qf[D / 16], of[D / 16];
+  f16x8 qf[D / 16];
+  bf16x8 of[D / 16];
+  float l1 = 0.f;  // |dO_i|_1 over this lane's half of the row
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) {
-    qf[dc] = as_bf16x8(ld16(q + head + (size_t)qrow * D + dc * 16 + g * 8));
-    of[dc] = as_bf16x8(ld16(dout + head + (size_t)qrow * D + dc * 16 + g * 8));
+    const u32x4 w = ld16(q + head + (size_t)qrow * D + dc * 16 + g * 8);
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = ldexpf(__uint_as_float(w[e] << 16), sQ);
+      f[2 * e + 1] = ldexpf(__uint_as_float(w[e] & 0xffff0000u), sQ);
+    }
+    qf[dc] = cvt8h(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+    const u32x4 od = ld16(dout + head + (size_t)qrow * D + dc * 16 + g * 8);
+    of[dc] = as_bf16x8(od);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l1 += fabsf(__uint_as_float(od[e] << 16)) + fabsf(__uint_as_float(od[e] & 0xffff0000u));
   }
+  l1 += xor32(l1);
+  // dS row scale 2^r (a normal float), r from the bound 2 |dO_i|_1 max|V| on |dS_ij|
+  const int r = min(max(f16_shift(__float_as_uint(2.f * l1 * vmax)), -120), 120);
+  const float dscale = ldexpf(1.f, r);
   const float my_lse2 = lse2[(size_t)bh * n + qrow];
-  const float my_d = dvec[(size_t)bh * n + qrow];
+  const float my_ds = dvec[(size_t)bh * n + qrow] * dscale;  // D_i 2^r
+  const float cs = ldexpf(c, -(sQ + sK));                     // S is scaled by 2^(sQ+sK)
 
   issue(blk_at(0), K0, V0);
   __syncthreads();
@@ -427,8 +455,6 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
   const int arow = sigma(c32);
   auto block = [&](const uint16_t* Kc, const uint16_t* Vc) {
     // one 32-key tile at a time: S^T, dP^T, dS^T, then its two 16-key chunks of dQ^T += K^T dS^T.
-    // dS is split into bf16 hi + lo parts: K's large entries would otherwise amplify dS's bf16
-    // rounding into dQ errors comparable to dQ's own bf16 storage rounding.
     // Fragment offsets come from one base per run (row_base / tr_base), recomputed per block,
     // and each k-step's operands are read one step ahead.
     const int rb = opaque(row_base<D>(arow, lane));
@@ -445,32 +471,29 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
           kn = row_frag_at<D>(Kc, rt, dc + 1);
           vn = row_frag_at<D>(Vc, rt, dc + 1);
         }
-        s = mfma32(ka, qf[dc], s);
+        s = mfma32h(as_f16x8(ka), qf[dc], s);
         dp = mfma32(va, of[dc], dp);
         ka = kn;
         va = vn;
       }
+      // dS 2^r = P (dP 2^r - D 2^r): the scaling is exact, folded into one fma
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        const float p = fast_exp2(fmaf(s[vv], c, -my_lse2));
-        dp[vv] = p * (dp[vv] - my_d);
+        const float p = fast_exp2(fmaf(s[vv], cs, -my_lse2));
+        dp[vv] = p * fmaf(dp[vv], dscale, -my_ds);
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int b0 = h2 * 8, cc = t * 2 + h2;
-        const bf16x8 hi = cvt8(dp[b0], dp[b0 + 1], dp[b0 + 2], dp[b0 + 3], dp[b0 + 4], dp[b0 + 5], dp[b0 + 6],
+        const f16x8 ds = cvt8h(dp[b0], dp[b0 + 1], dp[b0 + 2], dp[b0 + 3], dp[b0 + 4], dp[b0 + 5], dp[b0 + 6],
                                dp[b0 + 7]);
-        const bf16x8 lo = cvt8(dp[b0] - (float)hi[0], dp[b0 + 1] - (float)hi[1], dp[b0 + 2] - (float)hi[2],
-                               dp[b0 + 3] - (float)hi[3], dp[b0 + 4] - (float)hi[4], dp[b0 + 5] - (float)hi[5],
-                               dp[b0 + 6] - (float)hi[6], dp[b0 + 7] - (float)hi[7]);
         const int o0 = kb0 + cc * 16 * D, o1 = kb1 + cc * 16 * D;
         bf16x8 kt = tr_frag_at<D>(Kc, o0, o1, 0);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           bf16x8 ktn = kt;
           if (dt + 1 < D / 32) ktn = tr_frag_at<D>(Kc, o0, o1, dt + 1);
-          acc[dt] = mfma32(kt, hi, acc[dt]);
-          acc[dt] = mfma32(kt, lo, acc[dt]);
+          acc[dt] = mfma32h(as_f16x8(kt), ds, acc[dt]);
           kt = ktn;
         }
       }
@@ -493,8 +516,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
 #pragma unroll
     for (int vq = 0; vq < 4; ++vq) {
       const int d0 = dt * 32 + vq * 8 + g * 4;
-      u32x2 pk = {pack_bf16x2(acc[dt][vq * 4] * sm_scale, acc[dt][vq * 4 + 1] * sm_scale),
-                  pack_bf16x2(acc[dt][vq * 4 + 2] * sm_scale, acc[dt][vq * 4 + 3] * sm_scale)};
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = ldexpf(acc[dt][vq * 4 + e] * sm_scale, -(r + sK));  // exact unscale
+      u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
       *reinterpret_cast<u32x2*>(out + d0) = pk;
     }
 }
@@ -636,15 +661,31 @@ hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint
   return hipErrorInvalidValue;
 }
 
+size_t bwd_dq_bf16_ws_bytes(int bh, int n, int d) {
+  return align_ws((size_t)bh * n * d * 2) + head_absmax_ws_bytes(bh) + align_ws((size_t)bh * 3 * 4);
+}
+
 hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                               const float* lse2, const float* dvec, const int32_t* idx, const int32_t* cnts,
-                              uint16_t* dq, int bh, int n, int d, int bq, int topk, float sm_scale, hipStream_t st) {
+                              uint16_t* dq, void* ws, int bh, int n, int d, int bq, int topk, float sm_scale,
+                              hipStream_t st) {
   const int nwg = bh * (n / bq);
   const float c = sm_scale * kLog2e;
+  // fp16 copy of K and the per-head maxima of |K|, |Q|, |V|
+  const size_t per_head = (size_t)n * d;
+  char* w = static_cast<char*>(ws);
+  uint16_t* k16 = reinterpret_cast<uint16_t*>(w);
+  uint32_t* part = reinterpret_cast<uint32_t*>(w + align_ws((size_t)bh * per_head * 2));
+  uint32_t* absmax = reinterpret_cast<uint32_t*>(w + align_ws((size_t)bh * per_head * 2) + head_absmax_ws_bytes(bh));
+  hipError_t e = launch_head_absmax(k, part, absmax, bh, per_head, st);
+  if (e != hipSuccess) return e;
+  if ((e = launch_to_f16(k, absmax, k16, bh, per_head, st)) != hipSuccess) return e;
+  if ((e = launch_head_absmax(q, part, absmax + bh, bh, per_head, st)) != hipSuccess) return e;
+  if ((e = launch_head_absmax(v, part, absmax + 2 * bh, bh, per_head, st)) != hipSuccess) return e;
 #define DQ(D_, BQ_)                                                                                          \
   if (d == D_ && bq == BQ_) {                                                                                \
-    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, dout, lse2, \
-                       dvec, idx, cnts, dq, n, topk, nwg, c, sm_scale);                                      \
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k16, v, dout, lse2, \
+                       dvec, idx, cnts, dq, absmax, bh, n, topk, nwg, c, sm_scale);                          \
     return hipGetLastError();                                                                                \
   }
   DQ(64, 64) DQ(64, 128) DQ(128, 64) DQ(128, 128)

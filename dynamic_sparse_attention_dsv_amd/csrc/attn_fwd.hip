@@ -29,65 +29,14 @@
 
 namespace dsv {
 
-// ---------------------------------------------------------------- V to fp16 (training forward)
-//
-// Per head: the largest |V| (as float bits; |x| orders like its bits), in VMAX_PARTS partial
-// maxima per head, then V16 = fp16(V * 2^s) with s = f16_shift(max), exact for bf16 values
-// (8 significant bits) above 2^-28 of the maximum.  Deterministic, no atomics.
-constexpr int VMAX_PARTS = 32;
-
-__global__ __launch_bounds__(256) void vmax_part_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ part,
-                                                        size_t per_head /* elements, multiple of 8 */) {
-  __shared__ uint32_t red[4];
-  const int bh = blockIdx.y, ch = blockIdx.x;
-  const size_t chunk = (per_head / 8 + VMAX_PARTS - 1) / VMAX_PARTS;  // 16-byte units
-  const size_t u0 = ch * chunk, u1 = min(per_head / 8, u0 + chunk);
-  const uint16_t* src = v + (size_t)bh * per_head;
-  uint32_t m = 0;
-  for (size_t u = u0 + threadIdx.x; u < u1; u += 256) {
-    const u32x4 x = ld16(src + u * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m = max(m, max((x[e] & 0x7fffu) << 16, x[e] & 0x7fff0000u));
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) part[bh * VMAX_PARTS + ch] = max(max(red[0], red[1]), max(red[2], red[3]));
-}
-
-// grid (ceil(per_head / 2048), BH): 8 elements per thread; block 0 of each head also writes the
-// head's shift for the forward
-__global__ __launch_bounds__(256) void v_to_f16_kernel(const uint16_t* __restrict__ v, const uint32_t* __restrict__ part,
-                                                       uint16_t* __restrict__ v16, int32_t* __restrict__ shift,
-                                                       size_t per_head) {
-  const int bh = blockIdx.y, lane = threadIdx.x & 63;
-  uint32_t m = lane < VMAX_PARTS ? part[bh * VMAX_PARTS + lane] : 0u;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  const int s = f16_shift(m);
-  if (blockIdx.x == 0 && threadIdx.x == 0) shift[bh] = s;
-  const size_t u = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (u >= per_head / 8) return;
-  const u32x4 x = ld16(v + (size_t)bh * per_head + u * 8);
-  float y[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    y[2 * e] = ldexpf(__uint_as_float(x[e] << 16), s);
-    y[2 * e + 1] = ldexpf(__uint_as_float(x[e] & 0xffff0000u), s);
-  }
-  const f16x8 h = cvt8h(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
-  st16(v16 + (size_t)bh * per_head + u * 8, __builtin_bit_cast(u32x4, h));
-}
-
-// PV16: the training forward.  v is then the fp16 copy of V scaled by 2^vshift[bh]; P enters
-// O += P V rounded to fp16, and the kernel also writes O's rounding residual o_lo.
+// PV16: the training forward.  v is then the fp16 copy of V scaled by 2^f16_shift(vmax[bh]);
+// P enters O += P V rounded to fp16, and the kernel also writes O's rounding residual o_lo.
 template <int D, int BQ, bool PV16>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ o,
     float* __restrict__ lse, uint16_t* __restrict__ o_lo /* rounding residual of O (PV16) */,
-    const int32_t* __restrict__ vshift /* PV16: per-head exponent of V's scale */, int n, int topk, int nwg,
+    const uint32_t* __restrict__ vmax /* PV16: per-head max |V| (float bits) */, int n, int topk, int nwg,
     float c /* sm_scale * log2(e) */) {
   constexpr int WAVES = BQ / 32;
   constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
@@ -270,7 +219,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
 
   const float l = l_run + xor32(l_run);
   const float inv = 1.f / l;
-  const int unscale = PV16 ? -vshift[bh] : 0;  // O was accumulated against V * 2^vshift
+  const int unscale = PV16 ? -f16_shift(vmax[bh]) : 0;  // O was accumulated against the scaled V
   uint16_t* orow = o + head + (size_t)qrow * D;
   uint16_t* lrow = PV16 ? o_lo + head + (size_t)qrow * D : nullptr;
 #pragma unroll
@@ -337,7 +286,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restric
 // ---------------------------------------------------------------- launchers
 
 size_t attn_fwd_bf16_ws_bytes(int bh, int n, int d) {
-  return align_ws((size_t)bh * n * d * 2) + align_ws((size_t)bh * VMAX_PARTS * 4) + align_ws((size_t)bh * 4);
+  return align_ws((size_t)bh * n * d * 2) + head_absmax_ws_bytes(bh) + align_ws((size_t)bh * 4);
 }
 
 hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
@@ -346,28 +295,25 @@ hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint
   const int nwg = bh * (n / bq);
   const float c = sm_scale * kLog2e;
   uint16_t* v16 = nullptr;
-  int32_t* vshift = nullptr;
+  uint32_t* vmax = nullptr;
   if (o_lo) {  // training forward: V to fp16 first
     const size_t per_head = (size_t)n * d;
     char* w = static_cast<char*>(ws);
     v16 = reinterpret_cast<uint16_t*>(w);
     uint32_t* part = reinterpret_cast<uint32_t*>(w + align_ws((size_t)bh * per_head * 2));
-    vshift = reinterpret_cast<int32_t*>(w + align_ws((size_t)bh * per_head * 2) + align_ws((size_t)bh * VMAX_PARTS * 4));
-    hipLaunchKernelGGL(vmax_part_kernel, dim3(VMAX_PARTS, bh), dim3(256), 0, st, v, part, per_head);
-    hipError_t e = hipGetLastError();
+    vmax = reinterpret_cast<uint32_t*>(w + align_ws((size_t)bh * per_head * 2) + head_absmax_ws_bytes(bh));
+    hipError_t e = launch_head_absmax(v, part, vmax, bh, per_head, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(v_to_f16_kernel, dim3((unsigned)((per_head / 8 + 255) / 256), bh), dim3(256), 0, st, v, part,
-                       v16, vshift, per_head);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_to_f16(v, vmax, v16, bh, per_head, st)) != hipSuccess) return e;
   }
 #define FWD(D_, BQ_)                                                                                      \
   if (d == D_ && bq == BQ_) {                                                                             \
     if (o_lo)                                                                                             \
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, true>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v16, idx, \
-                         cnts, o, lse, o_lo, vshift, n, topk, nwg, c);                                    \
+                         cnts, o, lse, o_lo, vmax, n, topk, nwg, c);                                      \
     else                                                                                                  \
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, false>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, \
-                         idx, cnts, o, lse, o_lo, vshift, n, topk, nwg, c);                               \
+                         idx, cnts, o, lse, o_lo, vmax, n, topk, nwg, c);                                 \
     return hipGetLastError();                                                                             \
   }
   FWD(64, 64) FWD(64, 128) FWD(128, 64) FWD(128, 128)

@@ -158,7 +158,7 @@ PredictWs predict_ws(const Prob& o) {
 }
 
 struct BwdWs {
-  size_t dvec, lse2, bitmap, counts, col_ptr, rows, order, total;
+  size_t dvec, lse2, bitmap, counts, col_ptr, rows, order, dq16, total;
 };
 BwdWs bwd_ws(const Prob& o) {
   BwdWs w{};
@@ -167,6 +167,7 @@ BwdWs bwd_ws(const Prob& o) {
   if (o.dtype == DSV_BF16) {
     w.lse2 = off; off += rowf;
     w.order = off; off += align_up((size_t)o.bh() * o.nkb() * 4);
+    w.dq16 = off; off += align_up(dsv::bwd_dq_bf16_ws_bytes(o.bh(), o.n, o.d));
   }
   w.dvec = off; off += rowf;
   const int words = (o.nqb() + 31) / 32;
@@ -455,6 +456,9 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
   for (int i = 0; i < 9; ++i) TRY(check_ptr(ptrs[i], names[i]));
   TRY(check_ptr(block_idx, "block_idx", 4));
   if (block_counts) TRY(check_ptr(block_counts, "block_counts", 4));
+  // the dQ kernel's fp16 products scale S by up to 2^+-80 and fold the inverse into sm_scale
+  if (o.dtype == DSV_BF16 && !(o.sm >= 0x1p-40f && o.sm <= 0x1p40f))
+    return fail(DSV_ERR_UNSUPPORTED, "the bf16 backward needs sm_scale in [2^-40, 2^40]");
   TRY(check_residual(o, o_lo));
   TRY(check_ptr(workspace, "workspace", kWsAlign));
   const BwdWs w = bwd_ws(o);
@@ -479,7 +483,8 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
                                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), o.bh(), o.n, o.d, o.bq,
                                       o.k, o.sm, st), "attn_bwd_dkdv_kernel");
     TRY_HIP(dsv::launch_bwd_dq_bf16(q16, k16, v16, do16, lse2, dvec, block_idx, block_counts,
-                                    static_cast<uint16_t*>(dq), o.bh(), o.n, o.d, o.bq, o.k, o.sm, st),
+                                    static_cast<uint16_t*>(dq), at<void>(workspace, w.dq16), o.bh(), o.n, o.d, o.bq,
+                                    o.k, o.sm, st),
             "attn_bwd_dq_kernel");
   } else {
     TRY_HIP(dsv::launch_bwd_pre_f32(static_cast<const float*>(o_ptr), static_cast<const float*>(dout), dvec,

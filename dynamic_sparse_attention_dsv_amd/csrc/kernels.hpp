@@ -33,6 +33,13 @@ hipError_t launch_select_mass(const float* scores, int32_t* idx, int32_t* cnts, 
                               float tau, hipStream_t st);
 
 // forward (cnts: optional per-query-block list lengths, NULL = topk)
+// per-head max |x| of a bf16 tensor [bh, per_head] (float bits), via kAbsmaxParts partials in
+// `part` (head_absmax_ws_bytes(bh) bytes); y = fp16(x * 2^f16_shift(max)) per head
+size_t head_absmax_ws_bytes(int bh);
+hipError_t launch_head_absmax(const uint16_t* x, uint32_t* part, uint32_t* maxbits, int bh, size_t per_head,
+                              hipStream_t st);
+hipError_t launch_to_f16(const uint16_t* x, const uint32_t* maxbits, uint16_t* y, int bh, size_t per_head,
+                         hipStream_t st);
 // bytes of the training forward's scratch (fp16 copy of V, its per-head maxima and shifts)
 size_t attn_fwd_bf16_ws_bytes(int bh, int n, int d);
 // o_lo != nullptr selects the training forward, which needs ws of attn_fwd_bf16_ws_bytes bytes
@@ -53,9 +60,12 @@ hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint
                                 const float* lse2, const float* dvec, const int32_t* col_ptr, const int32_t* rows,
                                 const int32_t* order, uint16_t* dk, uint16_t* dv, int bh, int n, int d, int bq,
                                 int topk, float sm_scale, hipStream_t st);
+// the dQ kernel's scratch: an fp16 copy of K and per-head maxima (bwd_dq_bf16_ws_bytes bytes)
+size_t bwd_dq_bf16_ws_bytes(int bh, int n, int d);
 hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                               const float* lse2, const float* dvec, const int32_t* idx, const int32_t* cnts,
-                              uint16_t* dq, int bh, int n, int d, int bq, int topk, float sm_scale, hipStream_t st);
+                              uint16_t* dq, void* ws, int bh, int n, int d, int bq, int topk, float sm_scale,
+                              hipStream_t st);
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dout, const float* lse,
                           const float* dvec, const int32_t* idx, const int32_t* cnts, const int32_t* col_ptr,
                           const int32_t* rows, float* dq, float* dk, float* dv, int bh, int n, int d, int bq, int bk,

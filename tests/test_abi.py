@@ -171,3 +171,12 @@ def test_block_recall_validates_pointers(lib):
     assert lib.dsv_block_recall(ctypes.byref(p), FAKE, None, FAKE, None) == 1
     assert "lse_all" in lib.dsv_last_error().decode()
     assert lib.dsv_block_recall(None, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_bf16_backward_rejects_extreme_softmax_scales(lib):
+    for sc in (2.0 ** 50, 2.0 ** -50):
+        p = _prob(sm_scale=sc)
+        nb = lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(p))
+        st = lib.dsv_sparse_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                     FAKE, FAKE, nb, None)
+        assert st == 2 and "sm_scale" in lib.dsv_last_error().decode()
