@@ -441,7 +441,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
   }
   l1 += xor32(l1);
   // dS row scale 2^r (a normal float), r from the bound 2 |dO_i|_1 max|V| on |dS_ij|
-  const int r = min(max(f16_shift(__float_as_uint(2.f * l1 * vmax)), -120), 120);
+  const int r = min(max(f16_exponent(__float_as_uint(2.f * l1 * vmax)), -120), 120);
   const float dscale = ldexpf(1.f, r);
   const float my_lse2 = lse2[(size_t)bh * n + qrow];
   const float my_ds = dvec[(size_t)bh * n + qrow] * dscale;  // D_i 2^r

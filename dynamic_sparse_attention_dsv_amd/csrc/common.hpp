@@ -78,15 +78,17 @@ __device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
 }
 
 // Power-of-two exponent s such that a maximum magnitude m (float bits, m >= 0) scaled by 2^s lies
-// in [2^14, 2^15): a tensor scaled by 2^s fits fp16's range (largest finite 65504) with its
-// elements' 8 significant bits kept exactly down to 2^-28 of the maximum.  0 for m = 0 or
-// non-finite; capped to [-40, 40] (maxima in [2^-26, 2^54] reach the target range; outside it a
-// larger maximum would overflow fp16 and a smaller one keeps fewer exact bits).
-constexpr int kAbsmaxParts = 32;  // partial maxima per head
-__device__ __forceinline__ int f16_shift(uint32_t m) {
+// in [2^14, 2^15): values scaled by 2^s fit fp16's range (largest finite 65504), and a bf16 value
+// down to 2^-28 of the maximum stays exact.  0 for m = 0 or non-finite.
+__device__ __forceinline__ int f16_exponent(uint32_t m) {
   if (m == 0 || m >= 0x7f800000u) return 0;
-  return min(max(14 - ((int)(m >> 23) - 127), -40), 40);
+  return 14 - ((int)(m >> 23) - 127);
 }
+// The same for the per-head fp16 copies of tensors, capped to [-40, 40] so that the products of
+// two scaled copies and the inverse scales folded into softmax constants stay normal floats
+// (maxima in [2^-26, 2^54] reach the target range; a larger one would overflow fp16).
+constexpr int kAbsmaxParts = 32;  // partial maxima per head
+__device__ __forceinline__ int f16_shift(uint32_t m) { return min(max(f16_exponent(m), -40), 40); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
