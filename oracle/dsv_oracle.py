@@ -48,7 +48,13 @@ Readings where the pages are silent, ambiguous or garbled:
      scores sum to at least tau times the row's total score; capped at kmax blocks,
      never empty.  Lists are ascending and padded with -1 to kmax; a negative entry
      of any block list means "no block", and a query block whose list is empty has
-     O = 0, LSE = -inf and no gradient.
+     O = 0, LSE = -inf and no gradient;
+  R10 per-block activation of sparse attention (the pages switch a block to sparse
+     attention once it is sparse enough, [de] §2.A, stage 2; [es] §2.A): the measure
+     is a head's selected density, the selected KV blocks summed over its query
+     blocks divided by (query blocks x KV blocks); the head is flagged dense when
+     that sum exceeds floor(dense_above * query blocks * KV blocks), an integer
+     comparison.
 """
 from __future__ import annotations
 
@@ -244,6 +250,21 @@ def mass_margin(scores: np.ndarray, tau: float) -> np.ndarray:
         below = t - c[m - 2] if m >= 2 else np.inf
         out[i] = min(above, below)
     return out.reshape(scores.shape[:-1])
+
+
+def head_density(counts: Optional[np.ndarray], k: int, nqb: int, nkb: int, dense_above: float):
+    """Selected density of each head and its dense flag (R10).
+
+    counts [B, H, nqb] list lengths (clamped to [0, k]) or None (every list holds k blocks).
+    Returns (density [B, H] float64, dense [B, H] bool)."""
+    if counts is None:
+        raise ValueError("pass counts, or use np.full((B, H, nqb), k)")
+    c = np.clip(np.asarray(counts, np.int64), 0, k)
+    total = c.sum(axis=-1)                     # exact integer sums
+    cells = nqb * nkb
+    density = total / cells
+    limit = math.floor(dense_above * cells)    # dense_above * cells in float64, then floor
+    return density, total > limit
 
 
 def block_recall(q, k, idx, bq: int, bk: int, sm_scale: float) -> np.ndarray:

@@ -492,3 +492,18 @@ def test_block_recall_special_cases_and_identity_predictor():
     np.testing.assert_allclose(O.block_recall(q, k, both, bq, bk, 0.4),
                                O.block_recall(q, k, a, bq, bk, 0.4) + O.block_recall(q, k, b, bq, bk, 0.4), rtol=1e-12)
     assert np.all(O.block_recall(q, k, np.full((1, 1, nqb, 1), -1, np.int32), bq, bk, 0.4) == 0)
+
+
+def test_head_density_worked_example():
+    # R10 by hand: lists of lengths 1, 2, 3, 4 (clamped to k = 3) over 4 query blocks x 8 KV blocks
+    counts = np.array([[[1, 2, 3, 4], [-5, 0, 0, 3]]])
+    dens, dense = O.head_density(counts, 3, 4, 8, 0.28)
+    assert dens[0, 0] == 9 / 32 and dens[0, 1] == 3 / 32
+    assert bool(dense[0, 0]) and not bool(dense[0, 1])          # 9 > floor(8.96) = 8;  3 <= 8
+    _, dense = O.head_density(counts, 3, 4, 8, 0.3)
+    assert not bool(dense[0, 0])                                # 9 > floor(9.6) = 9 is false
+    # full lists: density k / nkb; never dense above 1, always dense below k / nkb
+    full = np.full((2, 3, 16), 5)
+    dens, dense = O.head_density(full, 5, 16, 40, 1.0)
+    assert np.all(dens == 5 / 40) and not dense.any()
+    assert O.head_density(full, 5, 16, 40, 0.1)[1].all()
