@@ -304,8 +304,13 @@ def main():
         ms = [evm[j].elapsed_time(evm[j + 1]) for j in range(3)]
         pairs_m = int(cnt_m.sum().item())
         flops_m = 14.0 * pairs_m * cfg.q_block * cfg.kv_block * cfg.head_dim
+        # per-head activation: selected density, and heads whose density exceeds one half
+        dens, dflag = dsv.head_density(cnt_m, topk=kmax, seq_len=N, q_block=cfg.q_block, kv_block=cfg.kv_block,
+                                       dense_above=0.5)
         mass = {"tau": a.mass_tau, "kmax": kmax, "mean_count": pairs_m / (B * H * cfg.nqb),
                 "min_count": int(cnt_m.min().item()), "max_count": int(cnt_m.max().item()),
+                "head_density_min": float(dens.min()), "head_density_max": float(dens.max()),
+                "heads_dense_above_half": int(dflag.sum()),
                 "select_ms": ms[0], "fwd_ms": ms[1], "bwd_ms": ms[2],
                 "attn_tflops": flops_m / ((ms[1] + ms[2]) * 1e-3) / 1e12}
         log(f"[bench] mass leg: mean count {mass['mean_count']:.1f}, select {ms[0]:.2f} ms, fwd {ms[1]:.1f} ms, "

@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
   sparse_attn_fwd(q, k, v, idx, ...)  -> (o, lse), or (o, lse, o_lo) with residual=True
   sparse_attn_bwd(q, k, v, o, do, lse, idx, ..., o_lo=None) -> (dq, dk, dv)
   block_recall(lse_selected, lse_all, q_block) -> recall [B, H, N/Bq] (true mass captured)
+  head_density(block_counts, topk, ...) -> (density [B, H], dense flag [B, H])
   pack_kv(k, v, idx, qb_begin, qb_end, ...) -> (k_packed, v_packed, packed_blocks, packed_counts, packed_idx)
 """
 from __future__ import annotations
@@ -31,7 +32,7 @@ STATUS = {0: "DSV_OK", 1: "DSV_ERR_INVALID_ARGUMENT", 2: "DSV_ERR_UNSUPPORTED", 
           4: "DSV_ERR_HIP"}
 
 EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_predict_representative", "dsv_select_topk",
-            "dsv_select_mass", "dsv_block_recall", "dsv_pack_kv_workspace_size", "dsv_pack_kv",
+            "dsv_select_mass", "dsv_head_density", "dsv_block_recall", "dsv_pack_kv_workspace_size", "dsv_pack_kv",
             "dsv_sparse_attn_fwd_workspace_size",
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd_workspace_size", "dsv_sparse_attn_bwd", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_timing_begin", "dsv_timing_end")
@@ -76,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsv_select_topk": (ctypes.c_int, [P, V, V, V]),
         "dsv_select_mass": (ctypes.c_int, [P, V, ctypes.c_float, V, V, V]),
         "dsv_block_recall": (ctypes.c_int, [P, V, V, V, V]),
+        "dsv_head_density": (ctypes.c_int, [P, V, ctypes.c_float, V, V, V]),
         "dsv_pack_kv_workspace_size": (S, [P]),
         "dsv_pack_kv": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, ctypes.c_int32, V, V, V, V, V, V, S, V]),
         "dsv_sparse_attn_fwd_workspace_size": (S, [P]),
@@ -307,6 +309,31 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block:
                                    _p(block_idx), _p(block_counts), _p(dq), _p(dk), _p(dv), _p(ws),
                                    ws.numel() * ws.element_size(), _stream(dev)), "dsv_sparse_attn_bwd")
     return dq, dk, dv
+
+
+def head_density(block_counts: Optional[torch.Tensor], *, topk: int, seq_len: int, q_block: int, kv_block: int = 64,
+                 dense_above: float = 0.5, batch: Optional[int] = None, heads: Optional[int] = None):
+    """Per-head selected density and dense flag (the per-block activation of sparse attention):
+    density = selected KV blocks / (N/Bq * N/Bk); dense = 1 where the selected count exceeds
+    floor(dense_above * N/Bq * N/Bk).  block_counts [B, H, N/Bq] int32, or None with batch, heads
+    given (every list full).  Returns (density float32 [B, H], dense int32 [B, H])."""
+    lib = load_library()
+    if block_counts is not None:
+        _contig(block_counts)
+        if block_counts.dtype != torch.int32 or block_counts.dim() != 3:
+            raise ValueError("block_counts must be int32 [B, H, N/Bq]")
+        batch, heads = block_counts.shape[0], block_counts.shape[1]
+        dev = block_counts.device
+    else:
+        if batch is None or heads is None:
+            raise ValueError("without block_counts, pass batch and heads")
+        dev = torch.device("cuda", torch.cuda.current_device())
+    prob = Problem(batch, heads, seq_len, 64, q_block, kv_block, topk, 1, DSV_BF16, 0.0, 0.0)
+    density = torch.empty((batch, heads), dtype=torch.float32, device=dev)
+    dense = torch.empty((batch, heads), dtype=torch.int32, device=dev)
+    _check(lib.dsv_head_density(ctypes.byref(prob), _p(block_counts), ctypes.c_float(dense_above), _p(density),
+                                _p(dense), _stream(dev)), "dsv_head_density")
+    return density, dense
 
 
 def block_recall(lse_selected: torch.Tensor, lse_all: torch.Tensor, *, q_block: int,

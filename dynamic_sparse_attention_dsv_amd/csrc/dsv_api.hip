@@ -343,6 +343,24 @@ dsv_status dsv_select_mass(const dsv_problem* p, const float* block_scores, floa
   return DSV_OK;
 }
 
+dsv_status dsv_head_density(const dsv_problem* p, const int32_t* block_counts, float dense_above, float* density,
+                            int32_t* dense, void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, false));
+  if (!std::isfinite(dense_above) || dense_above < 0.f)
+    return fail(DSV_ERR_INVALID_ARGUMENT, "dense_above must be finite and >= 0");
+  if (block_counts) TRY(check_ptr(block_counts, "block_counts", 4));
+  TRY(check_ptr(density, "density", 4));
+  if (dense) TRY(check_ptr(dense, "dense", 4));
+  const double cells = (double)o.nqb() * (double)o.nkb();
+  const long long limit = (long long)std::floor((double)dense_above * cells);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY_HIP(dsv::launch_head_density(block_counts, density, dense, o.nqb(), o.k, o.nkb(), limit, o.bh(), st),
+          "head_density_kernel");
+  return DSV_OK;
+}
+
 dsv_status dsv_block_recall(const dsv_problem* p, const float* lse_selected, const float* lse_all, float* recall,
                             void* stream) {
   g_err.clear();

@@ -27,6 +27,8 @@ hipError_t launch_scores_f32(const float* qlr, const float* klr, float* lse, flo
 
 // selection
 hipError_t launch_select_topk(const float* scores, int32_t* idx, int rows, int nkb, int k, hipStream_t st);
+hipError_t launch_head_density(const int32_t* cnts, float* density, int32_t* dense, int nqb, int k, int nkb,
+                               long long limit, int bh, hipStream_t st);
 hipError_t launch_block_recall(const float* lse_sel, const float* lse_all, float* recall, int rows, int bq,
                                hipStream_t st);
 hipError_t launch_select_mass(const float* scores, int32_t* idx, int32_t* cnts, int rows, int nkb, int kmax,

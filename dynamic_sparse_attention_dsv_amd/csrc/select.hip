@@ -198,6 +198,39 @@ hipError_t launch_block_recall(const float* lse_sel, const float* lse_all, float
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- per-head density (activation)
+//
+// The pages switch a block of the model to sparse attention once it is sparse enough ([de] §2.A,
+// stage 2).  The measure here: a head's selected density, its selected KV blocks summed over its
+// query blocks (exact integers) over query blocks x KV blocks, and a dense flag, set when that sum
+// exceeds `limit` = floor(dense_above * cells) (computed by the host).  One wave per head.
+__global__ __launch_bounds__(256) void head_density_kernel(const int32_t* __restrict__ cnts, float* __restrict__ density,
+                                                           int32_t* __restrict__ dense, int nqb, int k, int nkb,
+                                                           long long limit, int bh_total) {
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= bh_total) return;  // whole wave exits together
+  long long tot = 0;
+  if (cnts) {
+    for (int qb = lane; qb < nqb; qb += 64) tot += list_len(cnts, (size_t)bh * nqb + qb, k);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+  } else {
+    tot = (long long)k * nqb;
+  }
+  if (lane == 0) {
+    density[bh] = (float)((double)tot / ((double)nqb * (double)nkb));
+    if (dense) dense[bh] = tot > limit ? 1 : 0;
+  }
+}
+
+hipError_t launch_head_density(const int32_t* cnts, float* density, int32_t* dense, int nqb, int k, int nkb,
+                               long long limit, int bh, hipStream_t st) {
+  hipLaunchKernelGGL(head_density_kernel, dim3((bh + 3) / 4), dim3(256), 0, st, cnts, density, dense, nqb, k, nkb,
+                     limit, bh);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_topk(const float* scores, int32_t* idx, int rows, int nkb, int k, hipStream_t st) {
   const dim3 grid((rows + 3) / 4), block(256);
   const int npl = (nkb + 63) / 64;

@@ -178,6 +178,25 @@ dsv_status dsv_select_mass(const dsv_problem* p, const float* block_scores, floa
                            int32_t* block_counts, void* stream);
 
 /*
+ * dsv_head_density -- per-block activation of sparse attention: the pages switch a block of
+ * the model from full to sparse attention once its attention is sparse enough ([de] §2.A,
+ * stage 2).  The measure is each head's selected density,
+ *   S[b,h] = sum over query blocks of the list length (block_counts clamped to [0, k], or k
+ *            when block_counts is NULL),   density[b,h] = S / (N/Bq * N/Bk)  (float32 of the
+ *            exact quotient),
+ * and the head is flagged dense (dense[b,h] = 1, else 0) when S > floor(dense_above * N/Bq *
+ * N/Bk), the product taken in double precision on the host.  A caller runs flagged heads (or
+ * a layer with any flagged head) with every block selected, i.e. dense attention through the
+ * same kernels.
+ *   block_counts  [B, H, N/Bq] int32 (dsv_select_mass's counts) or NULL
+ *   dense_above   finite, >= 0 (e.g. 0.5);  density [B, H] float32 output;
+ *   dense         [B, H] int32 output, or NULL
+ * Uses problem.batch, heads, seq_len, q_block, kv_block and topk (= the lists' width k).
+ */
+dsv_status dsv_head_density(const dsv_problem* p, const int32_t* block_counts, float dense_above, float* density,
+                            int32_t* dense, void* stream);
+
+/*
  * dsv_block_recall -- sparsity profiler: the true attention mass a selection captures ([de]
  * §2.A: the critical KV carry most of the attention score).  For query row i with selected
  * keys J_i, the captured mass is sum_{j in J_i} softmax(s_i)_j over ALL keys

@@ -180,3 +180,11 @@ def test_bf16_backward_rejects_extreme_softmax_scales(lib):
         st = lib.dsv_sparse_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                      FAKE, FAKE, nb, None)
         assert st == 2 and "sm_scale" in lib.dsv_last_error().decode()
+
+
+def test_head_density_validates_threshold(lib):
+    p = _prob()
+    for thr in (-0.1, float("nan"), float("inf")):
+        assert lib.dsv_head_density(ctypes.byref(p), None, ctypes.c_float(thr), FAKE, None, None) == 1
+        assert "dense_above" in lib.dsv_last_error().decode()
+    assert lib.dsv_head_density(ctypes.byref(p), None, ctypes.c_float(0.5), None, None, None) == 1

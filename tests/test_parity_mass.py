@@ -153,3 +153,29 @@ def test_ragged_attention_f32_matches_the_oracle():
     assert np.abs(to_f64(lse) - lse_o).max() <= FWD_F32_MAXABS
     for got, ref in zip(grads, O.sparse_attn_bwd(x["q"], x["k"], x["v"], x["do"], lists, cfg.q_block, cfg.kv_block, sc)):
         assert np.abs(to_f64(got) - ref).max() <= 1e-4
+
+
+@pytest.mark.parametrize("dense_above", [0.0, 0.05, 0.3, 0.5, 0.9999])
+def test_head_density_matches_the_oracle(dense_above):
+    # counts from mass selection on real scores, plus constructed heads: empty, full, out of range
+    cfg = get_config("C2").with_(heads=4)
+    inp = make_inputs(cfg, with_grad=False)
+    t = {k: to_dev(v) for k, v in inp.items() if k in ("q", "k", "wq", "wk")}
+    scores = dsv.predict(t["q"], t["k"], t["wq"], t["wk"], q_block=cfg.q_block, kv_block=cfg.kv_block)
+    kmax = 96
+    _, cnt = dsv.select_mass(scores, 0.5, kmax, q_block=cfg.q_block, kv_block=cfg.kv_block)
+    cnt[0, 1] = 0
+    cnt[0, 2] = kmax
+    cnt[0, 3, ::2] = 1000
+    cnt[0, 3, 1::2] = -3
+    thr = float(np.float32(dense_above))  # the value the float argument carries
+    kw = dict(topk=kmax, seq_len=cfg.seq_len, q_block=cfg.q_block, kv_block=cfg.kv_block, dense_above=thr)
+    dens, flag = dsv.head_density(cnt, **kw)
+    torch.cuda.synchronize()
+    ref_d, ref_f = O.head_density(cnt.cpu().numpy(), kmax, cfg.nqb, cfg.nkb, thr)
+    assert np.array_equal(dens.cpu().numpy(), ref_d.astype(np.float32))
+    assert np.array_equal(flag.cpu().numpy().astype(bool), ref_f)
+    full_d, full_f = dsv.head_density(None, batch=1, heads=4, **kw)
+    torch.cuda.synchronize()
+    assert np.all(full_d.cpu().numpy() == np.float32(kmax / cfg.nkb))
+    log(f"[parity] head density (dense_above={thr}): {dens.cpu().numpy().round(4).tolist()}, flags {flag.cpu().numpy().tolist()}")
