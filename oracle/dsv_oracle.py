@@ -32,24 +32,24 @@ Readings where the pages are silent, ambiguous or garbled:
      1/sqrt(d)); there is no causal mask (video DiT self-attention is full);
   R3 Q_lr and K_lr are rounded to the run's storage dtype (bf16: nearest, ties
      to even) before the logit product; in fp32 runs they are kept exact;
-  R4 a block score is the predicted softmax mass of the query block on the KV
+  R4-R5 a block score is the predicted softmax mass of the query block on the KV
      block, SUMMED over the block's Bq rows (each score row sums to Bq);
-  R5 every query row of a group contributes (the Spanish page's joint
+  R6 every query row of a group contributes (the Spanish page's joint
      processing); the representative-row variant of the German page is a
      separate function;
-  R6 fixed k per query block; ties go to the smaller KV-block index; the list
+  R7 fixed k per query block; ties go to the smaller KV-block index; the list
      is emitted ascending and duplicate-free; no block is forced in;
-  R7 the sparse softmax is renormalised over the selected keys only; LSE is a
+  R8 the sparse softmax is renormalised over the selected keys only; LSE is a
      natural log of the scaled logits;
-  R8 N must be a multiple of Bq and of Bk, and Bq a multiple of Bk;
-  R9 mass-threshold selection (the pages' own rule: keep the critical KV blocks that
+  R9 N must be a multiple of Bq and of Bk, and Bq a multiple of Bk;
+  R13 mass-threshold selection (the pages' own rule: keep the critical KV blocks that
      carry ~90% of the score, [de] §2.A, [es] §2.A): per query block, the smallest
      set of KV blocks, taken by descending score (ties to the smaller index), whose
      scores sum to at least tau times the row's total score; capped at kmax blocks,
      never empty.  Lists are ascending and padded with -1 to kmax; a negative entry
      of any block list means "no block", and a query block whose list is empty has
      O = 0, LSE = -inf and no gradient;
-  R10 per-block activation of sparse attention (the pages switch a block to sparse
+  R14 per-block activation of sparse attention (the pages switch a block to sparse
      attention once it is sparse enough, [de] §2.A, stage 2; [es] §2.A): the measure
      is a head's selected density, the selected KV blocks summed over its query
      blocks divided by (query blocks x KV blocks); the head is flagged dense when
@@ -100,7 +100,7 @@ def rho(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def _check_blocks(n: int, bq: int, bk: int) -> None:
     if n % bq or n % bk or bq % bk:
-        raise ValueError(f"N={n} must be a multiple of Bq={bq} and Bk={bk}, and Bq of Bk (R8)")
+        raise ValueError(f"N={n} must be a multiple of Bq={bq} and Bk={bk}, and Bq of Bk (R9)")
 
 
 # --------------------------------------------------------------------------
@@ -119,7 +119,7 @@ def project(x: np.ndarray, w: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def block_scores_qblock(q_lr_blk: np.ndarray, k_lr: np.ndarray, bk: int, pred_scale: float) -> np.ndarray:
-    """Predicted softmax mass of one query block on every KV block -> [nkb] (R2, R4, R5).
+    """Predicted softmax mass of one query block on every KV block -> [nkb] (R2, R4-R5, R6).
 
     Every row i of the block gets the full predicted softmax over all N keys,
     P_ij = exp(l_ij - max_j l) / sum_j exp(l_ij - max_j l) with
@@ -181,7 +181,7 @@ def representative_scores_head(q_lr: np.ndarray, k_lr: np.ndarray, bq: int, bk: 
 
 def select_topk_row(scores_row: np.ndarray, k: int) -> np.ndarray:
     """The k highest-scoring KV blocks of one query block, ties to the smaller index,
-    returned ascending (R6)."""
+    returned ascending (R7)."""
     n = scores_row.shape[0]
     if not 1 <= k <= n:
         raise ValueError(f"k={k} out of range [1, {n}]")
@@ -207,7 +207,7 @@ def topk_gap(scores: np.ndarray, k: int) -> np.ndarray:
 
 
 def select_mass_row(scores_row: np.ndarray, tau: float, kmax: int) -> np.ndarray:
-    """Mass-threshold selection of one query block (R9): the smallest descending-score prefix
+    """Mass-threshold selection of one query block (R13): the smallest descending-score prefix
     (ties to the smaller index) whose sum reaches tau * sum(scores_row), at most kmax blocks and
     at least one; returned ascending."""
     n = scores_row.shape[0]
@@ -253,7 +253,7 @@ def mass_margin(scores: np.ndarray, tau: float) -> np.ndarray:
 
 
 def head_density(counts: Optional[np.ndarray], k: int, nqb: int, nkb: int, dense_above: float):
-    """Selected density of each head and its dense flag (R10).
+    """Selected density of each head and its dense flag (R14).
 
     counts [B, H, nqb] list lengths (clamped to [0, k]) or None (every list holds k blocks).
     Returns (density [B, H] float64, dense [B, H] bool)."""
@@ -268,8 +268,8 @@ def head_density(counts: Optional[np.ndarray], k: int, nqb: int, nkb: int, dense
 
 
 def block_recall(q, k, idx, bq: int, bk: int, sm_scale: float) -> np.ndarray:
-    """True attention mass captured by the selected blocks ([de] §2.A: the critical KV carry most of
-    the score; the profiler's question is how much): per query block, the mean over its rows of
+    """True attention mass captured by the selected blocks (R15; [de] §2.A: the critical KV carry
+    most of the score; the profiler's question is how much): per query block, the mean over its rows of
     sum_{j selected} softmax(sm_scale q_i K^T)_j, with the softmax over ALL keys.
     q, k [B, H, N, d]; idx [B, H, nqb, k] (negative entries select nothing) -> [B, H, nqb]."""
     q = np.asarray(q, np.float64)
@@ -335,17 +335,17 @@ def pack_rows(x: np.ndarray, blocks: np.ndarray, count: np.ndarray, bk: int) -> 
 
 def selected_keys(idx_row: np.ndarray, bk: int) -> np.ndarray:
     """Token indices of the selected KV blocks, block by block in list order (negative
-    entries pad a ragged list and select nothing, R9)."""
+    entries pad a ragged list and select nothing, R13)."""
     idx_row = np.asarray(idx_row, np.int64)
     idx_row = idx_row[idx_row >= 0]
     return (idx_row[:, None] * bk + np.arange(bk)[None, :]).reshape(-1)
 
 
 def attn_fwd_qblock(q_blk, k, v, idx_row, bk: int, sm_scale: float) -> Tuple[np.ndarray, np.ndarray]:
-    """Softmax attention of one query block over its selected keys only (R7).
+    """Softmax attention of one query block over its selected keys only (R8).
 
     Returns (O [Bq, d], LSE [Bq]) with LSE_i = log sum_j exp(sm_scale <q_i, k_j>).  An empty
-    list (R9) defines O = 0 and LSE = -inf.
+    list (R13) defines O = 0 and LSE = -inf.
     """
     keys = selected_keys(idx_row, bk)
     if keys.size == 0:

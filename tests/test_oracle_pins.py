@@ -364,11 +364,11 @@ def test_rejects_bad_block_sizes():
         O.sparse_attn_fwd(z, z, z, np.zeros((1, 1, 1, 1), np.int32), 64, 64, 1.0)
 
 
-# ------------------------------------------------------------------ mass-threshold selection (R9)
+# ------------------------------------------------------------------ mass-threshold selection (R13)
 
 
 def _greedy_mass_python(scores, tau, kmax):
-    """Independent statement of R9 with Python's sort and a running sum."""
+    """Independent statement of R13 with Python's sort and a running sum."""
     order = sorted(range(len(scores)), key=lambda i: (-scores[i], i))
     target, acc, chosen = tau * sum(scores), 0.0, []
     for i in order:
@@ -495,7 +495,7 @@ def test_block_recall_special_cases_and_identity_predictor():
 
 
 def test_head_density_worked_example():
-    # R10 by hand: lists of lengths 1, 2, 3, 4 (clamped to k = 3) over 4 query blocks x 8 KV blocks
+    # R14 by hand: lists of lengths 1, 2, 3, 4 (clamped to k = 3) over 4 query blocks x 8 KV blocks
     counts = np.array([[[1, 2, 3, 4], [-5, 0, 0, 3]]])
     dens, dense = O.head_density(counts, 3, 4, 8, 0.28)
     assert dens[0, 0] == 9 / 32 and dens[0, 1] == 3 / 32
