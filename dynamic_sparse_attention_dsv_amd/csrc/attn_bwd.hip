@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
         const bf16x8 pa = cvt8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
         const bf16x8 da = cvt8(dsv_[0], dsv_[1], dsv_[2], dsv_[3], dsv_[4], dsv_[5], dsv_[6], dsv_[7]);
         // rows cc*16.. of the query half: bases move by 16 rows
-        const int o0 = tb0 + cc * 16 * D, o1 = tb1 + cc * 16 * D;
+        const int o0 = tb0 + cc * 32 * D, o1 = tb1 + cc * 32 * D;
         bf16x8 ob = tr_frag_at<D>(os, o0, o1, 0), qb = tr_frag_at<D>(qs, o0, o1, 0);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16 s = f32x16{}, dp = f32x16{};
-      const int rt = rb + t * 32 * D;
+      const int rt = rb + t * 64 * D;
       bf16x8 ka = row_frag_at<D>(Kc, rt, 0), va = row_frag_at<D>(Vc, rt, 0);
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
         const int b0 = h2 * 8, cc = t * 2 + h2;
         const f16x8 ds = cvt8h(dp[b0], dp[b0 + 1], dp[b0 + 2], dp[b0 + 3], dp[b0 + 4], dp[b0 + 5], dp[b0 + 6],
                                dp[b0 + 7]);
-        const int o0 = kb0 + cc * 16 * D, o1 = kb1 + cc * 16 * D;
+        const int o0 = kb0 + cc * 32 * D, o1 = kb1 + cc * 32 * D;
         bf16x8 kt = tr_frag_at<D>(Kc, o0, o1, 0);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {

@@ -91,18 +91,18 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   const int arow = sigma(c32);
 
-  // S^T = K Q^T for one KV block (two 32-key tiles, K rows in sigma order: base + t*32*D), each
+  // S^T = K Q^T for one KV block (two 32-key tiles, K rows in sigma order: byte base + t*64*D), each
   // k-step's K operand read one step ahead; fragment offsets from one base, recomputed per block
   auto scores = [&](const uint16_t* Kc, f32x16 (&s)[2]) {
     const int rb = opaque(row_base<D>(arow, lane));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = f32x16{};
-      bf16x8 ka = row_frag_at<D>(Kc, rb + t * 32 * D, 0);
+      bf16x8 ka = row_frag_at<D>(Kc, rb + t * 64 * D, 0);
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
         bf16x8 kn = ka;
-        if (dc + 1 < D / 16) kn = row_frag_at<D>(Kc, rb + t * 32 * D, dc + 1);
+        if (dc + 1 < D / 16) kn = row_frag_at<D>(Kc, rb + t * 64 * D, dc + 1);
         s[t] = mfma32(ka, qf[dc], s[t]);
         ka = kn;
       }
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
       }
     l_run += psum;
     // O^T += V^T P^T: V^T operands by transposed reads of the row-major V tile (rows cc*16..:
-    // bases + cc*16*D); P^T chunk cc = registers (cc%2)*8.. of tile cc/2.  P <= 2^8 (lazy
+    // byte bases + cc*32*D); P^T chunk cc = registers (cc%2)*8.. of tile cc/2.  P <= 2^8 (lazy
     // rescaling), so fp16 holds it; a bf16 rounding of P (2^-8 relative) would be fine for O
     // itself but too coarse for the backward's D = rowsum(dO * O), which the dQ product
     // multiplies by K -- the training forward therefore rounds P to fp16 against fp16 V.
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     for (int cc = 0; cc < 4; ++cc) {
       const f32x16& st = s[cc >> 1];
       const int b0 = (cc & 1) * 8;
-      const int o0 = vb0 + cc * 16 * D, o1 = vb1 + cc * 16 * D;
+      const int o0 = vb0 + cc * 32 * D, o1 = vb1 + cc * 32 * D;
       bf16x8 va = tr_frag_at<D>(Vc, o0, o1, 0);
       if constexpr (PV16) {
         const f16x8 ph = cvt8h(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],

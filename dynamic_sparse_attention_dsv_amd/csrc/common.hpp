@@ -178,32 +178,34 @@ __device__ __forceinline__ bf16x8 row_frag(const uint16_t* tile, int row, int k0
 }
 
 // Cheap addressing of a run of fragments.  The k-step (16 columns) or the
-// 32-column tile index only moves bits of the element offset that neither the
-// row term nor the lane's in-chunk term touch, and it enters the swizzle by
-// XOR.  So one base offset per lane serves the whole run:
-//   row_frag(tile, row, 16*s, lane) == tile[row_base(row, lane) ^ (s << 4)]
-//   tr_frag (tile, k0, 32*t, lane)  == reads at tr_base{0,1}(k0, lane) ^ (t << 5)
-// (s < D/16, t < D/32).  Moving k0 or row by 16 adds 16*D to the base, since
-// the swizzle depends on the row modulo 16 only.
+// 32-column tile index only moves bits of the offset that neither the row term
+// nor the lane's in-chunk term touch, and it enters the swizzle by XOR.  So one
+// base offset per lane serves the whole run.  Bases are BYTE offsets, so each
+// fragment address costs one XOR:
+//   row_frag(tile, row, 16*s, lane) == tile bytes [row_base(row, lane) ^ (s << 5)]
+//   tr_frag (tile, k0, 32*t, lane)  == reads at tr_base{0,1}(k0, lane) ^ (t << 6)
+// (s < D/16, t < D/32).  Moving k0 or row by 16 adds 32*D bytes to the base,
+// since the swizzle depends on the row modulo 16 only.
 template <int D>
-__device__ __forceinline__ int row_base(int row, int lane) { return toff<D>(row, (lane >> 5) * 8); }
+__device__ __forceinline__ int row_base(int row, int lane) { return toff<D>(row, (lane >> 5) * 8) * 2; }
 
 template <int D>
 __device__ __forceinline__ bf16x8 row_frag_at(const uint16_t* tile, int base, int s) {
-  return as_bf16x8(ld16(tile + (base ^ (s << 4))));
+  return as_bf16x8(ld16(reinterpret_cast<const char*>(tile) + (base ^ (s << 5))));
 }
 
 template <int D>
 __device__ __forceinline__ int tr_base(int k0, int lane, int half) {
   const int row = k0 + (lane >> 5) * 8 + ((lane & 15) >> 2) + half * 4;
   const int col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-  return toff<D>(row, col);
+  return toff<D>(row, col) * 2;
 }
 
 template <int D>
 __device__ __forceinline__ bf16x8 tr_frag_at(const uint16_t* tile, int b0, int b1, int t) {
-  const i16x4 a = ds_read_tr16(tile + (b0 ^ (t << 5)));
-  const i16x4 b = ds_read_tr16(tile + (b1 ^ (t << 5)));
+  const char* base = reinterpret_cast<const char*>(tile);
+  const i16x4 a = ds_read_tr16(reinterpret_cast<const uint16_t*>(base + (b0 ^ (t << 6))));
+  const i16x4 b = ds_read_tr16(reinterpret_cast<const uint16_t*>(base + (b1 ^ (t << 6))));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, ab);
