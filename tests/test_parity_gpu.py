@@ -259,9 +259,11 @@ def test_single_block_and_unselected_blocks_get_zero_gradient():
 # ------------------------------------------------------------------ full-size configs, sampled outputs
 
 
-@pytest.mark.parametrize("name", ["C4", "C5"])
+@pytest.mark.parametrize("name", ["C4", "C5", "NMAX"])
 def test_full_size_sampled(name):
-    cfg = get_config(name)
+    # NMAX: the largest sequence the library takes, N/Bk = 4096 KV blocks (N = 262144, a 64^3
+    # latent), at C5's head shape and 10 % density, two heads
+    cfg = get_config("C5").with_(latent=(64, 64, 64), heads=2, topk=410) if name == "NMAX" else get_config(name)
     log(f"[parity] {name} full size N={cfg.seq_len} H={cfg.heads} k={cfg.topk}: generating inputs")
     inp = make_inputs(cfg, workers=16)
     sc = _scale(cfg.head_dim)
