@@ -108,10 +108,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
       }
     }
   };
-  // online softmax of one block's scores, part 1: the row maximum and the (rare) rescaling
-  auto rescale = [&](const f32x16 (&s)[2]) {
-    // online softmax (log2 domain); lane owns one query, 32 of the block's 64 keys.
-    // Row maximum by a tree over the 32 values.
+  // Row maximum of a block's raw scores: a tree over the lane's 32 values, then lane ^ 32.
+  auto raw_max = [&](const f32x16 (&s)[2]) {
     float mx8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -120,17 +118,39 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     for (int w = 4; w >= 1; w >>= 1)
 #pragma unroll
       for (int e = 0; e < w; ++e) mx8[e] = fmaxf(mx8[e], mx8[e + w]);
-    const float mx = max_xor32(mx8[0]) * c;
-    // Lazy rescaling: the running shift m_run only moves when the block's maximum exceeds it by
-    // more than 8 (log2 units), so exponentials stay below 2^8 and the accumulator and row sum
-    // are rescaled rarely.  Any shift gives the same O = acc / l; the choice only moves rounding.
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
+    return max_xor32(mx8[0]);
+  };
+  // online softmax of one block's scores, part 1: the exponents t = s c - m_run (in place), their
+  // row maximum and the (rare) rescaling.
+  // Lazy rescaling: the running shift m_run only moves when an exponent exceeds 8 (log2 units),
+  // so exponentials stay below 2^8 and the accumulator and row sum are rescaled rarely.  Any
+  // shift gives the same O = acc / l; the choice only moves rounding.  Taking the maximum over
+  // the exponents rather than the raw MFMA results saves work: they are needed anyway, and as
+  // fma results they take three-input maxima with no canonicalisation.
+  auto rescale = [&](f32x16 (&s)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) s[t][vv] = fmaf(s[t][vv], c, -m_run);
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+#pragma unroll
+    for (int e = 3; e < 31; e += 2) {
+      const float a = e < 16 ? s[0][e] : s[1][e - 16], b = e + 1 < 16 ? s[0][e + 1] : s[1][e + 1 - 16];
+      mx = fmaxf(fmaxf(mx, a), b);
+    }
+    mx = fmaxf(mx, s[1][15]);
+    mx = max_xor32(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > 8.f) != 0) {
+      const float shift = fmaxf(mx, 0.f);
+      const float alpha = fast_exp2(-shift);
+      m_run += shift;
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) s[t][vv] -= shift;
     }
   };
   // part 2: exponentials, row sum and O^T += V^T P^T from Vc
@@ -140,7 +160,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        s[t][vv] = fast_exp2(fmaf(s[t][vv], c, -m_run));
+        s[t][vv] = fast_exp2(s[t][vv]);
         psum += s[t][vv];
       }
     l_run += psum;
@@ -194,6 +214,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   issue(v, blk_at(0), V0);
   __syncthreads();
   scores(K0, sa);
+  m_run = raw_max(sa) * c;  // the first block sets the shift
   __syncthreads();  // every wave has read K0 before step 0 refills it
   int j = 0;
   for (; j + 1 < kq; j += 2) {
