@@ -27,14 +27,29 @@
 
 namespace dsv {
 
+// The dK/dV kernel's per-head dS exponent r: |dS_ij| <= |dP_ij - D_i| <= 2 d max|dO| max|V|, so
+// dS 2^r stays inside fp16's range at full precision.  absmax: per-head max |.| bits of K, Q, V,
+// dO (bh_total each).
+template <int D>
+__device__ __forceinline__ int dkdv_ds_exponent(const uint32_t* absmax, int bh, int bh_total) {
+  const float vmax = __uint_as_float(absmax[2 * bh_total + bh]);
+  const float omax = __uint_as_float(absmax[3 * bh_total + bh]);
+  return min(max(f16_exponent(__float_as_uint(2.f * (float)D * omax * vmax)), -120), 120);
+}
+
 // ---------------------------------------------------------------- D = rowsum(dO o O), lse2 = lse * log2(e)
+//
+// Also D 2^r with the dK/dV kernel's per-head dS exponent r (dvec_s), so that kernel forms
+// dS 2^r = P (dP 2^r - D 2^r) with no extra multiply.
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(const uint16_t* __restrict__ o,
                                                            const uint16_t* __restrict__ o_lo,
                                                            const uint16_t* __restrict__ dout,
                                                            const float* __restrict__ lse, float* __restrict__ dvec,
-                                                           float* __restrict__ lse2, int rows) {
+                                                           float* __restrict__ lse2, float* __restrict__ dvec_s,
+                                                           const uint32_t* __restrict__ absmax, int n, int bh_total,
+                                                           int rows) {
   constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
   const int t = blockIdx.x * 256 + threadIdx.x;
   const int row = t / LPR, c = t % LPR;
@@ -55,6 +70,7 @@ __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(const uint16_t* __res
   if (row < rows && c == 0) {
     dvec[row] = acc;
     lse2[row] = lse[row] * kLog2e;
+    dvec_s[row] = ldexpf(acc, dkdv_ds_exponent<D>(absmax, row / n, bh_total));
   }
 }
 
@@ -210,14 +226,23 @@ __global__ __launch_bounds__(256) void csc_emit_kernel(const uint32_t* __restric
 // LDS tiles by direct global->LDS loads (double-buffered) and read both row-wise (A operands of S = Q K^T
 // and dP = dO V^T) and transposed (B operands of dV += P^T dO, dK += dS^T Q).
 // The two query halves' partial dK/dV are summed through LDS at the end.
+//
+// All four products are fp16, on copies scaled per head by powers of two (exact for bf16
+// values): Q, K and dO come as fp16 copies from launch_bwd_prep_bf16, V is converted in
+// registers.  S and dP are then the exact bf16 products scaled by 2^(sQ+sK) and 2^(sO+sV).
+// dS is rounded to fp16 (2^-11 relative; a bf16 rounding lets Q's large entries amplify it into
+// dK) after scaling by 2^r: dK sums over queries, so the scale is one per head, from
+// |dS_ij| <= |dP_ij - D_i| <= 2 d max|dO| max|V|.  P <= 1 enters dV += P^T dO in fp16 as is.
+// Every scale is undone exactly at the end.
 
 template <int D, int BQ>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dvec,
-    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ rows, const int32_t* __restrict__ order,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int n, int nnz_per_bh, int nwg,
-    float c /* sm_scale*log2e */, float sm_scale) {
+    const uint16_t* __restrict__ q16, const uint16_t* __restrict__ k16, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ o16 /* fp16 copy of dO */, const float* __restrict__ lse2,
+    const float* __restrict__ dvec /* D 2^r */, const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ order, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    const uint32_t* __restrict__ absmax /* per head max |.| bits: K, Q, V, dO, bh_total each */, int bh_total,
+    int n, int nnz_per_bh, int nwg, float c /* sm_scale*log2e */, float sm_scale) {
   constexpr int QR = 64;                 // query rows per chunk
   constexpr int NT = QR * D / 512;       // global->LDS instructions per tile
   constexpr int SUBS = BQ / QR;
@@ -240,6 +265,25 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
   const int32_t* cp = col_ptr + (size_t)bh * (nkb + 1);
   const int start = cp[kb], cnt = cp[kb + 1] - start;
   const int32_t* list = rows + (size_t)bh * nnz_per_bh + start;
+  // per-head scales (wave-uniform, kept in scalar registers): r for dS, and the softmax constant
+  // with S's scale 2^(sQ+sK) folded in
+  struct Scales {
+    int r, sQ, sK, sV, sO;
+  };
+  auto head_scales = [&]() {
+    Scales h;
+    h.sK = f16_shift(absmax[bh]);
+    h.sQ = f16_shift(absmax[bh_total + bh]);
+    h.sV = f16_shift(absmax[2 * bh_total + bh]);
+    h.sO = f16_shift_wide(absmax[3 * bh_total + bh]);  // dO's shift cancels in pscale: not capped
+    h.r = dkdv_ds_exponent<D>(absmax, bh, bh_total);
+    return h;
+  };
+  auto uniform = [](float x) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x))); };
+  const Scales hs = head_scales();
+  const float cs = uniform(ldexpf(c, -(hs.sQ + hs.sK)));            // S is scaled by 2^(sQ+sK)
+  const float pscale = uniform(ldexpf(1.f, hs.r - hs.sO - hs.sV));   // dP (scaled by 2^(sO+sV)) to 2^r
+  const int sV = __builtin_amdgcn_readfirstlane(hs.sV);
 
   f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
@@ -248,11 +292,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
 
   if (cnt > 0) {
     // K^T and V^T as B operands: lane holds its key, 8 consecutive d per chunk
-    bf16x8 kf[D / 16], vf[D / 16];
+    bf16x8 kf[D / 16];
+    f16x8 vf[D / 16];
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) {
-      kf[dc] = as_bf16x8(ld16(k + head + (size_t)key * D + dc * 16 + g * 8));
-      vf[dc] = as_bf16x8(ld16(v + head + (size_t)key * D + dc * 16 + g * 8));
+      kf[dc] = as_bf16x8(ld16(k16 + head + (size_t)key * D + dc * 16 + g * 8));  // fp16 bits
+      const u32x4 w = ld16(v + head + (size_t)key * D + dc * 16 + g * 8);
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = ldexpf(__uint_as_float(w[e] << 16), sV);
+        f[2 * e + 1] = ldexpf(__uint_as_float(w[e] & 0xffff0000u), sV);
+      }
+      vf[dc] = cvt8h(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
     }
     const int nch = cnt * SUBS;
     auto q0_of = [&](int j) { return list[j / SUBS] * BQ + (j % SUBS) * QR; };
@@ -261,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
       for (int i = wave; i < 2 * NT; i += 4) {
         const bool iso = i >= NT;
         const int ii = iso ? i - NT : i;
-        lds_load_rows<D>((iso ? dout : q) + head + (size_t)q0 * D, iso ? od : qd, ii, lane);
+        lds_load_rows<D>((iso ? o16 : q16) + head + (size_t)q0 * D, iso ? od : qd, ii, lane);
       }
       if (wave == 3 && lane < 32)  // lanes 0-15: 64 lse2 values, lanes 16-31: 64 D values
         __builtin_amdgcn_global_load_lds((lane < 16 ? lse2 : dvec) + (size_t)bh * n + q0 + (lane & 15) * 4, ld, 16,
@@ -283,8 +335,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
           qn = row_frag_at<D>(qs, rb, dc + 1);
           on = row_frag_at<D>(os, rb, dc + 1);
         }
-        s = mfma32(qa, kf[dc], s);
-        dp = mfma32(oa, vf[dc], dp);
+        s = mfma32h(as_f16x8(qa), as_f16x8(kf[dc]), s);
+        dp = mfma32h(as_f16x8(oa), vf[dc], dp);
         qa = qn;
         oa = on;
       }
@@ -305,11 +357,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
           const int vv = cc * 8 + e;
           const float lq = e < 4 ? l0[e] : l1[e - 4];
           const float dd = e < 4 ? d0[e] : d1[e - 4];
-          pv[e] = fast_exp2(fmaf(s[vv], c, -lq));
-          dsv_[e] = pv[e] * (dp[vv] - dd);
+          pv[e] = fast_exp2(fmaf(s[vv], cs, -lq));
+          dsv_[e] = pv[e] * fmaf(dp[vv], pscale, -dd);  // dS 2^r (dd = D 2^r), exact scaling
         }
-        const bf16x8 pa = cvt8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-        const bf16x8 da = cvt8(dsv_[0], dsv_[1], dsv_[2], dsv_[3], dsv_[4], dsv_[5], dsv_[6], dsv_[7]);
+        const f16x8 pa = cvt8h(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        const f16x8 da = cvt8h(dsv_[0], dsv_[1], dsv_[2], dsv_[3], dsv_[4], dsv_[5], dsv_[6], dsv_[7]);
         // rows cc*16.. of the query half: bases move by 16 rows
         const int o0 = tb0 + cc * 32 * D, o1 = tb1 + cc * 32 * D;
         bf16x8 ob = tr_frag_at<D>(os, o0, o1, 0), qb = tr_frag_at<D>(qs, o0, o1, 0);
@@ -320,8 +372,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
             obn = tr_frag_at<D>(os, o0, o1, dt + 1);
             qbn = tr_frag_at<D>(qs, o0, o1, dt + 1);
           }
-          dva[dt] = mfma32(pa, ob, dva[dt]);
-          dka[dt] = mfma32(da, qb, dka[dt]);
+          dva[dt] = mfma32h(pa, as_f16x8(ob), dva[dt]);
+          dka[dt] = mfma32h(da, as_f16x8(qb), dka[dt]);
           ob = obn;
           qb = qbn;
         }
@@ -359,6 +411,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
   }
   __syncthreads();
   if (qh == 0) {
+    const Scales h = head_scales();  // recomputed rather than held through the loop
+    const int unscale_k = __builtin_amdgcn_readfirstlane(-(h.r + h.sQ));
+    const int unscale_v = __builtin_amdgcn_readfirstlane(-h.sO);
     // D layout of dK/dV tiles: lane holds d = dt*32 + c32; register vv holds key (vv/4)*8 + g*4 + vv%4
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -366,8 +421,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
       for (int vv = 0; vv < 16; ++vv) {
         const int kr = kb * 64 + kh * 32 + (vv >> 2) * 8 + g * 4 + (vv & 3);
         const size_t off = head + (size_t)kr * D + dt * 32 + c32;
-        dk[off] = f32_to_bf16((dka[dt][vv] + red(0)[ridx(dt, vv)]) * sm_scale);
-        dv[off] = f32_to_bf16(dva[dt][vv] + red(1)[ridx(dt, vv)]);
+        dk[off] = f32_to_bf16(ldexpf((dka[dt][vv] + red(0)[ridx(dt, vv)]) * sm_scale, unscale_k));  // exact
+        dv[off] = f32_to_bf16(ldexpf(dva[dt][vv] + red(1)[ridx(dt, vv)], unscale_v));                // unscale
       }
   }
 }
@@ -379,7 +434,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
 // dQ^T += K^T dS^T takes K^T from transposing reads of the row-major K tile.
 //
 // S and dQ are fp16 products: K comes as an fp16 copy scaled by 2^sK (sK = f16_shift of the
-// head's max |K|; exact for bf16 values), Q is converted in registers with its own head shift sQ,
+// head's max |K|; exact for bf16 values; made by launch_bwd_prep_bf16), Q is converted in
+// registers with its own head shift sQ,
 // so S is the exact bf16 product scaled by 2^(sQ+sK).  dS is rounded to fp16 (2^-11 relative;
 // a bf16 rounding would let K's large entries amplify dS's error into dQ) after scaling row i by
 // 2^r_i, with r_i from the bound |dS_ij| = P_ij |dP_ij - D_i| <= 2 |dO_i|_1 max|V| (both dP_ij
@@ -601,13 +657,18 @@ __global__ void attn_bwd_dkdv_f32_kernel(const float* __restrict__ q, const floa
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* o_lo, const uint16_t* dout, const float* lse,
-                               float* dvec, float* lse2, int rows, int d, hipStream_t st) {
+                               float* dvec, float* lse2, float* dvec_s, const void* f16ws, int bh, int n, int d,
+                               hipStream_t st) {
+  const int rows = bh * n;
   const int lanes = rows * (d / 8);
   dim3 grid((lanes + 255) / 256);
+  const uint32_t* absmax = bwd_f16_absmax(f16ws, bh, n, d);
   if (d == 64)
-    hipLaunchKernelGGL(bwd_pre_bf16_kernel<64>, grid, dim3(256), 0, st, o, o_lo, dout, lse, dvec, lse2, rows);
+    hipLaunchKernelGGL(bwd_pre_bf16_kernel<64>, grid, dim3(256), 0, st, o, o_lo, dout, lse, dvec, lse2, dvec_s, absmax,
+                       n, bh, rows);
   else if (d == 128)
-    hipLaunchKernelGGL(bwd_pre_bf16_kernel<128>, grid, dim3(256), 0, st, o, o_lo, dout, lse, dvec, lse2, rows);
+    hipLaunchKernelGGL(bwd_pre_bf16_kernel<128>, grid, dim3(256), 0, st, o, o_lo, dout, lse, dvec, lse2, dvec_s,
+                       absmax, n, bh, rows);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -643,49 +704,75 @@ hipError_t launch_csc(const int32_t* idx, const int32_t* cnts, uint32_t* bitmap,
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                                const float* lse2, const float* dvec, const int32_t* col_ptr, const int32_t* rows,
-                                const int32_t* order, uint16_t* dk, uint16_t* dv, int bh, int n, int d, int bq,
-                                int topk, float sm_scale, hipStream_t st) {
+// The backward's fp16 copies and per-head maxima, in the workspace at `ws`:
+//   K16, Q16, dO16 [bh, n, d] each, partial maxima, absmax [4][bh] (K, Q, V, dO).
+size_t bwd_f16_ws_bytes(int bh, int n, int d) {
+  return 3 * align_ws((size_t)bh * n * d * 2) + head_absmax_ws_bytes(bh) + align_ws((size_t)bh * 4 * 4);
+}
+
+namespace {
+struct F16Views {
+  uint16_t* k16;
+  uint16_t* q16;
+  uint16_t* o16;
+  uint32_t* part;
+  uint32_t* absmax;
+};
+F16Views f16_views(void* ws, int bh, int n, int d) {
+  char* w = static_cast<char*>(ws);
+  const size_t t = align_ws((size_t)bh * n * d * 2);
+  return {reinterpret_cast<uint16_t*>(w), reinterpret_cast<uint16_t*>(w + t), reinterpret_cast<uint16_t*>(w + 2 * t),
+          reinterpret_cast<uint32_t*>(w + 3 * t), reinterpret_cast<uint32_t*>(w + 3 * t + head_absmax_ws_bytes(bh))};
+}
+}  // namespace
+
+const uint32_t* bwd_f16_absmax(const void* ws, int bh, int n, int d) {
+  return f16_views(const_cast<void*>(ws), bh, n, d).absmax;
+}
+
+hipError_t launch_bwd_prep_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout, void* ws,
+                                int bh, int n, int d, hipStream_t st) {
+  const F16Views f = f16_views(ws, bh, n, d);
+  const size_t per_head = (size_t)n * d;
+  hipError_t e = launch_head_absmax(k, f.part, f.absmax, bh, per_head, st);
+  if (e != hipSuccess) return e;
+  if ((e = launch_to_f16(k, f.absmax, f.k16, bh, per_head, st)) != hipSuccess) return e;
+  if ((e = launch_head_absmax(q, f.part, f.absmax + bh, bh, per_head, st)) != hipSuccess) return e;
+  if ((e = launch_to_f16(q, f.absmax + bh, f.q16, bh, per_head, st)) != hipSuccess) return e;
+  if ((e = launch_head_absmax(v, f.part, f.absmax + 2 * bh, bh, per_head, st)) != hipSuccess) return e;
+  if ((e = launch_head_absmax(dout, f.part, f.absmax + 3 * bh, bh, per_head, st)) != hipSuccess) return e;
+  return launch_to_f16(dout, f.absmax + 3 * bh, f.o16, bh, per_head, st, /*wide=*/true);
+}
+
+hipError_t launch_bwd_dkdv_bf16(const void* ws, const uint16_t* v, const uint16_t* dout, const float* lse2,
+                                const float* dvec, const int32_t* col_ptr, const int32_t* rows, const int32_t* order,
+                                uint16_t* dk, uint16_t* dv, int bh, int n, int d, int bq, int topk, float sm_scale,
+                                hipStream_t st) {
+  const F16Views f = f16_views(const_cast<void*>(ws), bh, n, d);
   const int nwg = bh * (n / 64);
   const int nnz = (n / bq) * topk;
   const float c = sm_scale * kLog2e;
-#define DKDV(D_, BQ_)                                                                                       \
-  if (d == D_ && bq == BQ_) {                                                                               \
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(256), 0, st, q, k, v, dout, lse2, \
-                       dvec, col_ptr, rows, order, dk, dv, n, nnz, nwg, c, sm_scale);                       \
-    return hipGetLastError();                                                                               \
+#define DKDV(D_, BQ_)                                                                                          \
+  if (d == D_ && bq == BQ_) {                                                                                  \
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(256), 0, st, f.q16, f.k16, v, f.o16, \
+                       lse2, dvec, col_ptr, rows, order, dk, dv, f.absmax, bh, n, nnz, nwg, c, sm_scale);     \
+    return hipGetLastError();                                                                                  \
   }
   DKDV(64, 64) DKDV(64, 128) DKDV(128, 64) DKDV(128, 128)
 #undef DKDV
   return hipErrorInvalidValue;
 }
 
-size_t bwd_dq_bf16_ws_bytes(int bh, int n, int d) {
-  return align_ws((size_t)bh * n * d * 2) + head_absmax_ws_bytes(bh) + align_ws((size_t)bh * 3 * 4);
-}
-
-hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                              const float* lse2, const float* dvec, const int32_t* idx, const int32_t* cnts,
-                              uint16_t* dq, void* ws, int bh, int n, int d, int bq, int topk, float sm_scale,
-                              hipStream_t st) {
+hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* v, const uint16_t* dout, const float* lse2,
+                              const float* dvec, const int32_t* idx, const int32_t* cnts, uint16_t* dq, const void* ws,
+                              int bh, int n, int d, int bq, int topk, float sm_scale, hipStream_t st) {
+  const F16Views f = f16_views(const_cast<void*>(ws), bh, n, d);
   const int nwg = bh * (n / bq);
   const float c = sm_scale * kLog2e;
-  // fp16 copy of K and the per-head maxima of |K|, |Q|, |V|
-  const size_t per_head = (size_t)n * d;
-  char* w = static_cast<char*>(ws);
-  uint16_t* k16 = reinterpret_cast<uint16_t*>(w);
-  uint32_t* part = reinterpret_cast<uint32_t*>(w + align_ws((size_t)bh * per_head * 2));
-  uint32_t* absmax = reinterpret_cast<uint32_t*>(w + align_ws((size_t)bh * per_head * 2) + head_absmax_ws_bytes(bh));
-  hipError_t e = launch_head_absmax(k, part, absmax, bh, per_head, st);
-  if (e != hipSuccess) return e;
-  if ((e = launch_to_f16(k, absmax, k16, bh, per_head, st)) != hipSuccess) return e;
-  if ((e = launch_head_absmax(q, part, absmax + bh, bh, per_head, st)) != hipSuccess) return e;
-  if ((e = launch_head_absmax(v, part, absmax + 2 * bh, bh, per_head, st)) != hipSuccess) return e;
 #define DQ(D_, BQ_)                                                                                          \
   if (d == D_ && bq == BQ_) {                                                                                \
-    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k16, v, dout, lse2, \
-                       dvec, idx, cnts, dq, absmax, bh, n, topk, nwg, c, sm_scale);                          \
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, f.k16, v, dout,  \
+                       lse2, dvec, idx, cnts, dq, f.absmax, bh, n, topk, nwg, c, sm_scale);                  \
     return hipGetLastError();                                                                                \
   }
   DQ(64, 64) DQ(64, 128) DQ(128, 64) DQ(128, 128)

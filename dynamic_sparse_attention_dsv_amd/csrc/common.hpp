@@ -89,6 +89,9 @@ __device__ __forceinline__ int f16_exponent(uint32_t m) {
 // (maxima in [2^-26, 2^54] reach the target range; a larger one would overflow fp16).
 constexpr int kAbsmaxParts = 32;  // partial maxima per head
 __device__ __forceinline__ int f16_shift(uint32_t m) { return min(max(f16_exponent(m), -40), 40); }
+// The wide form, for a copy whose scale only meets its own inverse (the output gradient: its
+// shift cancels in dS's scale), so tiny training gradients keep full precision.
+__device__ __forceinline__ int f16_shift_wide(uint32_t m) { return min(max(f16_exponent(m), -120), 120); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

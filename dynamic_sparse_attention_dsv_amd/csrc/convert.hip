@@ -50,11 +50,11 @@ __global__ __launch_bounds__(256) void absmax_final_kernel(const uint32_t* __res
 
 // grid (ceil(per_head / 2048), BH): 8 elements per thread
 __global__ __launch_bounds__(256) void to_f16_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ maxbits,
-                                                     uint16_t* __restrict__ y, size_t per_head) {
+                                                     uint16_t* __restrict__ y, size_t per_head, int wide) {
   const int bh = blockIdx.y;
   const size_t u = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (u >= per_head / 8) return;
-  const int s = f16_shift(maxbits[bh]);
+  const int s = wide ? f16_shift_wide(maxbits[bh]) : f16_shift(maxbits[bh]);
   const u32x4 w = ld16(x + (size_t)bh * per_head + u * 8);
   float f[8];
 #pragma unroll
@@ -77,9 +77,9 @@ hipError_t launch_head_absmax(const uint16_t* x, uint32_t* part, uint32_t* maxbi
 }
 
 hipError_t launch_to_f16(const uint16_t* x, const uint32_t* maxbits, uint16_t* y, int bh, size_t per_head,
-                         hipStream_t st) {
+                         hipStream_t st, bool wide) {
   hipLaunchKernelGGL(to_f16_kernel, dim3((unsigned)((per_head / 8 + 255) / 256), bh), dim3(256), 0, st, x, maxbits, y,
-                     per_head);
+                     per_head, wide ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -158,7 +158,7 @@ PredictWs predict_ws(const Prob& o) {
 }
 
 struct BwdWs {
-  size_t dvec, lse2, bitmap, counts, col_ptr, rows, order, dq16, total;
+  size_t dvec, lse2, dvec_s, bitmap, counts, col_ptr, rows, order, f16, total;
 };
 BwdWs bwd_ws(const Prob& o) {
   BwdWs w{};
@@ -166,8 +166,9 @@ BwdWs bwd_ws(const Prob& o) {
   const size_t rowf = align_up((size_t)o.bh() * o.n * sizeof(float));
   if (o.dtype == DSV_BF16) {
     w.lse2 = off; off += rowf;
+    w.dvec_s = off; off += rowf;
     w.order = off; off += align_up((size_t)o.bh() * o.nkb() * 4);
-    w.dq16 = off; off += align_up(dsv::bwd_dq_bf16_ws_bytes(o.bh(), o.n, o.d));
+    w.f16 = off; off += align_up(dsv::bwd_f16_ws_bytes(o.bh(), o.n, o.d));
   }
   w.dvec = off; off += rowf;
   const int words = (o.nqb() + 31) / 32;
@@ -495,14 +496,16 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
     const uint16_t* do16 = static_cast<const uint16_t*>(dout);
     float* lse2 = at<float>(workspace, w.lse2);
+    void* f16 = at<void>(workspace, w.f16);
+    float* dvec_s = at<float>(workspace, w.dvec_s);
+    TRY_HIP(dsv::launch_bwd_prep_bf16(q16, k16, v16, do16, f16, o.bh(), o.n, o.d, st), "bwd_prep_kernels");
     TRY_HIP(dsv::launch_bwd_pre_bf16(static_cast<const uint16_t*>(o_ptr), static_cast<const uint16_t*>(o_lo), do16,
-                                     lse, dvec, lse2, o.bh() * o.n, o.d, st), "bwd_pre_kernel");
-    TRY_HIP(dsv::launch_bwd_dkdv_bf16(q16, k16, v16, do16, lse2, dvec, col_ptr, rows, order,
-                                      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), o.bh(), o.n, o.d, o.bq,
-                                      o.k, o.sm, st), "attn_bwd_dkdv_kernel");
-    TRY_HIP(dsv::launch_bwd_dq_bf16(q16, k16, v16, do16, lse2, dvec, block_idx, block_counts,
-                                    static_cast<uint16_t*>(dq), at<void>(workspace, w.dq16), o.bh(), o.n, o.d, o.bq,
-                                    o.k, o.sm, st),
+                                     lse, dvec, lse2, dvec_s, f16, o.bh(), o.n, o.d, st), "bwd_pre_kernel");
+    TRY_HIP(dsv::launch_bwd_dkdv_bf16(f16, v16, do16, lse2, dvec_s, col_ptr, rows, order, static_cast<uint16_t*>(dk),
+                                      static_cast<uint16_t*>(dv), o.bh(), o.n, o.d, o.bq, o.k, o.sm, st),
+            "attn_bwd_dkdv_kernel");
+    TRY_HIP(dsv::launch_bwd_dq_bf16(q16, v16, do16, lse2, dvec, block_idx, block_counts, static_cast<uint16_t*>(dq),
+                                    f16, o.bh(), o.n, o.d, o.bq, o.k, o.sm, st),
             "attn_bwd_dq_kernel");
   } else {
     TRY_HIP(dsv::launch_bwd_pre_f32(static_cast<const float*>(o_ptr), static_cast<const float*>(dout), dvec,

@@ -40,8 +40,9 @@ hipError_t launch_select_mass(const float* scores, int32_t* idx, int32_t* cnts, 
 size_t head_absmax_ws_bytes(int bh);
 hipError_t launch_head_absmax(const uint16_t* x, uint32_t* part, uint32_t* maxbits, int bh, size_t per_head,
                               hipStream_t st);
+// (wide: the shift from f16_shift_wide instead of f16_shift)
 hipError_t launch_to_f16(const uint16_t* x, const uint32_t* maxbits, uint16_t* y, int bh, size_t per_head,
-                         hipStream_t st);
+                         hipStream_t st, bool wide = false);
 // bytes of the training forward's scratch (fp16 copy of V, its per-head maxima and shifts)
 size_t attn_fwd_bf16_ws_bytes(int bh, int n, int d);
 // o_lo != nullptr selects the training forward, which needs ws of attn_fwd_bf16_ws_bytes bytes
@@ -53,21 +54,27 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, c
                                int topk, float sm_scale, hipStream_t st);
 
 // backward and helpers
+// D, lse2 and D 2^r (r: the dK/dV kernel's per-head dS exponent, from the maxima in the f16 workspace,
+// so launch_bwd_prep_bf16 runs first)
 hipError_t launch_bwd_pre_bf16(const uint16_t* o, const uint16_t* o_lo, const uint16_t* dout, const float* lse,
-                               float* dvec, float* lse2, int rows, int d, hipStream_t st);
+                               float* dvec, float* lse2, float* dvec_s, const void* f16ws, int bh, int n, int d,
+                               hipStream_t st);
 hipError_t launch_bwd_pre_f32(const float* o, const float* dout, float* dvec, int rows, int d, hipStream_t st);
 hipError_t launch_csc(const int32_t* idx, const int32_t* cnts, uint32_t* bitmap, int32_t* counts, int32_t* col_ptr,
                       int32_t* rows, int32_t* order, int bh, int nqb, int nkb, int topk, hipStream_t st);
-hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                                const float* lse2, const float* dvec, const int32_t* col_ptr, const int32_t* rows,
-                                const int32_t* order, uint16_t* dk, uint16_t* dv, int bh, int n, int d, int bq,
-                                int topk, float sm_scale, hipStream_t st);
-// the dQ kernel's scratch: an fp16 copy of K and per-head maxima (bwd_dq_bf16_ws_bytes bytes)
-size_t bwd_dq_bf16_ws_bytes(int bh, int n, int d);
-hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                              const float* lse2, const float* dvec, const int32_t* idx, const int32_t* cnts,
-                              uint16_t* dq, void* ws, int bh, int n, int d, int bq, int topk, float sm_scale,
-                              hipStream_t st);
+// the backward's fp16 copies of K, Q and dO and per-head maxima of |K|, |Q|, |V|, |dO|
+// (bwd_f16_ws_bytes bytes at ws), made by launch_bwd_prep_bf16 and read by both kernels below
+size_t bwd_f16_ws_bytes(int bh, int n, int d);
+const uint32_t* bwd_f16_absmax(const void* ws, int bh, int n, int d);
+hipError_t launch_bwd_prep_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout, void* ws,
+                                int bh, int n, int d, hipStream_t st);
+hipError_t launch_bwd_dkdv_bf16(const void* ws, const uint16_t* v, const uint16_t* dout, const float* lse2,
+                                const float* dvec, const int32_t* col_ptr, const int32_t* rows, const int32_t* order,
+                                uint16_t* dk, uint16_t* dv, int bh, int n, int d, int bq, int topk, float sm_scale,
+                                hipStream_t st);
+hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* v, const uint16_t* dout, const float* lse2,
+                              const float* dvec, const int32_t* idx, const int32_t* cnts, uint16_t* dq, const void* ws,
+                              int bh, int n, int d, int bq, int topk, float sm_scale, hipStream_t st);
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dout, const float* lse,
                           const float* dvec, const int32_t* idx, const int32_t* cnts, const int32_t* col_ptr,
                           const int32_t* rows, float* dq, float* dk, float* dv, int bh, int n, int d, int bq, int bk,

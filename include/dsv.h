@@ -292,7 +292,12 @@ size_t dsv_sparse_attn_bwd_workspace_size(const dsv_problem* p);
  *   o_lo              the forward's o_lo output, or NULL (then D uses o alone).
  *                     DSV_BF16 only; must be NULL for DSV_F32.
  *   dq, dk, dv        [B, H, N, d] outputs (dtype), fully overwritten
- *   workspace         >= dsv_sparse_attn_bwd_workspace_size(p) bytes
+ *   workspace         >= dsv_sparse_attn_bwd_workspace_size(p) bytes (256-byte aligned).
+ *                     DSV_BF16: the row statistics, the transposed block lists, and fp16
+ *                     copies of Q, K and dO (3 x B*H*N*d*2 bytes): every product of the
+ *                     bf16 backward runs in fp16 on copies scaled per head by powers of two
+ *                     (exact for bf16 values), with dS scaled before its fp16 rounding, and
+ *                     every scale undone exactly.  Requires sm_scale in [2^-40, 2^40].
  */
 dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
                                const void* o, const void* o_lo, const void* dout, const float* lse,

@@ -95,9 +95,15 @@ def test_select_matches_oracle_bit_exactly(b, h, nqb, nkb, k):
 # ------------------------------------------------------------------ bf16 configs, full oracle on sampled heads
 
 
-def _bf16_config_check(name, heads_checked):
+def _bf16_config_check(name, heads_checked, generator=None, storage_aware=False):
+    """storage_aware: the max-abs bounds apply to the error beyond each element's bf16 output
+    rounding (half a bf16 ulp of the reference), for inputs whose outputs exceed 16 in magnitude,
+    where that rounding alone is larger than the 3e-2 gradient bound."""
     cfg = get_config(name)
-    log(f"[parity] {name} bf16 N={cfg.seq_len} H={cfg.heads} d={cfg.head_dim} r={cfg.rank} k={cfg.topk}")
+    if generator:
+        cfg = cfg.with_(generator=generator)
+    log(f"[parity] {name} bf16 N={cfg.seq_len} H={cfg.heads} d={cfg.head_dim} r={cfg.rank} k={cfg.topk} "
+        f"inputs {cfg.generator}")
     inp = make_inputs(cfg, workers=8)
     sc = _scale(cfg.head_dim)
     # oracle indices for the checked heads; other heads get a seeded list
@@ -128,17 +134,23 @@ def _bf16_config_check(name, heads_checked):
     # forward with the oracle's indices
     o_o, lse_o = O.sparse_attn_fwd(x["q"], x["k"], x["v"], idx_o, cfg.q_block, cfg.kv_block, sc)
     og = to_f64(r["o"][:, hs])
-    err, rl2 = np.abs(og - o_o).max(), rel_l2(og, o_o)
-    log(f"[parity] {name} fwd max-abs {err:.3e} rel-L2 {rl2:.3e}")
+
+    def beyond_storage(got, ref):  # error left after each element's bf16 output rounding
+        return np.maximum(np.abs(got - ref) - (0.5 * bf16_ulp(np.abs(ref)) if storage_aware else 0.0), 0.0).max()
+
+    err, rl2 = beyond_storage(og, o_o), rel_l2(og, o_o)
+    log(f"[parity] {name} fwd max-abs {np.abs(og - o_o).max():.3e} (beyond bf16 output rounding {err:.3e}) "
+        f"rel-L2 {rl2:.3e}")
     assert err <= FWD_BF16_MAXABS and rl2 <= FWD_BF16_RELL2
     assert np.abs(to_f64(r["lse"][:, hs]) - lse_o).max() <= 1e-2
     # backward
     g_o = O.sparse_attn_bwd(x["q"], x["k"], x["v"], x["do"], idx_o, cfg.q_block, cfg.kv_block, sc)
     for nm, got, ref in zip(("dq", "dk", "dv"), r["grads"], g_o):
         gg = to_f64(got[:, hs])
-        e = np.abs(gg - ref).max()
-        log(f"[parity] {name} {nm} max-abs {e:.3e} rel-L2 {rel_l2(gg, ref):.3e}")
-        assert e <= GRAD_BF16_MAXABS
+        e = beyond_storage(gg, ref)
+        log(f"[parity] {name} {nm} max-abs {np.abs(gg - ref).max():.3e} (beyond bf16 output rounding {e:.3e}) "
+            f"max|ref| {np.abs(ref).max():.1f} rel-L2 {rel_l2(gg, ref):.3e}")
+        assert e <= GRAD_BF16_MAXABS and rel_l2(gg, ref) <= FWD_BF16_RELL2
     return cfg, inp, r, idx_fed
 
 
@@ -154,6 +166,13 @@ def test_c2_bf16_all_heads():
 
 def test_c3_bf16_sampled_heads():
     _bf16_config_check("C3", [0, 23])
+
+
+def test_c3_g2_inputs():
+    # 3D-cube token order with smooth Q and K fields: sharper, spatially coherent attention (more
+    # rows under the exact index rule, and more rescaling in the forward's online softmax).
+    # Gradients reach ~24 here, where half a bf16 ulp (0.0625) exceeds the 3e-2 bound by itself.
+    _bf16_config_check("C3", [0, 11], generator="g2", storage_aware=True)
 
 
 def test_o_residual_and_backward_without_it():
