@@ -10,16 +10,18 @@
 //   dV_kb += P^T dO_qb,  dP = dO_qb V_kb^T,  dS = P o (dP - D),  D = rowsum(dO o O),
 //   dK_kb += sm_scale dS^T Q_qb,  dQ_qb += sm_scale dS K_kb.
 //
-// gfx950 design (bf16):
+// gfx950 design (bf16 inputs and outputs):
 //  * dK/dV: one workgroup per KV block walks the list of query blocks that
 //    selected it (the transposed lists), 32 query rows at a time, with dK and dV
 //    accumulated in registers -- no atomics, deterministic;
 //  * dQ: one workgroup per query block walks its own k blocks (recomputing P and
 //    dP), accumulating dQ in registers -- again no atomics;
-//  * every GEMM is a v_mfma 32x32x16 bf16; operands that contract along a row
-//    of a gathered tile are plain LDS reads, operands that contract down its
-//    columns come from transposing LDS reads (ds_read_b64_tr_b16) of the same
-//    row-major tile, so no transposed copy of any tensor is made.
+//  * every GEMM is a v_mfma 32x32x16 (fp16 on power-of-two-scaled copies where
+//    the rounding of an operand reaches a gradient, else bf16); operands that
+//    contract along a row of a gathered tile are plain LDS reads, operands that
+//    contract down its columns come from transposing LDS reads
+//    (ds_read_b64_tr_b16) of the same row-major tile, so no transposed copy of
+//    any tensor is made.
 #include "common.hpp"
 #include "kernels.hpp"
 
