@@ -278,11 +278,18 @@ def test_single_block_and_unselected_blocks_get_zero_gradient():
 # ------------------------------------------------------------------ full-size configs, sampled outputs
 
 
-@pytest.mark.parametrize("name", ["C4", "C5", "NMAX"])
+@pytest.mark.parametrize("name", ["C4", "C5", "NMAX", "C4-G2"])
 def test_full_size_sampled(name):
     # NMAX: the largest sequence the library takes, N/Bk = 4096 KV blocks (N = 262144, a 64^3
-    # latent), at C5's head shape and 10 % density, two heads
-    cfg = get_config("C5").with_(latent=(64, 64, 64), heads=2, topk=410) if name == "NMAX" else get_config(name)
+    # latent), at C5's head shape and 10 % density, two heads.  C4-G2: C4 on the 3D-cube inputs
+    # with smooth Q and K fields (larger gradients: bounds beyond the bf16 output rounding)
+    if name == "NMAX":
+        cfg = get_config("C5").with_(latent=(64, 64, 64), heads=2, topk=410)
+    elif name == "C4-G2":
+        cfg = get_config("C4").with_(generator="g2", heads=8)
+    else:
+        cfg = get_config(name)
+    slack = (lambda ref: 0.5 * bf16_ulp(np.abs(ref))) if name == "C4-G2" else (lambda ref: 0.0)
     log(f"[parity] {name} full size N={cfg.seq_len} H={cfg.heads} k={cfg.topk}: generating inputs")
     inp = make_inputs(cfg, workers=16)
     sc = _scale(cfg.head_dim)
@@ -307,17 +314,17 @@ def test_full_size_sampled(name):
             cov = check_indices(idx_all[0, h, qb][None], s_o[None], cfg.topk)
             o_o, lse_o = O.attn_fwd_qblock(xq[rows], xk, xv, idx_fed[0, h, qb], cfg.kv_block, sc)
             og = to_f64(r["o"][0, h, rows])
-            assert np.abs(og - o_o).max() <= FWD_BF16_MAXABS and rel_l2(og, o_o) <= FWD_BF16_RELL2
+            assert (np.abs(og - o_o) - slack(o_o)).max() <= FWD_BF16_MAXABS and rel_l2(og, o_o) <= FWD_BF16_RELL2
             assert np.abs(to_f64(r["lse"][0, h, rows]) - lse_o).max() <= 1e-2
             dq_o, _, _, _ = O.attn_bwd_qblock(xq[rows], xk, xv, xdo[rows], idx_fed[0, h, qb], cfg.kv_block, sc)
-            assert np.abs(to_f64(r["grads"][0][0, h, rows]) - dq_o).max() <= GRAD_BF16_MAXABS
+            assert (np.abs(to_f64(r["grads"][0][0, h, rows]) - dq_o) - slack(dq_o)).max() <= GRAD_BF16_MAXABS
             log(f"[parity] {name} h={h} qb={qb} ok (exact-rule row: {bool(cov)})")
         kbs = rng.choice(cfg.nkb, size=2, replace=False)
         for kb in kbs:
             dk_o, dv_o = O.attn_bwd_kvblock(xq, xk, xv, xdo, idx_fed[0, h], kb, cfg.q_block, cfg.kv_block, sc)
             keys = slice(kb * cfg.kv_block, (kb + 1) * cfg.kv_block)
-            assert np.abs(to_f64(r["grads"][1][0, h, keys]) - dk_o).max() <= GRAD_BF16_MAXABS
-            assert np.abs(to_f64(r["grads"][2][0, h, keys]) - dv_o).max() <= GRAD_BF16_MAXABS
+            assert (np.abs(to_f64(r["grads"][1][0, h, keys]) - dk_o) - slack(dk_o)).max() <= GRAD_BF16_MAXABS
+            assert (np.abs(to_f64(r["grads"][2][0, h, keys]) - dv_o) - slack(dv_o)).max() <= GRAD_BF16_MAXABS
             log(f"[parity] {name} h={h} kb={kb} dK/dV ok")
 
 
