@@ -73,7 +73,30 @@ def build(jobs: int = 8, verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources for {ARCH}")
+    build_native_caller(verbose)
     return LIB
+
+
+NATIVE_SRC = os.path.join(os.path.dirname(PKG), "tests", "native", "abi_roundtrip.cpp")
+NATIVE_BIN = os.path.join(os.path.dirname(PKG), "tests", "native", "abi_roundtrip")
+
+
+def build_native_caller(verbose: bool = True) -> str:
+    """The test program that calls the C ABI from C++ (tests/native), linked against libdsv.so
+    with an rpath relative to the binary."""
+    # host code only (no kernels): the system C++ compiler against the HIP runtime
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    rpath = "$ORIGIN/" + os.path.relpath(os.path.dirname(LIB), os.path.dirname(NATIVE_BIN))
+    cmd = [shutil.which("g++") or "g++", "-O2", "-std=c++17", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include", NATIVE_SRC,
+           "-o", NATIVE_BIN + ".tmp", f"-L{os.path.dirname(LIB)}", "-ldsv", f"-L{rocm}/lib", "-lamdhip64", f"-Wl,-rpath,{rpath}",
+           f"-Wl,-rpath,{rocm}/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"native caller build failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(NATIVE_BIN + ".tmp", NATIVE_BIN)
+    if verbose:
+        print(f"built {NATIVE_BIN}")
+    return NATIVE_BIN
 
 
 if __name__ == "__main__":

@@ -188,3 +188,14 @@ def test_head_density_validates_threshold(lib):
         assert lib.dsv_head_density(ctypes.byref(p), None, ctypes.c_float(thr), FAKE, None, None) == 1
         assert "dense_above" in lib.dsv_last_error().decode()
     assert lib.dsv_head_density(ctypes.byref(p), None, ctypes.c_float(0.5), None, None, None) == 1
+
+
+def test_native_caller_is_built_and_checks_its_arguments():
+    exe = os.path.join(ROOT, "tests", "native", "abi_roundtrip")
+    if not os.path.exists(exe):
+        pytest.skip("native caller not built")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
+    r = subprocess.run([exe, "/nonexistent", "/tmp/x", "1", "1", "1024", "64", "16", "64", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 1 and "cannot read" in r.stderr
