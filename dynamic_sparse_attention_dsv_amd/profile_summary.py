@@ -38,19 +38,24 @@ KERNELS = {
     "attn_bwd_dkdv_kernel": ("attn_bwd_dkdv_bf16_kernel", ["attn_bwd.hip", "common.hpp"]),
     "attn_bwd_dq_kernel": ("attn_bwd_dq_bf16_kernel", ["attn_bwd.hip", "common.hpp"]),
 }
-BUILD_FILES = [os.path.join(HERE, "build.py")]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_KIB = 1 << 20  # 1 GiB
 
 
 def source_hash(timing_name: str) -> str | None:
-    """SHA-256 over the kernel's source files and the build script (compiler flags)."""
+    """SHA-256 over the kernel's source files and the compiler flags they are built with (the
+    common flags and the kernel file's own, from build.py; other edits of build.py do not count)."""
     if timing_name not in KERNELS:
         return None
+    from . import build as B
+
     h = hashlib.sha256()
-    for path in [os.path.join(CSRC, f) for f in KERNELS[timing_name][1]] + BUILD_FILES:
+    files = KERNELS[timing_name][1]
+    for path in [os.path.join(CSRC, f) for f in files]:
         with open(path, "rb") as fh:
             h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+    flags = [f for f in B.HIP_FLAGS if not f.startswith(B.ROOT)] + B.FILE_FLAGS.get(files[0], [])
+    h.update(b"flags\0" + " ".join(flags).encode())
     return h.hexdigest()
 
 
