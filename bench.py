@@ -132,8 +132,8 @@ def cpu_baseline(cfg, inp, target_s):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path; "
-              "the sharding design is documented with the library", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the library has no multi-GPU path; "
+              "its sharding design is documented with it", file=sys.stderr)
         sys.exit(2)
     import torch
 
