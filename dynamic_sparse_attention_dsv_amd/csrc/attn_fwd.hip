@@ -155,14 +155,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   };
   // part 2: exponentials, row sum and O^T += V^T P^T from Vc
   auto exp_pv = [&](f32x16 (&s)[2], const uint16_t* Vc) {
-    float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        s[t][vv] = fast_exp2(s[t][vv]);
-        psum += s[t][vv];
-      }
+      for (int vv = 0; vv < 16; ++vv) s[t][vv] = fast_exp2(s[t][vv]);
+    float psum = s[0][0];  // seeded with the first term: 0 + x would cost an add
+#pragma unroll
+    for (int e = 1; e < 32; ++e) psum += e < 16 ? s[0][e] : s[1][e - 16];
     l_run += psum;
     // O^T += V^T P^T: V^T operands by transposed reads of the row-major V tile (rows cc*16..:
     // byte bases + cc*32*D); P^T chunk cc = registers (cc%2)*8.. of tile cc/2.  P <= 2^8 (lazy

@@ -235,7 +235,10 @@ __device__ __forceinline__ void lds_load_rows(const uint16_t* src, uint16_t* dst
   constexpr int R = 512 / D;
   const int row = i * R + lane / (D / 8);
   const int c = ((lane % (D / 8)) ^ swz<D>(row)) & (D / 8 - 1);
-  __builtin_amdgcn_global_load_lds(src + (size_t)row * D + c * 8, dst + i * 512, 16, 0, 0);
+  // a uniform base plus a 32-bit lane offset: the load then takes its base from scalar registers
+  // and needs no 64-bit address arithmetic per lane
+  const uint32_t off = (uint32_t)(row * D + c * 8) * 2u;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + off, dst + i * 512, 16, 0, 0);
 }
 
 // Workspace sub-buffers start on 256-byte boundaries.

@@ -173,9 +173,12 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
     };
     // the block's mass for this lane's query of half h: 2^l summed over its 64 keys (two lanes)
     auto block_mass = [&](const f32x16 (&acc)[2]) {
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      // seeded with the first exponentials rather than 0: 0 + x is not folded away (it would
+      // turn -0 into +0), and these four adds per half are a tenth of the sweep's adds
+      float s0 = fast_exp2(acc[0][0]), s1 = fast_exp2(acc[0][1]), s2 = fast_exp2(acc[1][0]),
+            s3 = fast_exp2(acc[1][1]);
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
+      for (int v = 2; v < 16; v += 2) {
         s0 += fast_exp2(acc[0][v]);
         s1 += fast_exp2(acc[0][v + 1]);
         s2 += fast_exp2(acc[1][v]);
