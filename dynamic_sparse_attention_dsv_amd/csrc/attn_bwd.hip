@@ -324,7 +324,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
     const int arow = qh * 32 + sigma(c32);
     auto chunk = [&](const uint16_t* qs, const uint16_t* os, const float* ld) {
       // Fragment offsets from two bases (see row_base / tr_base); kept opaque so that they are
-      // recomputed here rather than held in registers for the whole loop.
+      // recomputed here rather than held in registers for the whole loop: this kernel sits at the
+      // 256-register limit of two waves per SIMD, and loop-invariant offsets (row_offsets /
+      // tr_offsets, as the forward and dQ kernels use) would spill.
       const int rb = opaque(row_base<D>(arow, lane));
       // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys (A rows in sigma order),
       // each k-step's operands read one step ahead
@@ -511,23 +513,27 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   const int arow = sigma(c32);
+  // loop-invariant fragment offsets (row_offsets / tr_offsets): the 32-key tile t adds t*64*D
+  // bytes to a row read, the 16-key chunk cc adds cc*32*D to a transposed read
+  int rbs[D / 16], tb0s[D / 32], tb1s[D / 32];
+  row_offsets<D>(rbs, arow, lane);
+  tr_offsets<D>(tb0s, tb1s, 0, lane);
+  auto rd_row = [&](const uint16_t* tile, int dc, int add) { return row_frag_off(tile, rbs[dc], add); };
+  auto rd_tr = [&](const uint16_t* tile, int dt, int add) { return tr_frag_off(tile, tb0s[dt], tb1s[dt], add); };
   auto block = [&](const uint16_t* Kc, const uint16_t* Vc) {
-    // one 32-key tile at a time: S^T, dP^T, dS^T, then its two 16-key chunks of dQ^T += K^T dS^T.
-    // Fragment offsets come from one base per run (row_base / tr_base), recomputed per block,
-    // and each k-step's operands are read one step ahead.
-    const int rb = opaque(row_base<D>(arow, lane));
-    const int kb0 = opaque(tr_base<D>(0, lane, 0)), kb1 = opaque(tr_base<D>(0, lane, 1));
+    // one 32-key tile at a time: S^T, dP^T, dS^T, then its two 16-key chunks of dQ^T += K^T dS^T;
+    // each k-step's operands read one step ahead
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16 s = f32x16{}, dp = f32x16{};
-      const int rt = rb + t * 64 * D;
-      bf16x8 ka = row_frag_at<D>(Kc, rt, 0), va = row_frag_at<D>(Vc, rt, 0);
+      const int rt = t * 64 * D;
+      bf16x8 ka = rd_row(Kc, 0, rt), va = rd_row(Vc, 0, rt);
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
         bf16x8 kn = ka, vn = va;
         if (dc + 1 < D / 16) {
-          kn = row_frag_at<D>(Kc, rt, dc + 1);
-          vn = row_frag_at<D>(Vc, rt, dc + 1);
+          kn = rd_row(Kc, dc + 1, rt);
+          vn = rd_row(Vc, dc + 1, rt);
         }
         s = mfma32h(as_f16x8(ka), qf[dc], s);
         dp = mfma32(va, of[dc], dp);
@@ -545,12 +551,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
         const int b0 = h2 * 8, cc = t * 2 + h2;
         const f16x8 ds = cvt8h(dp[b0], dp[b0 + 1], dp[b0 + 2], dp[b0 + 3], dp[b0 + 4], dp[b0 + 5], dp[b0 + 6],
                                dp[b0 + 7]);
-        const int o0 = kb0 + cc * 32 * D, o1 = kb1 + cc * 32 * D;
-        bf16x8 kt = tr_frag_at<D>(Kc, o0, o1, 0);
+        bf16x8 kt = rd_tr(Kc, 0, cc * 32 * D);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           bf16x8 ktn = kt;
-          if (dt + 1 < D / 32) ktn = tr_frag_at<D>(Kc, o0, o1, dt + 1);
+          if (dt + 1 < D / 32) ktn = rd_tr(Kc, dt + 1, cc * 32 * D);
           acc[dt] = mfma32h(as_f16x8(kt), ds, acc[dt]);
           kt = ktn;
         }

@@ -90,19 +90,23 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const int arow = sigma(c32);
+  // loop-invariant fragment offsets (row_offsets / tr_offsets): the 32-key tile t adds t*64*D
+  // bytes to a K read, the 16-key chunk cc adds cc*32*D to a transposed V read
+  int rbs[D / 16], vb0s[D / 32], vb1s[D / 32];
+  row_offsets<D>(rbs, arow, lane);
+  tr_offsets<D>(vb0s, vb1s, 0, lane);
 
   // S^T = K Q^T for one KV block (two 32-key tiles, K rows in sigma order: byte base + t*64*D), each
   // k-step's K operand read one step ahead; fragment offsets from one base, recomputed per block
   auto scores = [&](const uint16_t* Kc, f32x16 (&s)[2]) {
-    const int rb = opaque(row_base<D>(arow, lane));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = f32x16{};
-      bf16x8 ka = row_frag_at<D>(Kc, rb + t * 64 * D, 0);
+      bf16x8 ka = row_frag_off(Kc, rbs[0], t * 64 * D);
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
         bf16x8 kn = ka;
-        if (dc + 1 < D / 16) kn = row_frag_at<D>(Kc, rb + t * 64 * D, dc + 1);
+        if (dc + 1 < D / 16) kn = row_frag_off(Kc, rbs[dc + 1], t * 64 * D);
         s[t] = mfma32(ka, qf[dc], s[t]);
         ka = kn;
       }
@@ -168,20 +172,18 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
     // rescaling), so fp16 holds it; a bf16 rounding of P (2^-8 relative) would be fine for O
     // itself but too coarse for the backward's D = rowsum(dO * O), which the dQ product
     // multiplies by K -- the training forward therefore rounds P to fp16 against fp16 V.
-    const int vb0 = opaque(tr_base<D>(0, lane, 0)), vb1 = opaque(tr_base<D>(0, lane, 1));
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const f32x16& st = s[cc >> 1];
       const int b0 = (cc & 1) * 8;
-      const int o0 = vb0 + cc * 32 * D, o1 = vb1 + cc * 32 * D;
-      bf16x8 va = tr_frag_at<D>(Vc, o0, o1, 0);
+      bf16x8 va = tr_frag_off(Vc, vb0s[0], vb1s[0], cc * 32 * D);
       if constexpr (PV16) {
         const f16x8 ph = cvt8h(st[b0], st[b0 + 1], st[b0 + 2], st[b0 + 3], st[b0 + 4], st[b0 + 5], st[b0 + 6],
                                st[b0 + 7]);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           bf16x8 vn = va;
-          if (dt + 1 < D / 32) vn = tr_frag_at<D>(Vc, o0, o1, dt + 1);
+          if (dt + 1 < D / 32) vn = tr_frag_off(Vc, vb0s[dt + 1], vb1s[dt + 1], cc * 32 * D);
           oacc[dt] = mfma32h(as_f16x8(va), ph, oacc[dt]);
           va = vn;
         }
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           bf16x8 vn = va;
-          if (dt + 1 < D / 32) vn = tr_frag_at<D>(Vc, o0, o1, dt + 1);
+          if (dt + 1 < D / 32) vn = tr_frag_off(Vc, vb0s[dt + 1], vb1s[dt + 1], cc * 32 * D);
           oacc[dt] = mfma32(va, ph, oacc[dt]);
           va = vn;
         }

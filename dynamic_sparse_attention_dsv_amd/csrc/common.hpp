@@ -214,6 +214,42 @@ __device__ __forceinline__ bf16x8 tr_frag_at(const uint16_t* tile, int b0, int b
   return __builtin_bit_cast(bf16x8, ab);
 }
 
+// Loop-invariant fragment offsets.  Within a tile, the XOR of the swizzle only touches the
+// offset bits of the k-step (row reads) or of the 32-column tile (transposed reads), while whole
+// 16-row steps move bits above them.  So the per-step XOR can be done once, outside a loop, and
+// a 16-row (or 32-key) step becomes a plain add that folds into the read's immediate offset:
+//   row_frag(tile, row + 16*u, 16*s, lane)  == row_frag_off(tile, off[s], 32*D*u),
+//     off = row_offsets(row, lane);
+//   tr_frag(tile, k0 + 16*u, 32*t, lane)    == tr_frag_off(tile, o0[t], o1[t], 32*D*u),
+//     (o0, o1) = tr_offsets(k0, lane).
+// That costs D/16 + D/8 registers and removes one VALU op from every LDS read in the loop.
+template <int D>
+__device__ __forceinline__ void row_offsets(int (&off)[D / 16], int row, int lane) {
+  const int b = row_base<D>(row, lane);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) off[s] = b ^ (s << 5);
+}
+template <int D>
+__device__ __forceinline__ void tr_offsets(int (&o0)[D / 32], int (&o1)[D / 32], int k0, int lane) {
+  const int b0 = tr_base<D>(k0, lane, 0), b1 = tr_base<D>(k0, lane, 1);
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    o0[t] = b0 ^ (t << 6);
+    o1[t] = b1 ^ (t << 6);
+  }
+}
+__device__ __forceinline__ bf16x8 row_frag_off(const uint16_t* tile, int off, int add) {
+  return as_bf16x8(ld16(reinterpret_cast<const char*>(tile) + add + off));
+}
+__device__ __forceinline__ bf16x8 tr_frag_off(const uint16_t* tile, int o0, int o1, int add) {
+  const char* base = reinterpret_cast<const char*>(tile) + add;
+  const i16x4 a = ds_read_tr16(reinterpret_cast<const uint16_t*>(base + o0));
+  const i16x4 b = ds_read_tr16(reinterpret_cast<const uint16_t*>(base + o1));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
 // Keep a value in a register without letting the compiler see through it, so
 // that offsets derived from it are recomputed where used instead of being
 // hoisted out of a loop into registers of their own.
