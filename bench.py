@@ -109,12 +109,12 @@ def cpu_baseline(cfg, inp, target_s):
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         xq, xk, xv, xdo = (widen(inp[n][0, 0]) for n in ("q", "k", "v", "do"))
-        qlr = O.project(xq, widen(inp["wq"][0]), cfg.dtype)
+        qlr = O.project_query(xq, widen(inp["wq"][0]), sc, cfg.dtype)
         klr = O.project(xk, widen(inp["wk"][0]), cfg.dtype)
         done = 0
         while True:
             rows = slice(done * cfg.q_block, (done + 1) * cfg.q_block)
-            s = O.block_scores_qblock(qlr[rows], klr, cfg.kv_block, sc)
+            s = O.block_scores_qblock(qlr[rows], klr, cfg.kv_block, O.LN2)
             idx = O.select_topk_row(s, cfg.topk)
             O.attn_fwd_qblock(xq[rows], xk, xv, idx, cfg.kv_block, sc)
             O.attn_bwd_qblock(xq[rows], xk, xv, xdo[rows], idx, cfg.kv_block, sc)

@@ -171,7 +171,9 @@ def predict(q, k, wq, wk, *, q_block: int, kv_block: int = 64, pred_scale: Optio
     """Predicted attention mass per (query block, KV block): [B, H, N/Bq, N/Bk] float32.
 
     With ``rep_row`` the representative-row variant: the mass of the single row
-    qb * q_block + rep_row of each query block (rows sum to 1)."""
+    qb * q_block + rep_row of each query block (rows sum to 1).  ``return_projections`` also
+    returns the two operands of the logit product: Q~ = round(pred_scale * log2(e) * q @ wq) (the
+    scale applied before the one rounding) and K_lr = round(k @ wk); logit = ln(2) * <Q~_i, K_lr_j>."""
     lib = load_library()
     dev = _dev(q, k, wq, wk)
     _contig(q, k, wq, wk)

@@ -277,28 +277,32 @@ dsv_status predict_impl(const dsv_problem* p, const void* q, const void* k, cons
   if (workspace_bytes < w.total)
     return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "predict workspace needs " + std::to_string(w.total) + " bytes");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // The query projection carries the logit scale in base-2 units, applied before its one rounding:
+  // Q~ = rho(pred_scale log2(e) Q Wq), so <Q~_i, K_lr_j> is the logit l_ij / ln 2 and the score
+  // kernels take 2^<Q~_i, K_lr_j> (the fp32 kernels as exp(ln 2 <Q~_i, K_lr_j>)).
+  const float q_scale = o.ps * 1.4426950408889634f;  // log2(e)
   if (o.dtype == DSV_BF16) {
     uint16_t* qlr = at<uint16_t>(workspace, w.qlr);
     uint16_t* klr = at<uint16_t>(workspace, w.klr);
     TRY_HIP(dsv::launch_proj_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(wq), qlr, o.bh(), o.n,
-                                  o.h, o.d, o.r, st), "proj_kernel(q)");
+                                  o.h, o.d, o.r, q_scale, st), "proj_kernel(q)");
     TRY_HIP(dsv::launch_proj_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(wk), klr, o.bh(), o.n,
-                                  o.h, o.d, o.r, st), "proj_kernel(k)");
+                                  o.h, o.d, o.r, 1.f, st), "proj_kernel(k)");
     TRY_HIP(dsv::launch_scores_bf16(qlr, klr, at<float>(workspace, w.scratch), block_scores, o.bh(), o.n, o.nkb(),
-                                    o.r, o.bq, o.ps, rep, st), "scores_kernel");
+                                    o.r, o.bq, rep, st), "scores_kernel");
   } else {
     float* qlr = at<float>(workspace, w.qlr);
     float* klr = at<float>(workspace, w.klr);
     TRY_HIP(dsv::launch_proj_f32(static_cast<const float*>(q), static_cast<const float*>(wq), qlr, o.bh(), o.n, o.h,
-                                 o.d, o.r, st), "proj_kernel(q)");
+                                 o.d, o.r, q_scale, st), "proj_kernel(q)");
     TRY_HIP(dsv::launch_proj_f32(static_cast<const float*>(k), static_cast<const float*>(wk), klr, o.bh(), o.n, o.h,
-                                 o.d, o.r, st), "proj_kernel(k)");
+                                 o.d, o.r, 1.f, st), "proj_kernel(k)");
     if (rep < 0)
       TRY_HIP(dsv::launch_scores_f32(qlr, klr, at<float>(workspace, w.lse), block_scores, o.bh(), o.n, o.r, o.bq,
-                                     o.bk, o.ps, st), "scores_kernel");
+                                     o.bk, 0.6931471805599453f /* ln 2 */, st), "scores_kernel");
     else
       TRY_HIP(dsv::launch_rep_scores_f32(qlr, klr, at<float>(workspace, w.lse), block_scores, o.bh(), o.n, o.r,
-                                         o.bq, o.bk, o.ps, rep, st), "scores_kernel");
+                                         o.bq, o.bk, 0.6931471805599453f /* ln 2 */, rep, st), "scores_kernel");
   }
   return DSV_OK;
 }

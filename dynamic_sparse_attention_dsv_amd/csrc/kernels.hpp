@@ -10,16 +10,18 @@
 namespace dsv {
 
 // predictor
+// out = rho(scale * x w): the query side passes scale = pred_scale * log2(e), the key side 1
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* w, uint16_t* out, int bh, int n, int heads,
-                            int d, int r, hipStream_t st);
+                            int d, int r, float scale, hipStream_t st);
 hipError_t launch_proj_f32(const float* x, const float* w, float* out, int bh, int n, int heads, int d, int r,
-                           hipStream_t st);
+                           float scale, hipStream_t st);
 int score_slots(int items);
 size_t score_scratch_bytes(int items, int nkb);
 int score_items(int bh, int n, int bq, bool representative);
-// rep < 0: block scores (every row of a query block); rep >= 0: the masses of row qb * bq + rep
+// rep < 0: block scores (every row of a query block); rep >= 0: the masses of row qb * bq + rep.
+// qlr is the scaled query projection: <qlr_i, klr_j> is the logit in log2 units.
 hipError_t launch_scores_bf16(const uint16_t* qlr, const uint16_t* klr, float* scratch, float* scores, int bh,
-                              int n, int nkb, int r, int bq, float pred_scale, int rep, hipStream_t st);
+                              int n, int nkb, int r, int bq, int rep, hipStream_t st);
 hipError_t launch_rep_scores_f32(const float* qlr, const float* klr, float* lse, float* scores, int bh, int n,
                                  int r, int bq, int bk, float pred_scale, int rep, hipStream_t st);
 hipError_t launch_scores_f32(const float* qlr, const float* klr, float* lse, float* scores, int bh, int n, int r,

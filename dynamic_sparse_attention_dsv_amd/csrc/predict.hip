@@ -13,11 +13,13 @@
 //
 // gfx950 design (bf16):
 //  * projection: one MFMA 16x16x32 GEMM per 16-row tile, W^T held in registers;
+//    the query side is scaled by pred_scale * log2(e) before its one rounding to
+//    bf16, so that the query operand Q~ = bf16(pred_scale log2(e) Q W^Q_lr)
+//    against K_lr = bf16(K W^K_lr) gives each logit in log2 units;
 //  * scores: persistent workgroups of 4 waves; each work item is 256 query rows
-//    of one head, 64 per wave.  Each wave sweeps every KV block once: 32x32x16
-//    MFMAs with the scale folded into the query operand produce the logits in
-//    log2 units, and 2^l summed over the block's 64 keys gives the row's block
-//    mass.  Block masses go to a per-workgroup scratch of nkb x 256 floats
+//    of one head, 64 per wave.  Each wave sweeps every KV block once: one bf16
+//    32x32x16 MFMA product of Q~ and K_lr gives the logits in log2 units, and 2^l
+//    summed over the block's 64 keys gives the row's block mass.  Block masses go to a per-workgroup scratch of nkb x 256 floats
 //    (never N x N); the row totals are their sums, and after the sweep the same
 //    workgroup divides and sums them into block scores.  The sweep is bound by
 //    the vector ALU (one exp2 and one add per logit), not by MFMA or memory.
@@ -31,8 +33,9 @@ namespace dsv {
 template <int D, int R>
 __global__ __launch_bounds__(256) void proj_bf16_kernel(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ w,
-                                                        uint16_t* __restrict__ out, int n, int heads) {
+                                                        uint16_t* __restrict__ out, int n, int heads, float scale) {
   // grid: (ceil(n/256), B*H). x, out: [BH, n, D] / [BH, n, R]; w: [H, D, R].
+  // out = bf16(scale * x w): the fp32 product is scaled, then rounded once (scale = 1: exact no-op).
   const int bh = blockIdx.y;
   const int h = bh % heads;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(const uint16_t* __restri
 #pragma unroll
       for (int kc = 0; kc < D / 32; ++kc) acc = mfma16(wa[rt][kc], xb8[kc], acc);
       // D layout: lane holds col (row index) c16, registers rows r = rt*16 + g*4 + v
-      u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      u32x2 pk = {pack_bf16x2(acc[0] * scale, acc[1] * scale), pack_bf16x2(acc[2] * scale, acc[3] * scale)};
       *reinterpret_cast<u32x2*>(ob + (size_t)row * R + rt * 16 + g * 4) = pk;
     }
   }
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------- projection (f32)
 
 __global__ void proj_f32_kernel(const float* __restrict__ x, const float* __restrict__ w,
-                                float* __restrict__ out, int n, int d, int r, int heads) {
+                                float* __restrict__ out, int n, int d, int r, int heads, float scale) {
   // grid: (ceil(n*r/256), B*H)
   const int bh = blockIdx.y;
   const int h = bh % heads;
@@ -83,7 +86,7 @@ __global__ void proj_f32_kernel(const float* __restrict__ x, const float* __rest
   const float* wc = w + (size_t)h * d * r + col;
   float acc = 0.f;
   for (int c = 0; c < d; ++c) acc = fmaf(xr[c], wc[(size_t)c * r], acc);
-  out[((size_t)bh * n + row) * r + col] = acc;
+  out[((size_t)bh * n + row) * r + col] = acc * scale;
 }
 
 // ---------------------------------------------------------------- scores (bf16, MFMA)
@@ -98,16 +101,15 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ klr,
                                                           float* __restrict__ scratch,
                                                           float* __restrict__ scores, int n, int nkb,
-                                                          int items, float pc, int rep) {
-  // qlr, klr: [BH, n, R] bf16.  scratch: gridDim.x slots of [nkb][256] float.
-  // scores: [BH, n/BQ, nkb].  pc = pred_scale * log2(e).
+                                                          int items, int rep) {
+  // qlr, klr: [BH, n, R] bf16, qlr the scaled query projection Q~ (logits <Q~_i, K_lr_j> in log2
+  // units).  scratch: gridDim.x slots of [nkb][256] float.  scores: [BH, n/BQ, nkb].
   // Each wave owns 64 query rows (two 32-row halves): every K_lr fragment it loads feeds
   // two MFMA tiles, halving the K_lr traffic per logit.
   //
-  // The scale pc is folded into the MFMA: the query operand is pc * Q_lr as two bf16 parts
-  // (hi = bf16(pc q), lo = bf16(pc q - hi); together exact to ~2^-18), so each MFMA result is
-  // already a logit in log2 units.  The fast sweep then takes 2^logit with no shift and sums
-  // block masses linearly: one exp and one add per logit.  That is exact (up to rounding) for
+  // Each MFMA result is already a logit in log2 units (the projection carries the scale), so the
+  // fast sweep takes 2^logit with no shift and sums block masses linearly: one exp and one add per
+  // logit.  That is exact (up to rounding) for
   // rows whose total mass T = sum_j 2^l_ij lies in [2^-100, fp32 max]; an item holding any
   // other row is redone with a per-block maximum in the log domain.
   static_assert(kScoreRows % BQ == 0 && BQ % 64 == 0, "BQ must be 64 or 128");
@@ -128,26 +130,14 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
     // to a valid one and its scores are never written)
     auto qrow_of = [&](int i) { return REP ? min(row0 + i, nqb - 1) * BQ + rep : row0 + i; };
     const uint16_t* kh = klr + (size_t)bh * n * R;
-    // B operands = (pc Q_lr)^T as hi and lo parts for the wave's two 32-row halves: lane holds
-    // its query row, 8 consecutive r per chunk
-    bf16x8 qh[2][NC], ql[2][NC];
+    // B operands = Q~^T for the wave's two 32-row halves: lane holds its query row, 8 consecutive
+    // r per chunk
+    bf16x8 qh[2][NC];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint16_t* qrow = qlr + ((size_t)bh * n + qrow_of(wave * 64 + h * 32 + c32)) * R;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x4 raw = ld16(qrow + c * 16 + g * 8);
-        float y[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[2 * e] = __uint_as_float(raw[e] << 16) * pc;
-          y[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u) * pc;
-        }
-        qh[h][c] = cvt8(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lo[e] = y[e] - (float)qh[h][c][e];
-        ql[h][c] = cvt8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
-      }
+      for (int c = 0; c < NC; ++c) qh[h][c] = as_bf16x8(ld16(qrow + c * 16 + g * 8));
     }
     // A operands (K_lr rows, 8 consecutive r) of one KV block: 2 tiles x NC chunks
     auto load_k = [&](int kb, u32x4 (&ka)[2][NC]) {
@@ -165,10 +155,7 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
         for (int t = 0; t < 2; ++t) {
           acc[h][t] = f32x16{};
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            acc[h][t] = mfma32(as_bf16x8(ka[t][c]), qh[h][c], acc[h][t]);
-            acc[h][t] = mfma32(as_bf16x8(ka[t][c]), ql[h][c], acc[h][t]);
-          }
+          for (int c = 0; c < NC; ++c) acc[h][t] = mfma32(as_bf16x8(ka[t][c]), qh[h][c], acc[h][t]);
         }
     };
     // the block's mass for this lane's query of half h: 2^l summed over its 64 keys (two lanes)
@@ -422,11 +409,11 @@ hipError_t launch_rep_scores_f32(const float* qlr, const float* klr, float* lse,
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* w, uint16_t* out, int bh, int n, int heads,
-                            int d, int r, hipStream_t st) {
+                            int d, int r, float scale, hipStream_t st) {
   dim3 grid((n + 255) / 256, bh);
 #define PROJ(D_, R_)                                                                                  \
   if (d == D_ && r == R_) {                                                                           \
-    hipLaunchKernelGGL((proj_bf16_kernel<D_, R_>), grid, dim3(256), 0, st, x, w, out, n, heads);      \
+    hipLaunchKernelGGL((proj_bf16_kernel<D_, R_>), grid, dim3(256), 0, st, x, w, out, n, heads, scale); \
     return hipGetLastError();                                                                         \
   }
   PROJ(64, 16) PROJ(64, 32) PROJ(128, 16) PROJ(128, 32)
@@ -435,9 +422,9 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* w, uint16_t* out,
 }
 
 hipError_t launch_proj_f32(const float* x, const float* w, float* out, int bh, int n, int heads, int d,
-                           int r, hipStream_t st) {
+                           int r, float scale, hipStream_t st) {
   dim3 grid((unsigned)(((size_t)n * r + 255) / 256), bh);
-  hipLaunchKernelGGL(proj_f32_kernel, grid, dim3(256), 0, st, x, w, out, n, d, r, heads);
+  hipLaunchKernelGGL(proj_f32_kernel, grid, dim3(256), 0, st, x, w, out, n, d, r, heads, scale);
   return hipGetLastError();
 }
 
@@ -460,19 +447,18 @@ int score_items(int bh, int n, int bq, bool representative) {
 }
 
 hipError_t launch_scores_bf16(const uint16_t* qlr, const uint16_t* klr, float* scratch, float* scores,
-                              int bh, int n, int nkb, int r, int bq, float pred_scale, int rep, hipStream_t st) {
+                              int bh, int n, int nkb, int r, int bq, int rep, hipStream_t st) {
   const bool representative = rep >= 0;
   const int items = score_items(bh, n, bq, representative);
   const int slots = score_slots(items);
-  const float pc = pred_scale * kLog2e;
 #define SC(R_, BQ_)                                                                                           \
   if (r == R_ && bq == BQ_) {                                                                                 \
     if (representative)                                                                                       \
       hipLaunchKernelGGL((scores_bf16_kernel<R_, BQ_, true>), dim3(slots), dim3(256), 0, st, qlr, klr, scratch, \
-                         scores, n, nkb, items, pc, rep);                                                     \
+                         scores, n, nkb, items, rep);                                                         \
     else                                                                                                      \
       hipLaunchKernelGGL((scores_bf16_kernel<R_, BQ_, false>), dim3(slots), dim3(256), 0, st, qlr, klr,         \
-                         scratch, scores, n, nkb, items, pc, 0);                                              \
+                         scratch, scores, n, nkb, items, 0);                                                  \
     return hipGetLastError();                                                                                 \
   }
   SC(16, 64) SC(16, 128) SC(32, 64) SC(32, 128)

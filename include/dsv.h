@@ -109,8 +109,10 @@ size_t dsv_predict_workspace_size(const dsv_problem* p);
  * dsv_predict -- low-rank sparsity predictor ([es] §2.A; [de] §2.A;
  * [de] §2.B, the fused matmul and top-k; [de] §2.B query grouping).
  *
- *   Q_lr = round(Q Wq[h]),  K_lr = round(K Wk[h])        (round = to dtype, RNE)
- *   l_ij = pred_scale * <Q_lr_i, K_lr_j>                  (all j: no causal mask)
+ *   Q~   = round(pred_scale log2(e) Q Wq[h]),  K_lr = round(K Wk[h])
+ *                                  (round = once, to dtype, RNE; fp32 keeps them exact)
+ *   l_ij = ln(2) <Q~_i, K_lr_j>    (= pred_scale <Q Wq[h], K_lr_j> up to the rounding;
+ *                                   all j: no causal mask)
  *   P_ij = exp(l_ij) / sum_j' exp(l_ij')                  (row softmax over all N keys)
  *   block_scores[b,h,qb,kb] = sum_{i in qb} sum_{j in kb} P_ij
  * i.e. the predicted attention mass of query block qb on KV block kb, summed
@@ -120,7 +122,7 @@ size_t dsv_predict_workspace_size(const dsv_problem* p);
  *   q, k          [B, H, N, d]   inputs
  *   wq, wk        [H, d, r]      predictor weights
  *   workspace     >= dsv_predict_workspace_size(p) bytes, caller-owned scratch.
- *                 On return its first bytes hold Q_lr then K_lr, each
+ *                 On return its first bytes hold Q~ then K_lr, each
  *                 [B, H, N, r] in dtype (a by-product callers may inspect).
  *   block_scores  [B, H, N/Bq, N/Bk] float32 output.
  */

@@ -30,8 +30,12 @@ Readings where the pages are silent, ambiguous or garbled:
      with W in R^{d x r};
   R2 predicted logits are pred_scale * <Q_lr_i, K_lr_j> (pred_scale defaults to
      1/sqrt(d)); there is no causal mask (video DiT self-attention is full);
-  R3 Q_lr and K_lr are rounded to the run's storage dtype (bf16: nearest, ties
-     to even) before the logit product; in fp32 runs they are kept exact;
+  R3 the two operands of the logit product are rounded once to the run's
+     storage dtype (bf16: nearest, ties to even; fp32 runs keep them exact).  The
+     query operand carries the logit scale, in base-2 units, before that rounding:
+     Q~ = rho(pred_scale * log2(e) * Q W^Q_lr), K_lr = rho(K W^K_lr), and the
+     logit is l_ij = ln(2) * <Q~_i, K_lr_j> (in fp32 runs exactly R2's
+     pred_scale * <Q_lr_i, K_lr_j>);
   R4-R5 a block score is the predicted softmax mass of the query block on the KV
      block, SUMMED over the block's Bq rows (each score row sums to Bq);
   R6 every query row of a group contributes (the Spanish page's joint
@@ -113,6 +117,20 @@ def project(x: np.ndarray, w: np.ndarray, dtype: str) -> np.ndarray:
     return rho(np.asarray(x, np.float64) @ np.asarray(w, np.float64), dtype)
 
 
+LOG2E = 1.0 / math.log(2.0)
+LN2 = math.log(2.0)
+
+
+def project_query(x: np.ndarray, w: np.ndarray, pred_scale: float, dtype: str) -> np.ndarray:
+    """Query operand of the predictor (R1-R3): rho(pred_scale * log2(e) * (x @ w)).
+
+    The logit scale in base-2 units is applied before the one rounding, so the
+    logit of R2 is ln(2) * <Q~_i, K_lr_j>: pass ``LN2`` as the scale of the score
+    functions below when they are given Q~.
+    """
+    return rho(pred_scale * LOG2E * (np.asarray(x, np.float64) @ np.asarray(w, np.float64)), dtype)
+
+
 # --------------------------------------------------------------------------
 # 2. predicted block mass ([de] §2.A, §2.B; [es] §2.A-B)
 # --------------------------------------------------------------------------
@@ -146,7 +164,8 @@ def block_scores_head(q_lr: np.ndarray, k_lr: np.ndarray, bq: int, bk: int, pred
 def predict(q, k, wq, wk, bq: int, bk: int, pred_scale: float, dtype: str):
     """Full predictor over [B, H, N, d] inputs and [H, d, r] weights.
 
-    Returns (scores [B, H, nqb, nkb], q_lr [B, H, N, r], k_lr [B, H, N, r]).
+    Returns (scores [B, H, nqb, nkb], q~ [B, H, N, r], k_lr [B, H, N, r]), q~ the
+    scaled query operand of R3 (logits ln(2) <q~_i, k_lr_j>).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -158,9 +177,9 @@ def predict(q, k, wq, wk, bq: int, bk: int, pred_scale: float, dtype: str):
     scores = np.empty((b_, h_, n // bq, n // bk))
     for b in range(b_):
         for h in range(h_):
-            q_lr[b, h] = project(q[b, h], wq[h], dtype)
+            q_lr[b, h] = project_query(q[b, h], wq[h], pred_scale, dtype)
             k_lr[b, h] = project(k[b, h], wk[h], dtype)
-            scores[b, h] = block_scores_head(q_lr[b, h], k_lr[b, h], bq, bk, pred_scale)
+            scores[b, h] = block_scores_head(q_lr[b, h], k_lr[b, h], bq, bk, LN2)
     return scores, q_lr, k_lr
 
 

@@ -273,6 +273,33 @@ def test_score_rows_sum_to_block_size_and_are_nonnegative():
     np.testing.assert_allclose(s.sum(-1), bq, rtol=0, atol=1e-10)
 
 
+def test_bf16_query_operand_carries_the_scale_before_its_rounding():
+    # R3: the query operand is bf16(pred_scale * log2(e) * Q Wq).  With pred_scale * log2(e) a
+    # power of two the scaling commutes with the rounding, so the bf16 predictor must equal the
+    # textbook predicted mass of pred_scale * <bf16(Q Wq), bf16(K Wk)> (float64 torch softmax over
+    # every key, then block sums; bf16 rounding by torch's own cast).  This catches a scale applied
+    # twice or not at all, logits left in base-2 units, and a rounding in the wrong place.
+    rng = _rng(16)
+    n, d, r, bq, bk = 512, 32, 8, 64, 64
+    q, k = rng.standard_normal((1, 2, n, d)) * 2, rng.standard_normal((1, 2, n, d)) * 2
+    wq, wk = rng.standard_normal((2, d, r)), rng.standard_normal((2, d, r))
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).double()
+    ps = 0.125 * math.log(2.0)  # pred_scale * log2(e) = 2^-3
+    s, qt, kl = O.predict(q, k, wq, wk, bq, bk, ps, "bf16")
+    for h in range(2):
+        ql, kk = bf(q[0, h] @ wq[h]), bf(k[0, h] @ wk[h])
+        p = torch.softmax(ps * ql @ kk.T, dim=-1)
+        mass = p.reshape(n // bq, bq, n // bk, bk).sum(dim=(1, 3)).numpy()
+        np.testing.assert_allclose(s[0, h], mass, rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(qt[0, h], (0.125 * ql).numpy())
+    # any other scale: the operand is the rounding of the scaled product (not the scaled rounding)
+    ps = 0.3
+    _, qt, _ = O.predict(q, k, wq, wk, bq, bk, ps, "bf16")
+    y = ps / math.log(2.0) * (q[0, 0] @ wq[0])
+    np.testing.assert_array_equal(qt[0, 0], bf(y).numpy())
+    assert np.any(qt[0, 0] != ps / math.log(2.0) * bf(q[0, 0] @ wq[0]).numpy())
+
+
 def test_representative_scores_are_the_one_row_softmax():
     rng = _rng(14)
     n, r, bq, bk = 256, 8, 64, 32

@@ -114,11 +114,14 @@ def _bf16_config_check(name, heads_checked, generator=None, storage_aware=False)
     idx_fed = seeded_idx(7, (cfg.batch, cfg.heads), cfg.nqb, cfg.nkb, cfg.topk)
     idx_fed[:, hs] = idx_o
     r = _run_gpu_path(cfg, inp, idx_fed=idx_fed)
-    # projections: the GPU rounds an fp32 accumulation to bf16, the oracle the exact product;
-    # they may differ by the fp32 summation error (<= d * 2^-24 * sum|x w|) plus one bf16 ulp
+    # projections: the GPU rounds an fp32 accumulation (the query side scaled by
+    # pred_scale * log2(e) in fp32) to bf16, the oracle the exact scaled product; they may differ by
+    # the fp32 summation error (<= d * 2^-24 * sum|x w|, scaled), the fp32 rounding of the scaling
+    # and one bf16 ulp
     qg, kg = to_f64(r["qlr"][:, hs]), to_f64(r["klr"][:, hs])
-    for got, ref, xs, ws in ((qg, qlr_o, x["q"], x["wq"]), (kg, klr_o, x["k"], x["wk"])):
-        bound = bf16_ulp(np.maximum(np.abs(got), np.abs(ref))) + cfg.head_dim * 2.0 ** -24 * np.einsum(
+    for got, ref, xs, ws, s_ in ((qg, qlr_o, x["q"], x["wq"], sc * O.LOG2E), (kg, klr_o, x["k"], x["wk"], 1.0)):
+        mag = np.maximum(np.abs(got), np.abs(ref))
+        bound = bf16_ulp(mag) + 2.0 ** -24 * mag + s_ * cfg.head_dim * 2.0 ** -24 * np.einsum(
             "bhnd,hdr->bhnr", np.abs(xs), np.abs(ws))
         assert np.all(np.abs(got - ref) <= bound * 1.0001)
         assert (got != ref).mean() < 1e-2, (got != ref).mean()
@@ -126,7 +129,7 @@ def _bf16_config_check(name, heads_checked, generator=None, storage_aware=False)
     sg = to_f64(r["scores"][:, hs])
     for bi in range(cfg.batch):
         for j in range(len(hs)):
-            ref = O.block_scores_head(qg[bi, j], kg[bi, j], cfg.q_block, cfg.kv_block, sc)
+            ref = O.block_scores_head(qg[bi, j], kg[bi, j], cfg.q_block, cfg.kv_block, O.LN2)
             np.testing.assert_allclose(sg[bi, j], ref, rtol=2e-4, atol=2e-5)
     np.testing.assert_allclose(to_f64(r["scores"]).sum(-1), cfg.q_block, rtol=1e-4)
     cov = check_indices(r["idx"][:, hs].cpu().numpy(), scores_o, cfg.topk)
@@ -306,11 +309,11 @@ def test_full_size_sampled(name):
     rng = np.random.default_rng(5)
     for h in (0, cfg.heads - 1):
         xq, xk, xv, xdo = (widen(inp[n][0, h]) for n in ("q", "k", "v", "do"))
-        qlr_o = O.project(xq, widen(inp["wq"][h]), "bf16")
+        qlr_o = O.project_query(xq, widen(inp["wq"][h]), sc, "bf16")
         klr_o = O.project(xk, widen(inp["wk"][h]), "bf16")
         for qb in rng.choice(cfg.nqb, size=3, replace=False):
             rows = slice(qb * cfg.q_block, (qb + 1) * cfg.q_block)
-            s_o = O.block_scores_qblock(qlr_o[rows], klr_o, cfg.kv_block, sc)
+            s_o = O.block_scores_qblock(qlr_o[rows], klr_o, cfg.kv_block, O.LN2)
             cov = check_indices(idx_all[0, h, qb][None], s_o[None], cfg.topk)
             o_o, lse_o = O.attn_fwd_qblock(xq[rows], xk, xv, idx_fed[0, h, qb], cfg.kv_block, sc)
             og = to_f64(r["o"][0, h, rows])
@@ -353,7 +356,7 @@ def test_predictor_extreme_logits_use_the_exact_fallback(case):
     scores, qlr, klr = dsv.predict(t["q"], t["k"], t["w"], t["w"], q_block=bq, kv_block=bk, return_projections=True)
     torch.cuda.synchronize()
     sg = to_f64(scores)[0, 0]
-    ref = O.block_scores_head(to_f64(qlr)[0, 0], to_f64(klr)[0, 0], bq, bk, 1 / 8)
+    ref = O.block_scores_head(to_f64(qlr)[0, 0], to_f64(klr)[0, 0], bq, bk, O.LN2)  # qlr: the scaled Q~
     assert np.isfinite(sg).all()
     np.testing.assert_allclose(sg, ref, rtol=2e-4, atol=2e-5)
     assert np.all(sg[:, 5] > 0.99 * bq)  # block 5 takes essentially all the mass

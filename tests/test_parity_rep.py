@@ -37,11 +37,11 @@ def test_representative_scores_and_selection(name, rep):
     k = min(cfg.topk, cfg.nkb)
     idx = dsv.select_topk(scores, k, q_block=cfg.q_block, kv_block=cfg.kv_block)
     torch.cuda.synchronize()
-    sc = 1.0 / np.sqrt(cfg.head_dim)
     sg, ig = to_f64(scores), idx.cpu().numpy()
     covered = []
     for h in range(cfg.heads):
-        ref = O.representative_scores_head(to_f64(qlr)[0, h], to_f64(klr)[0, h], cfg.q_block, cfg.kv_block, sc, rep=rep)
+        ref = O.representative_scores_head(to_f64(qlr)[0, h], to_f64(klr)[0, h], cfg.q_block, cfg.kv_block, O.LN2,
+                                           rep=rep)  # qlr: the scaled query operand Q~
         np.testing.assert_allclose(sg[0, h], ref, rtol=2e-4, atol=1e-6)
         np.testing.assert_allclose(sg[0, h].sum(-1), 1.0, rtol=1e-4)
         ref_idx, gap = O.select_topk(ref, k), O.topk_gap(ref, k)
