@@ -312,10 +312,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
     auto q0_of = [&](int j) { return list[j / SUBS] * BQ + (j % SUBS) * QR; };
     // asynchronous gather of a 64-row chunk (Q and dO tiles, lse2 and D) into one buffer set
     auto issue = [&](int q0, uint16_t* qd, uint16_t* od, float* ld) {
-      for (int i = wave; i < 2 * NT; i += 4) {
-        const bool iso = i >= NT;
-        const int ii = iso ? i - NT : i;
-        lds_load_rows<D>((iso ? o16 : q16) + head + (size_t)q0 * D, iso ? od : qd, ii, lane);
+      // instruction wave + 4m: Q rows for m < NT/4, dO rows after (compile-time per m); the lane
+      // offset is computed once for the batch
+      const int ln = opaque(lane);
+#pragma unroll
+      for (int m = 0; m < 2 * NT / 4; ++m) {
+        const bool iso = m >= NT / 4;
+        const int ii = wave + 4 * (iso ? m - NT / 4 : m);
+        lds_load_rows<D>((iso ? o16 : q16) + head + (size_t)q0 * D, iso ? od : qd, ii, ln);
       }
       if (wave == 3 && lane < 32)  // lanes 0-15: 64 lse2 values, lanes 16-31: 64 D values
         __builtin_amdgcn_global_load_lds((lane < 16 ? lse2 : dvec) + (size_t)bh * n + q0 + (lane & 15) * 4, ld, 16,
@@ -472,10 +476,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
   const int nkb = n / 64;
   auto blk_at = [&](int j) { return min(max(blocks[j], 0), nkb - 1); };  // clamp out-of-range indices
   auto issue = [&](int blk, uint16_t* kd, uint16_t* vd) {  // asynchronous gather of a K and V block
-    for (int i = wave; i < NI; i += WAVES) {
-      const bool isv = i >= NI / 2;
-      const int ii = isv ? i - NI / 2 : i;
-      lds_load_rows<D>((isv ? v : k16) + head + (size_t)blk * 64 * D, isv ? vd : kd, ii, lane);
+    // instruction wave + WAVES m: K rows for m < NI/2/WAVES, V rows after (compile-time per m);
+    // the lane offset is computed once for the batch
+    const int ln = opaque(lane);
+#pragma unroll
+    for (int m = 0; m < NI / WAVES; ++m) {
+      const bool isv = m >= NI / 2 / WAVES;
+      const int ii = wave + WAVES * (isv ? m - NI / 2 / WAVES : m);
+      lds_load_rows<D>((isv ? v : k16) + head + (size_t)blk * 64 * D, isv ? vd : kd, ii, ln);
     }
   };
   const int sK = f16_shift(absmax[bh]), sQ = f16_shift(absmax[bh_total + bh]);

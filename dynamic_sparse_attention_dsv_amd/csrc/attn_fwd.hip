@@ -61,9 +61,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
   // the next barrier)
   static_assert((NI / 2) % WAVES == 0, "each wave issues the same number of copies");
   auto issue = [&](const uint16_t* src, int blk, uint16_t* dst) {
+    const int ln = opaque(lane);  // the copies' lane offset is computed here, once per batch
 #pragma unroll
     for (int m = 0; m < NI / 2 / WAVES; ++m)
-      lds_load_rows<D>(src + head + (size_t)blk * 64 * D, dst, wave + m * WAVES, lane);
+      lds_load_rows<D>(src + head + (size_t)blk * 64 * D, dst, wave + m * WAVES, ln);
   };
 
   // Q^T as the B operand of S^T = K Q^T: lane holds its query row, 8 consecutive d per 16-wide chunk

@@ -266,15 +266,26 @@ __device__ __forceinline__ int opaque(int x) {
 // stride D elements); `dst` is the LDS tile; `i` is the instruction index.
 // The data is visible after the next __syncthreads() (the compiler waits for
 // the outstanding loads before the barrier).
+//
+// The address is a uniform base (the tile's row i*R, in scalar registers) plus the lane's byte
+// offset within those R rows.  The swizzle repeats every 16 rows, so that offset depends on i only
+// modulo 16/R: a batch of copies whose instruction indices step by a multiple of 16/R computes it
+// once.  Callers inside a loop pass the lane id through opaque() once per batch: the offset is then
+// recomputed per batch (three VALU ops) rather than hoisted out of the loop, where the compiler
+// would hold it as a 64-bit value and give up the scalar-base form of the load.
+template <int D>
+__device__ __forceinline__ uint32_t lds_lane_off(int i, int lane) {
+  constexpr int R = 512 / D, P = 16 / R;
+  const int row = (i & (P - 1)) * R + lane / (D / 8);  // the row modulo 16
+  const int c = ((lane % (D / 8)) ^ swz<D>(row)) & (D / 8 - 1);
+  return (uint32_t)((lane / (D / 8)) * D + c * 8) * 2u;
+}
 template <int D>
 __device__ __forceinline__ void lds_load_rows(const uint16_t* src, uint16_t* dst, int i, int lane) {
   constexpr int R = 512 / D;
-  const int row = i * R + lane / (D / 8);
-  const int c = ((lane % (D / 8)) ^ swz<D>(row)) & (D / 8 - 1);
-  // a uniform base plus a 32-bit lane offset: the load then takes its base from scalar registers
-  // and needs no 64-bit address arithmetic per lane
-  const uint32_t off = (uint32_t)(row * D + c * 8) * 2u;
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + off, dst + i * 512, 16, 0, 0);
+  const char* rows = reinterpret_cast<const char*>(src) + (size_t)i * R * D * 2;
+  const uint32_t off = lds_lane_off<D>(i, lane);
+  __builtin_amdgcn_global_load_lds(rows + off, dst + i * 512, 16, 0, 0);
 }
 
 // Workspace sub-buffers start on 256-byte boundaries.
