@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--mass-tau", type=float, default=0.1,
                     help="tau of the mass-threshold leg (kmax = 2k); with the random-init predictor's near-uniform "
                          "scores, 0.1 selects about the headline density")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the measured-peak probes (MFMA bf16/fp16, exp, HBM copy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a reference for HBM byte counters)")
     return ap.parse_args()
@@ -248,6 +250,23 @@ def main():
             pk, scale, unit = peaks[bnd]
             rates[n] = {"bound": bnd, "achieved": work / s / scale, "unit": unit, "frac": work / s / scale / pk}
 
+    # measured peaks (after the timed region): the rates this device sustains for the bounding
+    # operations, beside the vendor figures
+    measured = None
+    if not a.no_probe:
+        log("[bench] measured peaks (MFMA bf16/fp16, exp, HBM copy probes)")
+        measured = {"mfma_bf16_tflops": dsv.peak_probe("mfma_bf16") / 1e12,
+                    "mfma_f16_tflops": dsv.peak_probe("mfma_f16") / 1e12,
+                    "exp_texp_per_s": dsv.peak_probe("exp_f32") / 1e12,
+                    "hbm_copy_gbs": dsv.peak_probe("hbm_copy") / 1e9,
+                    "hbm_read_gbs": dsv.peak_probe("hbm_read") / 1e9}
+        log(f"[bench] measured peaks: {measured}")
+        mpk = {"mfma": measured["mfma_bf16_tflops"], "alu": measured["exp_texp_per_s"], "hbm": measured["hbm_read_gbs"]}
+        for r in list(rates.values()) + [roof]:
+            if r.get("achieved") is not None and r.get("bound") in mpk:
+                r["peak_measured"] = mpk[r["bound"]]
+                r["frac_measured"] = r["achieved"] / mpk[r["bound"]]
+
     dense = None
     if not a.no_dense:
         log("[bench] dense comparator (k = N/Bk through the same kernels)")
@@ -372,7 +391,9 @@ def main():
                    "generator": cfg.generator},
         "tokens_per_s": B * N / (ms_step * 1e-3),
         "attn_fwd_bwd": {"ms": attn_ms, "tflops": attn_tflops, "frac_of_peak": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
+                         "frac_of_measured_peak": attn_tflops / measured["mfma_bf16_tflops"] if measured else None,
                          "tokens_per_s": B * N / (attn_ms * 1e-3)},
+        "measured_peaks": measured,
         "phases_ms": {"predict": phases[0], "select": phases[1], "fwd": phases[2], "bwd": phases[3]},
         "kernels": kern, "kernel_rates": rates, "dense": dense, "mass_selection": mass, "representative": rep, "pack": pack,
         "roofline": roof, "cpu_baseline": cpu,

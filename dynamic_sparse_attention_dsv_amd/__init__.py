@@ -35,7 +35,8 @@ EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_predict_representa
             "dsv_select_mass", "dsv_head_density", "dsv_block_recall", "dsv_pack_kv_workspace_size", "dsv_pack_kv",
             "dsv_sparse_attn_fwd_workspace_size",
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd_workspace_size", "dsv_sparse_attn_bwd", "dsv_status_string",
-            "dsv_last_error", "dsv_version", "dsv_timing_begin", "dsv_timing_end")
+            "dsv_last_error", "dsv_version", "dsv_timing_begin", "dsv_timing_end", "dsv_peak_probe_workspace_size",
+            "dsv_peak_probe")
 
 
 class Problem(ctypes.Structure):
@@ -89,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsv_version": (ctypes.c_int32, []),
         "dsv_timing_begin": (ctypes.c_int, []),
         "dsv_timing_end": (ctypes.c_int32, [ctypes.POINTER(KernelStat), ctypes.c_int32]),
+        "dsv_peak_probe_workspace_size": (S, [ctypes.c_int32]),
+        "dsv_peak_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, V, S, ctypes.POINTER(ctypes.c_double), V]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -384,6 +387,23 @@ def workspace_sizes(q: torch.Tensor, *, q_block: int, kv_block: int, topk: int, 
     return (int(lib.dsv_predict_workspace_size(ctypes.byref(prob))),
             int(lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(prob))),
             int(lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(prob))))
+
+
+PEAK_KINDS = {"mfma_bf16": 0, "mfma_f16": 1, "exp_f32": 2, "hbm_copy": 3, "hbm_read": 4}
+
+
+def peak_probe(kind: str, repeats: int = 5, device: Optional[torch.device] = None) -> float:
+    """Sustained rate of one operation on this device (blocks): ``mfma_bf16`` / ``mfma_f16`` in
+    flop/s (MFMA 32x32x16), ``exp_f32`` in exponentials/s, ``hbm_copy`` in bytes/s read + written,
+    ``hbm_read`` in bytes/s read."""
+    lib = load_library()
+    code = PEAK_KINDS[kind]
+    dev = device or torch.device("cuda", torch.cuda.current_device())
+    nbytes = int(lib.dsv_peak_probe_workspace_size(code))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rate = ctypes.c_double(0.0)
+    _check(lib.dsv_peak_probe(code, int(repeats), _p(ws), nbytes, ctypes.byref(rate), _stream(dev)), "dsv_peak_probe")
+    return rate.value
 
 
 def timing_begin() -> None:

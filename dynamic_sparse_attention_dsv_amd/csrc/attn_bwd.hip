@@ -451,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(
 // range at full precision.  dQ is unscaled exactly at the end.  dP stays a bf16 product.
 
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_bf16_kernel(
+__global__ __launch_bounds__(BQ * 2, (kMinWavesPerSimd<D, BQ>)) void attn_bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k16, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dvec,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ dq,

@@ -32,7 +32,7 @@ namespace dsv {
 // PV16: the training forward.  v is then the fp16 copy of V scaled by 2^f16_shift(vmax[bh]);
 // P enters O += P V rounded to fp16, and the kernel also writes O's rounding residual o_lo.
 template <int D, int BQ, bool PV16>
-__global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(BQ * 2, (kMinWavesPerSimd<D, BQ>)) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ o,
     float* __restrict__ lse, uint16_t* __restrict__ o_lo /* rounding residual of O (PV16) */,

@@ -288,6 +288,13 @@ __device__ __forceinline__ void lds_load_rows(const uint16_t* src, uint16_t* dst
   __builtin_amdgcn_global_load_lds(rows + off, dst + i * 512, 16, 0, 0);
 }
 
+// Waves per SIMD a query-parallel attention kernel (Bq/32 waves per workgroup, four 64-key K/V
+// tiles of D columns in LDS) can reach: two, except at D = 128 with Bq = 64, where a workgroup of
+// two waves holds 64 KB of LDS, two workgroups fill a compute unit's 160 KB and each SIMD runs one
+// wave (the register budget is then that of one wave).
+template <int D, int BQ>
+constexpr int kMinWavesPerSimd = (D == 128 && BQ == 64) ? 1 : 2;
+
 // Workspace sub-buffers start on 256-byte boundaries.
 __host__ __device__ inline size_t align_ws(size_t x) { return (x + 255) / 256 * 256; }
 

@@ -209,6 +209,50 @@ const char* dsv_last_error(void) { return g_err.c_str(); }
 
 int32_t dsv_version(void) { return 100; }
 
+size_t dsv_peak_probe_workspace_size(int32_t kind) {
+  const size_t per_thread = (size_t)dsv::kProbeMaxCus * 8 * 256 * sizeof(float);  // one word per probe thread
+  if (kind == DSV_PEAK_MFMA_BF16 || kind == DSV_PEAK_MFMA_F16 || kind == DSV_PEAK_EXP_F32) return per_thread;
+  if (kind == DSV_PEAK_HBM_COPY) return dsv::kProbeCopyBytes;
+  if (kind == DSV_PEAK_HBM_READ) return dsv::kProbeCopyBytes + per_thread;
+  return 0;
+}
+
+dsv_status dsv_peak_probe(int32_t kind, int32_t repeats, void* workspace, size_t workspace_bytes, double* rate,
+                          void* stream) {
+  g_err.clear();
+  const size_t need = dsv_peak_probe_workspace_size(kind);
+  if (need == 0) return fail(DSV_ERR_INVALID_ARGUMENT, "unknown probe kind " + std::to_string(kind));
+  if (repeats < 1 || repeats > 100) return fail(DSV_ERR_INVALID_ARGUMENT, "repeats must lie in [1, 100]");
+  if (!rate) return fail(DSV_ERR_INVALID_ARGUMENT, "rate is null");
+  TRY(check_ptr(workspace, "workspace", kWsAlign));
+  if (workspace_bytes < need)
+    return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "probe workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+    if (a) (void)hipEventDestroy(a);
+    return fail(DSV_ERR_HIP, "hipEventCreate failed");
+  }
+  double best_ms = 0.0, work = 0.0;
+  dsv_status s = DSV_OK;
+  for (int i = 0; i < repeats && s == DSV_OK; ++i) {
+    float ms = 0.f;
+    hipError_t e = hipEventRecord(a, st);
+    if (e == hipSuccess) e = dsv::launch_peak_probe(kind, workspace, need, st, &work);
+    if (e == hipSuccess) e = hipEventRecord(b, st);
+    if (e == hipSuccess) e = hipEventSynchronize(b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    if (e != hipSuccess) s = hip_status(e, "peak probe");
+    else if (i == 0 || ms < best_ms) best_ms = ms;
+  }
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  if (s != DSV_OK) return s;
+  if (!(best_ms > 0.0)) return fail(DSV_ERR_HIP, "peak probe: no elapsed time recorded");
+  *rate = work / (best_ms * 1e-3);
+  return DSV_OK;
+}
+
 dsv_status dsv_timing_begin(void) {
   g_err.clear();
   if (g_timing) return fail(DSV_ERR_INVALID_ARGUMENT, "timing already active on this thread");

@@ -87,4 +87,10 @@ hipError_t launch_pack_kv(const void* k, const void* v, const int32_t* idx, cons
                           int32_t* blocks, int32_t* count, int32_t* packed_idx, int32_t* flags, int32_t* pos, int bh,
                           int n, int row_bytes, int nqb, int nkb, int topk, int qb0, int qb1, hipStream_t st);
 
+// peak-rate probes (probe.hip): kind 0/1 MFMA 32x32x16 bf16/fp16 (flop), 2 v_exp_f32 (results),
+// 3 HBM copy (bytes read + written), 4 HBM read (bytes).  *work is the launch's amount of that work.
+constexpr int kProbeMaxCus = 1024;
+constexpr size_t kProbeCopyBytes = (size_t)1 << 30;  // 512 MiB read + 512 MiB written
+hipError_t launch_peak_probe(int kind, void* ws, size_t ws_bytes, hipStream_t st, double* work);
+
 }  // namespace dsv

@@ -335,6 +335,40 @@ typedef struct {
 dsv_status dsv_timing_begin(void);
 int32_t dsv_timing_end(dsv_kernel_stat* out, int32_t capacity);
 
+/*
+ * Peak-rate probes (measurement).  The rates this device sustains for the operations the hot
+ * path's kernels are bound by, so that a kernel's rate can be stated as a fraction of a measured
+ * peak beside the vendor's: the attention products run on the matrix cores (MFMA 32x32x16, bf16
+ * and fp16 operands), the predictor on the transcendental unit (one v_exp_f32 per predicted
+ * logit), selection and the copies on HBM.  Each probe kernel does only that operation, over
+ * enough waves to fill every SIMD:
+ *   DSV_PEAK_MFMA_BF16, DSV_PEAK_MFMA_F16   rate in flop/s (2*32*32*16 per instruction)
+ *   DSV_PEAK_EXP_F32                        rate in exponentials/s
+ *   DSV_PEAK_HBM_COPY                       rate in bytes/s, read + written, over 1 GiB of workspace
+ *   DSV_PEAK_HBM_READ                       rate in bytes/s, loads only, over 1 GiB of workspace
+ *
+ *   kind        one of dsv_peak_kind
+ *   repeats     launches to time, 1..100; the fastest is reported
+ *   workspace   >= dsv_peak_probe_workspace_size(kind) bytes, 256-byte aligned, caller-owned
+ *               device scratch (its contents are overwritten)
+ *   rate        host pointer, receives the rate
+ * Unlike every other call this one BLOCKS: it records HIP events around each launch on `stream`
+ * and waits for them.  Errors: DSV_ERR_INVALID_ARGUMENT (unknown kind, repeats out of range, null
+ * pointers), DSV_ERR_WORKSPACE_TOO_SMALL, DSV_ERR_HIP.
+ */
+typedef enum {
+  DSV_PEAK_MFMA_BF16 = 0,
+  DSV_PEAK_MFMA_F16 = 1,
+  DSV_PEAK_EXP_F32 = 2,
+  DSV_PEAK_HBM_COPY = 3,
+  DSV_PEAK_HBM_READ = 4
+} dsv_peak_kind;
+
+/* Workspace bytes of a probe (0 for an unknown kind). */
+size_t dsv_peak_probe_workspace_size(int32_t kind);
+dsv_status dsv_peak_probe(int32_t kind, int32_t repeats, void* workspace, size_t workspace_bytes, double* rate,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -199,3 +199,22 @@ def test_native_caller_is_built_and_checks_its_arguments():
     r = subprocess.run([exe, "/nonexistent", "/tmp/x", "1", "1", "1024", "64", "16", "64", "2"], capture_output=True,
                        text=True, timeout=60)
     assert r.returncode == 1 and "cannot read" in r.stderr
+
+
+def test_peak_probe_validates_before_any_launch(lib):
+    # workspace sizes: one float per probe thread (MFMA, exp), 1 GiB for the copy; 0 = unknown kind
+    assert lib.dsv_peak_probe_workspace_size(0) == lib.dsv_peak_probe_workspace_size(2) > 0
+    assert lib.dsv_peak_probe_workspace_size(3) == 1 << 30
+    assert lib.dsv_peak_probe_workspace_size(4) > 1 << 30
+    assert lib.dsv_peak_probe_workspace_size(5) == 0 and lib.dsv_peak_probe_workspace_size(-1) == 0
+    rate = ctypes.c_double(0.0)
+    nb = lib.dsv_peak_probe_workspace_size(0)
+    assert lib.dsv_peak_probe(9, 1, FAKE, nb, ctypes.byref(rate), None) == 1          # unknown kind
+    assert lib.dsv_peak_probe(0, 0, FAKE, nb, ctypes.byref(rate), None) == 1          # repeats out of range
+    assert lib.dsv_peak_probe(0, 101, FAKE, nb, ctypes.byref(rate), None) == 1
+    assert lib.dsv_peak_probe(0, 1, FAKE, nb, None, None) == 1                        # no rate pointer
+    assert lib.dsv_peak_probe(0, 1, None, nb, ctypes.byref(rate), None) == 1          # no workspace
+    assert lib.dsv_peak_probe(0, 1, ctypes.c_void_p((1 << 20) + 16), nb, ctypes.byref(rate), None) == 1  # alignment
+    assert lib.dsv_peak_probe(3, 1, FAKE, (1 << 30) - 1, ctypes.byref(rate), None) == 3  # workspace too small
+    assert "workspace" in lib.dsv_last_error().decode()
+    assert rate.value == 0.0
