@@ -51,3 +51,31 @@ def test_bench_reports_traffic_only_for_an_unchanged_kernel(tmp_path, monkeypatc
     assert bench.measured_traffic(cfg, "attn_fwd_kernel")[0] == 6.0
     assert bench.measured_traffic(cfg, "attn_bwd_dq_kernel") == (None, None)   # sources changed since
     assert bench.measured_traffic(cfg, "scores_kernel") == (None, None)        # never measured
+
+
+def test_counter_summary_ratios(tmp_path):
+    from dynamic_sparse_attention_dsv_amd import profile_counters as pc
+
+    def pmc(path, rows):
+        con = sqlite3.connect(path)
+        con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
+        con.executemany("insert into counters_collection values (?,?,?)", rows)
+        con.commit()
+        con.close()
+        return str(path)
+
+    # two passes; GRBM_GUI_ACTIVE in both (the first is kept); two dispatches averaged in pass 1
+    p1 = pmc(tmp_path / "p1.db", [(KNAME, "GRBM_GUI_ACTIVE", 1000.0), (KNAME, "SQ_BUSY_CU_CYCLES", 256000.0),
+                                  (KNAME, "SQ_VALU_MFMA_BUSY_CYCLES", 512000.0),
+                                  (KNAME, "SQ_VALU_MFMA_BUSY_CYCLES", 512000.0), (KNAME, "SQ_INSTS_MFMA", 100.0),
+                                  (KNAME, "SQ_INSTS_VALU", 250.0)])
+    p2 = pmc(tmp_path / "p2.db", [(KNAME, "GRBM_GUI_ACTIVE", 999.0), (KNAME, "SQ_VALU_MFMA_COEXEC_CYCLES", 128000.0),
+                                  (KNAME, "TCC_HIT_sum", 30.0), (KNAME, "TCC_MISS_sum", 10.0),
+                                  (KNAME, "SQ_WAVE_CYCLES", 400.0), (KNAME, "SQ_WAIT_INST_ANY", 100.0)])
+    data = pc.merge([p1, p2])
+    r = pc.ratios(data["attn_fwd_bf16_kernel<128, 128>"], cus=256)
+    assert r["MFMA busy"] == 512000.0 / (4 * 256000.0)   # 0.5
+    assert r["co-exec"] == 0.25 and r["VALU / MFMA"] == 2.5
+    assert r["L2 hit"] == 0.75 and r["wait"] == 0.25 and r["LDS conflicts"] is None
+    md = pc.to_markdown(data, ["attn_fwd"], 256, "cmd", "t")
+    assert "| attn_fwd_bf16_kernel<128, 128> | 50.0 % | 25.0 % | 2.50 | 25.0 % | - | - | 75.0 % |" in md
