@@ -22,6 +22,11 @@ average of every counter and these ratios:
 
     python -m dynamic_sparse_attention_dsv_amd.profile_counters P1.db P2.db ... \\
         --kernels attn_fwd_bf16_kernel attn_bwd_dkdv_bf16_kernel --command "..." --md out.md
+
+With ``--clocks``, the one database given must come from a run that took the kernel trace and
+the counters GRBM_GUI_ACTIVE and SQ_BUSY_CU_CYCLES together; the table then gives each kernel's
+effective clock over its dispatch: GRBM_GUI_ACTIVE / XCDs / duration (the GPU-busy cycles are
+summed over the XCDs) and SQ_BUSY_CU_CYCLES / CUs / duration (the compute units' busy cycles).
 """
 from __future__ import annotations
 
@@ -87,6 +92,35 @@ def to_markdown(data: dict, kernels, cus: int, command: str, title: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def clocks(db: str, kernels, xcds: int, cus: int):
+    """[(kernel, avg ms, GHz from GRBM_GUI_ACTIVE, GHz from SQ_BUSY_CU_CYCLES)] of one database."""
+    con = sqlite3.connect(db)
+    dur = {short(n): avg_us for n, avg_us in con.execute("select name, average from top_kernels")}
+    cnt = per_kernel(db)
+    rows = []
+    for k, avg_us in dur.items():
+        if not any(k.startswith(p) for p in kernels) or k not in cnt:
+            continue
+        t = avg_us * 1e-6
+        g, b = cnt[k].get("GRBM_GUI_ACTIVE"), cnt[k].get("SQ_BUSY_CU_CYCLES")
+        rows.append((k, avg_us / 1e3, None if g is None else g / xcds / t / 1e9,
+                     None if b is None else b / cus / t / 1e9))
+    return rows
+
+
+def clocks_markdown(rows, command: str, title: str) -> str:
+    out = [f"# {title}", "", "Command (repository root, one MI355X, `export TMPDIR=/tmp`):", ""]
+    out += ["    " + ln for ln in command.split("\n")] + [""]
+    out += ["Effective clock over each kernel's dispatch, from the kernel trace and two counters of the "
+            "same run (`profile_counters.py --clocks`).", "",
+            "| kernel | avg ms | GHz (GRBM_GUI_ACTIVE / 8 XCDs) | GHz (SQ_BUSY_CU_CYCLES / 256 CUs) |",
+            "|---|---|---|---|"]
+    for k, ms, g1, g2 in rows:
+        f = lambda v: "-" if v is None else f"{v:.3f}"
+        out.append(f"| {k} | {ms:.3f} | {f(g1)} | {f(g2)} |")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("dbs", nargs="+")
@@ -95,8 +129,13 @@ def main():
     ap.add_argument("--command", required=True)
     ap.add_argument("--title", default="Hardware counters")
     ap.add_argument("--md")
+    ap.add_argument("--clocks", action="store_true", help="effective clocks from one trace+counter database")
+    ap.add_argument("--xcds", type=int, default=8)
     a = ap.parse_args()
-    md = to_markdown(merge(a.dbs), a.kernels, a.cus, a.command, a.title)
+    if a.clocks:
+        md = clocks_markdown(clocks(a.dbs[0], a.kernels, a.xcds, a.cus), a.command, a.title)
+    else:
+        md = to_markdown(merge(a.dbs), a.kernels, a.cus, a.command, a.title)
     if a.md:
         with open(a.md, "w") as fh:
             fh.write(md)

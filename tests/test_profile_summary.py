@@ -79,3 +79,17 @@ def test_counter_summary_ratios(tmp_path):
     assert r["L2 hit"] == 0.75 and r["wait"] == 0.25 and r["LDS conflicts"] is None
     md = pc.to_markdown(data, ["attn_fwd"], 256, "cmd", "t")
     assert "| attn_fwd_bf16_kernel<128, 128> | 50.0 % | 25.0 % | 2.50 | 25.0 % | - | - | 75.0 % |" in md
+
+
+def test_effective_clocks(tmp_path):
+    from dynamic_sparse_attention_dsv_amd import profile_counters as pc
+
+    db = _db(tmp_path / "clk.db", kernels=[(KNAME, 2, 20000.0, 10000.0, 90.0)])  # 10 ms per dispatch
+    con = sqlite3.connect(db)
+    con.executemany("insert into counters_collection values (?,?,?)",
+                    [(KNAME, "GRBM_GUI_ACTIVE", 8 * 1.5e7), (KNAME, "SQ_BUSY_CU_CYCLES", 256 * 1.4e7)])
+    con.commit()
+    con.close()
+    (k, ms, g1, g2), = pc.clocks(db, ["attn_fwd"], xcds=8, cus=256)
+    assert ms == 10.0 and abs(g1 - 1.5) < 1e-12 and abs(g2 - 1.4) < 1e-12
+    assert "| 1.500 | 1.400 |" in pc.clocks_markdown([(k, ms, g1, g2)], "cmd", "t")
