@@ -281,7 +281,7 @@ def test_single_block_and_unselected_blocks_get_zero_gradient():
 # ------------------------------------------------------------------ full-size configs, sampled outputs
 
 
-@pytest.mark.parametrize("name", ["C4", "C5", "NMAX", "C4-G2"])
+@pytest.mark.parametrize("name", ["C4", "C4b", "C5", "NMAX", "C4-G2"])
 def test_full_size_sampled(name):
     # NMAX: the largest sequence the library takes, N/Bk = 4096 KV blocks (N = 262144, a 64^3
     # latent), at C5's head shape and 10 % density, two heads.  C4-G2: C4 on the 3D-cube inputs
