@@ -19,10 +19,11 @@
 //  * scores: persistent workgroups of 4 waves; each work item is 256 query rows
 //    of one head, 64 per wave.  Each wave sweeps every KV block once: one bf16
 //    32x32x16 MFMA product of Q~ and K_lr gives the logits in log2 units, and 2^l
-//    summed over the block's 64 keys gives the row's block mass.  Block masses go to a per-workgroup scratch of nkb x 256 floats
-//    (never N x N); the row totals are their sums, and after the sweep the same
-//    workgroup divides and sums them into block scores.  The sweep is bound by
-//    the vector ALU (one exp2 and one add per logit), not by MFMA or memory.
+//    summed over the block's 64 keys gives the row's block mass.  Block masses go to
+//    a per-workgroup scratch of nkb x 256 floats (never N x N); the row totals are
+//    their sums, and the same workgroup divides and sums them into block scores
+//    while it sweeps its next item (two scratch halves per workgroup).  The sweep is
+//    bound by the vector ALU (one exp2 and one add per logit), not by MFMA or memory.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -103,7 +104,8 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
                                                           float* __restrict__ scores, int n, int nkb,
                                                           int items, int rep) {
   // qlr, klr: [BH, n, R] bf16, qlr the scaled query projection Q~ (logits <Q~_i, K_lr_j> in log2
-  // units).  scratch: gridDim.x slots of [nkb][256] float.  scores: [BH, n/BQ, nkb].
+  // units).  scratch: gridDim.x slots of two [nkb][256] float halves (REP: one).  scores:
+  // [BH, n/BQ, nkb].
   // Each wave owns 64 query rows (two 32-row halves): every K_lr fragment it loads feeds
   // two MFMA tiles, halving the K_lr traffic per logit.
   //
@@ -115,17 +117,72 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
   static_assert(kScoreRows % BQ == 0 && BQ % 64 == 0, "BQ must be 64 or 128");
   constexpr int NC = R / 16;
   constexpr float kTinyMass = 7.888609052210118e-31f;  // 2^-100
-  __shared__ float row_s[kScoreRows];  // 1/T (fast path) or log2 T (exact path) per row
+  __shared__ float row_s[2][kScoreRows];  // per slot half: 1/T (fast path) or log2 T (exact path) per row
   __shared__ float part_s[4][64];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
-  float* slot = scratch + (size_t)blockIdx.x * nkb * kScoreRows;
+  const size_t slot_elems = (size_t)nkb * kScoreRows;
+  float* const slots = scratch + (size_t)blockIdx.x * (REP ? 1 : 2) * slot_elems;
   const int nqb = n / BQ;
   const int items_per_head = REP ? (nqb + kScoreRows - 1) / kScoreRows : n / kScoreRows;
+
+  // finalize: score[qb, kb] = sum_{i in qb} mass[kb][i] / T_i (log domain on the exact path), all
+  // at once after a sweep.  chunks of 64 KV blocks: lane <-> kb, wave w sums its rows [64w, 64w+64).
+  auto finalize_now = [&](const float* sl, const float* rs_all, bool exact, float* sc_head, int qb0) {
+    for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
+      const int kb = kb0 + lane;
+      float acc0 = 0.f, acc1 = 0.f;
+      if (kb < nkb) {
+        const float* src = sl + (size_t)kb * kScoreRows + wave * 64;
+        const float* rs = rs_all + wave * 64;
+        if (!exact) {
+#pragma unroll
+          for (int i = 0; i < 64; i += 4) {
+            const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
+            acc0 = fmaf(tv[0], rs[i], fmaf(tv[1], rs[i + 1], acc0));
+            acc1 = fmaf(tv[2], rs[i + 2], fmaf(tv[3], rs[i + 3], acc1));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 64; i += 4) {
+            const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
+            acc0 += fast_exp2(tv[0] - rs[i]) + fast_exp2(tv[1] - rs[i + 1]);
+            acc1 += fast_exp2(tv[2] - rs[i + 2]) + fast_exp2(tv[3] - rs[i + 3]);
+          }
+        }
+      }
+      part_s[wave][lane] = acc0 + acc1;
+      __syncthreads();
+      constexpr int QBS = kScoreRows / BQ;    // query blocks per item
+      constexpr int WPQ = BQ / 64;            // waves per query block
+      if (threadIdx.x < 64 * QBS) {
+        const int qq = threadIdx.x / 64, kk = kb0 + (threadIdx.x & 63);
+        if (kk < nkb) {
+          float tot = 0.f;
+#pragma unroll
+          for (int w = 0; w < WPQ; ++w) tot += part_s[qq * WPQ + w][threadIdx.x & 63];
+          sc_head[(size_t)(qb0 + qq) * nkb + kk] = tot;
+        }
+      }
+      __syncthreads();
+    }
+  };
+
+  // Deferred finalisation (fast path, REP = false).  A fast item's masses stay in one half of the
+  // slot while the next item's sweep fills the other half; that sweep finalises them in passing,
+  // one 16-row step per trip, so the HBM-bound reads overlap the VALU-bound sweeps of the whole
+  // grid instead of running in step across all slots.  Wave w owns the chunks of 64 KV blocks
+  // w, w + 4, ...; each step of a wave reads 16 rows of one chunk for the lane's KV block and adds
+  // them, weighted by 1/T, into the running score of their query block.
+  bool pend = false;  // the other half holds a fast item still to be finalised
+  int pbh = 0, pqb0 = 0, buf = 0;
+  const int nch = (nkb + 63) / 64;
+  const int nchw = wave < nch ? (nch - 1 - wave) / 4 + 1 : 0;
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int bh = item / items_per_head;
     const int row0 = (item % items_per_head) * kScoreRows;  // first row, or first query block (REP)
+    float* const slot = slots + (size_t)buf * slot_elems;
     // query row of the item's local row i (REP: past the last query block the row is clamped
     // to a valid one and its scores are never written)
     auto qrow_of = [&](int i) { return REP ? min(row0 + i, nqb - 1) * BQ + rep : row0 + i; };
@@ -189,23 +246,73 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
       tot0 += b0;
       tot1 += b1;
     };
-    load_k(0, ka);
-    logits(ka, A);
-    load_k(1, ka);
-    for (int kb = 0; kb < nkb; kb += 2) {
+    // the pending item's finalisation: P steps for this wave, one in each of the first E1 trips
+    // (spreading them thinner over the sweep, with an unrolled group of trips per step, measured
+    // slower: the larger loop body costs more than the lighter bursts of reads save).
+    // Step p covers chunk p / 16 and its rows 16 (p mod 16) .. +15 (four 16-byte loads per lane).
+    const float* const pslot = slots + (size_t)(buf ^ 1) * slot_elems;
+    const float* const prs = row_s[buf ^ 1];
+    float* const psc = scores + (size_t)pbh * nqb * nkb;
+    const int P = (!REP && pend) ? nchw * (kScoreRows / 16) : 0;
+    const int E1 = min(nkb / 2, P);
+    f32x4 fv[4];
+    float fa = 0.f;
+    auto issue = [&](int p) {
+      const uint32_t voff = (uint32_t)min((wave + 4 * (p >> 4)) * 64 + lane, nkb - 1) * (kScoreRows * 4);
+      const char* b = reinterpret_cast<const char*>(pslot + (p & 15) * 16);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fv[u] = *reinterpret_cast<const f32x4*>(b + voff + u * 16);
+    };
+    auto consume = [&](int p) {
+      const int r0 = (p & 15) * 16;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(prs + r0 + 4 * u);
+        fa = fmaf(fv[u][3], w[3], fmaf(fv[u][2], w[2], fmaf(fv[u][1], w[1], fmaf(fv[u][0], w[0], fa))));
+      }
+      if (((p + 1) & (BQ / 16 - 1)) == 0) {  // the query block's last sixteen rows
+        const int kbs = (wave + 4 * (p >> 4)) * 64 + lane;
+        if (kbs < nkb) psc[(size_t)(pqb0 + r0 / BQ) * nkb + kbs] = fa;
+        fa = 0.f;
+      }
+    };
+    // one trip: blocks kb and kb + 1.  The finalisation loads are issued after the trip's last
+    // K_lr loads, so the K_lr waits that follow leave them in flight; the first trip with loads is
+    // peeled so that the loop is entered with the same loads outstanding as at its back edge.
+    auto trip = [&](int kb, bool ev, bool cons) {
       logits(ka, B);  // block kb + 1
       load_k(min(kb + 2, nkb - 1), ka);
       finish(kb, A);
       logits(ka, A);  // block kb + 2
       load_k(min(kb + 3, nkb - 1), ka);
+      if (ev) {
+        if (cons) consume(kb / 2 - 1);
+        issue(kb / 2);
+      }
       finish(kb + 1, B);
+    };
+    load_k(0, ka);
+    logits(ka, A);
+    load_k(1, ka);
+    int kb = 0;
+    if (E1 > 0) {
+      trip(0, true, false);
+      for (kb = 2; kb < 2 * E1; kb += 2) trip(kb, true, true);
+    }
+    for (; kb < nkb; kb += 2) trip(kb, false, false);
+    if (P > 0) {  // the last step, and any beyond the sweep's trips (nkb / 2 < P)
+      consume(E1 - 1);
+      for (int p = E1; p < P; ++p) {
+        issue(p);
+        consume(p);
+      }
     }
     const bool exact = __syncthreads_or(!(tot0 < INFINITY) || !(tot0 >= kTinyMass) || !(tot1 < INFINITY) ||
                                         !(tot1 >= kTinyMass));
     if (!exact) {
       if (g == 0) {
-        row_s[wave * 64 + c32] = 1.f / tot0;
-        row_s[wave * 64 + 32 + c32] = 1.f / tot1;
+        row_s[buf][wave * 64 + c32] = 1.f / tot0;
+        row_s[buf][wave * 64 + 32 + c32] = 1.f / tot1;
       }
     } else {
       // exact path: block log-masses t = m + log2 sum_j 2^(l_ij - m) with m the block's own
@@ -237,8 +344,8 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
         store(kb, g ? t2[1] : t2[0]);
       }
       if (g == 0) {
-        row_s[wave * 64 + c32] = run_m[0] + fast_log2(run_s[0]);
-        row_s[wave * 64 + 32 + c32] = run_m[1] + fast_log2(run_s[1]);
+        row_s[buf][wave * 64 + c32] = run_m[0] + fast_log2(run_s[0]);
+        row_s[buf][wave * 64 + 32 + c32] = run_m[1] + fast_log2(run_s[1]);
       }
     }
     __threadfence_block();
@@ -254,54 +361,25 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
         const float* src = slot + (size_t)kb * kScoreRows;
         for (int i = wave * 64; i < wave * 64 + 64; ++i) {
           if (row0 + i >= nqb) break;
-          sc_head[(size_t)(row0 + i) * nkb + kb] = exact ? fast_exp2(src[i] - row_s[i]) : src[i] * row_s[i];
+          sc_head[(size_t)(row0 + i) * nkb + kb] =
+              exact ? fast_exp2(src[i] - row_s[0][i]) : src[i] * row_s[0][i];
         }
       }
       __syncthreads();  // the slot and row_s are reused by the next item
       continue;
     }
-    // finalize: score[qb, kb] = sum_{i in qb} mass[kb][i] / T_i  (log domain on the exact path).
-    // chunks of 64 KV blocks: lane <-> kb, wave w sums its rows [64w, 64w+64).
-    float* sc_head = scores + (size_t)bh * (n / BQ) * nkb;
-    const int qb0 = row0 / BQ;
-    for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
-      const int kb = kb0 + lane;
-      float acc0 = 0.f, acc1 = 0.f;
-      if (kb < nkb) {
-        const float* src = slot + (size_t)kb * kScoreRows + wave * 64;
-        const float* rs = row_s + wave * 64;
-        if (!exact) {
-#pragma unroll
-          for (int i = 0; i < 64; i += 4) {
-            const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
-            acc0 = fmaf(tv[0], rs[i], fmaf(tv[1], rs[i + 1], acc0));
-            acc1 = fmaf(tv[2], rs[i + 2], fmaf(tv[3], rs[i + 3], acc1));
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 64; i += 4) {
-            const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
-            acc0 += fast_exp2(tv[0] - rs[i]) + fast_exp2(tv[1] - rs[i + 1]);
-            acc1 += fast_exp2(tv[2] - rs[i + 2]) + fast_exp2(tv[3] - rs[i + 3]);
-          }
-        }
-      }
-      part_s[wave][lane] = acc0 + acc1;
-      __syncthreads();
-      constexpr int QBS = kScoreRows / BQ;    // query blocks per item
-      constexpr int WPQ = BQ / 64;            // waves per query block
-      if (threadIdx.x < 64 * QBS) {
-        const int qq = threadIdx.x / 64, kk = kb0 + (threadIdx.x & 63);
-        if (kk < nkb) {
-          float tot = 0.f;
-#pragma unroll
-          for (int w = 0; w < WPQ; ++w) tot += part_s[qq * WPQ + w][threadIdx.x & 63];
-          sc_head[(size_t)(qb0 + qq) * nkb + kk] = tot;
-        }
-      }
-      __syncthreads();
+    if (exact) {  // finalised at once (its masses are log-domain); nothing stays pending
+      finalize_now(slot, row_s[buf], true, scores + (size_t)bh * nqb * nkb, row0 / BQ);
+      pend = false;
+    } else {
+      pend = true;
+      pbh = bh;
+      pqb0 = row0 / BQ;
+      buf ^= 1;
     }
   }
+  if (!REP && pend) finalize_now(slots + (size_t)(buf ^ 1) * slot_elems, row_s[buf ^ 1], false,
+                                 scores + (size_t)pbh * nqb * nkb, pqb0);
 }
 
 // ---------------------------------------------------------------- scores (f32, plain VALU)
@@ -438,8 +516,8 @@ int score_slots(int items) {
   return items < slots ? items : slots;
 }
 
-size_t score_scratch_bytes(int items, int nkb) {
-  return (size_t)score_slots(items) * nkb * kScoreRows * sizeof(float);
+size_t score_scratch_bytes(int items, int nkb) {  // two halves per slot (deferred finalisation)
+  return (size_t)score_slots(items) * 2 * nkb * kScoreRows * sizeof(float);
 }
 
 int score_items(int bh, int n, int bq, bool representative) {
