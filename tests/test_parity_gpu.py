@@ -331,6 +331,42 @@ def test_full_size_sampled(name):
             log(f"[parity] {name} h={h} kb={kb} dK/dV ok")
 
 
+@pytest.mark.parametrize("r,bq", [(32, 128), (16, 64)])
+def test_predictor_slots_running_several_items_with_exact_items_between(r, bq):
+    # The score sweep runs persistent workgroups ("slots", 4 per compute unit), each taking items
+    # of 256 query rows in turn; a fast item's masses are finalised during the slot's next sweep
+    # and the slot's last item at its end, while an exact-path item is finalised at once.  540
+    # heads of N = 1024 make 2160 items, so every slot runs two or three, and every third head
+    # (overflowing block masses) or ninth (vanishing ones) takes the exact path between fast
+    # items.  With W = [I; 0] the projections are the first r columns of Q and K; every head is
+    # compared with the oracle on the GPU's own projections.
+    heads, n, d, bk = 540, 1024, 64, 64
+    rng = np.random.default_rng(37)
+    q = rng.standard_normal((1, heads, n, d)).astype(np.float32)
+    k = rng.standard_normal((1, heads, n, d)).astype(np.float32)
+    over = [h for h in range(heads) if h % 3 == 1]
+    tiny = [h for h in range(heads) if h % 9 == 5]
+    q[0, over + tiny, :, :r] = 1.0
+    big = 768.0 / r  # logits of ~138 (log2) on block 5: 2^138 overflows fp32
+    k[0, over, 0:64, :r] = 0.0
+    k[0, over, 5 * 64:6 * 64, :r] = big
+    k[0, tiny, :, :r] = -big - np.abs(k[0, tiny, :, :r]) * 8
+    k[0, tiny, 5 * 64:6 * 64, :r] = -big
+    w = np.zeros((heads, d, r), np.float32)
+    w[:, :r, :r] = np.eye(r)
+    from workloads.generator import bf16_bits_from_f32
+    t = {nm: to_dev(bf16_bits_from_f32(a)) for nm, a in (("q", q), ("k", k), ("w", w))}
+    scores, qlr, klr = dsv.predict(t["q"], t["k"], t["w"], t["w"], q_block=bq, kv_block=bk, return_projections=True)
+    torch.cuda.synchronize()
+    sg, ql, kl = to_f64(scores)[0], to_f64(qlr)[0], to_f64(klr)[0]
+    assert np.isfinite(sg).all()
+    for h in range(heads):
+        ref = O.block_scores_head(ql[h], kl[h], bq, bk, O.LN2)
+        np.testing.assert_allclose(sg[h], ref, rtol=2e-4, atol=2e-5, err_msg=f"head {h}")
+    assert np.all(sg[over, :, 5] > 0.99 * bq) and np.all(sg[tiny, :, 5] > 0.99 * bq)
+    log(f"[parity] predictor r={r} bq={bq}: {heads} heads, {len(over) + len(tiny)} on the exact path, all match")
+
+
 @pytest.mark.parametrize("case", ["overflow", "tiny"])
 def test_predictor_extreme_logits_use_the_exact_fallback(case):
     # With W = [I; 0], Q_lr and K_lr are the first r columns of Q and K, and every logit is
