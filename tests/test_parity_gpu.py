@@ -367,6 +367,31 @@ def test_predictor_slots_running_several_items_with_exact_items_between(r, bq):
     log(f"[parity] predictor r={r} bq={bq}: {heads} heads, {len(over) + len(tiny)} on the exact path, all match")
 
 
+@pytest.mark.parametrize("n,heads,r,bq,check_every", [(256, 2100, 32, 128, 1), (4352, 130, 16, 64, 6)])
+def test_predictor_deferred_finalisation_at_edge_sizes(n, heads, r, bq, check_every):
+    # Enough score items (heads * N / 256) that every persistent slot runs two or more, at the
+    # edges of the deferred finalisation: N = 256 has 4 KV blocks (one chunk of 64, mostly past
+    # the end) and more finalisation steps than sweep trips; N = 4352 has 68 KV blocks, so the
+    # second chunk holds 4.  Projections as in the test above (W = [I; 0]).
+    d, bk = 64, 64
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((1, heads, n, d)).astype(np.float32)
+    k = rng.standard_normal((1, heads, n, d)).astype(np.float32)
+    w = np.zeros((heads, d, r), np.float32)
+    w[:, :r, :r] = np.eye(r)
+    from workloads.generator import bf16_bits_from_f32
+    t = {nm: to_dev(bf16_bits_from_f32(a)) for nm, a in (("q", q), ("k", k), ("w", w))}
+    scores, qlr, klr = dsv.predict(t["q"], t["k"], t["w"], t["w"], q_block=bq, kv_block=bk, return_projections=True)
+    torch.cuda.synchronize()
+    sg, ql, kl = to_f64(scores)[0], to_f64(qlr)[0], to_f64(klr)[0]
+    assert np.isfinite(sg).all()
+    np.testing.assert_allclose(sg.sum(axis=-1), bq, rtol=1e-5)  # every row's masses sum to 1
+    for h in range(0, heads, check_every):
+        ref = O.block_scores_head(ql[h], kl[h], bq, bk, O.LN2)
+        np.testing.assert_allclose(sg[h], ref, rtol=2e-4, atol=2e-5, err_msg=f"head {h}")
+    log(f"[parity] predictor N={n} heads={heads} r={r} bq={bq}: every {check_every}th head matches")
+
+
 @pytest.mark.parametrize("case", ["overflow", "tiny"])
 def test_predictor_extreme_logits_use_the_exact_fallback(case):
     # With W = [I; 0], Q_lr and K_lr are the first r columns of Q and K, and every logit is
