@@ -109,6 +109,20 @@ def test_o_residual_is_bf16_only_and_aligned(lib):
     assert st == 1 and "o_lo" in lib.dsv_last_error().decode()
 
 
+def test_predict_workspace_is_the_projections_then_two_mass_halves_per_score_slot(lib):
+    # bf16: Q~ and K_lr ([B, H, N, r] bf16 each), then per persistent score workgroup two
+    # [N/64][256] float halves of per-row block masses (one filled by the sweep while the other
+    # waits for its finalisation).  2 heads x 1024 rows / 256 make eight work items, so eight
+    # workgroups on any device with two or more compute units.
+    p = _prob()
+    lr = 1 * 2 * 1024 * 16 * 2
+    slots, nkb = 2 * 1024 // 256, 1024 // 64
+    nw = lib.dsv_predict_workspace_size(ctypes.byref(p))
+    assert nw == 2 * lr + slots * 2 * nkb * 256 * 4
+    assert lib.dsv_predict(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, nw - 1, FAKE, None) == 3
+    assert "workspace" in lib.dsv_last_error().decode()
+
+
 def test_workspace_sizes_and_short_workspace_is_rejected(lib):
     p = _prob()
     # bf16 training forward (o_lo given): an fp16 copy of V, B*H*N*d*2 bytes, plus per-head words
