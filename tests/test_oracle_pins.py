@@ -300,6 +300,53 @@ def test_bf16_query_operand_carries_the_scale_before_its_rounding():
     assert np.any(qt[0, 0] != ps / math.log(2.0) * bf(q[0, 0] @ wq[0]).numpy())
 
 
+@pytest.mark.parametrize("generator", ["g1", "g2"])
+def test_bf16_scores_lie_within_two_operand_roundings_of_the_exact_mass(generator):
+    # R3 at the default, non-power-of-two scale, pinned to the unrounded predictor rather than to
+    # the oracle's own formula.  Exact fp64 logits: l*_ij = pred_scale <a_i, b_j>, a = Q Wq,
+    # b = K Wk.  Rounding each operand once to bf16 (8 significant bits: relative error at most
+    # u = 2^-8 for these normal-range values) moves a logit by D_ij with
+    #   |D_ij| <= E_ij = pred_scale sum_c |a_ic b_jc| (2u + u^2).
+    # With P* the exact softmax, P_ij = P*_ij exp(D_ij) / Z_i and Z_i = sum_j P*_ij exp(D_ij) lies in
+    # [sum_j P*_ij exp(-E_ij), sum_j P*_ij exp(E_ij)], so a block score sum_{i in qb, j in kb} P_ij
+    # lies between sum P*_ij exp(-E_ij) / Zhi_i and sum P*_ij exp(E_ij) / Zlo_i.
+    from workloads import get_config, make_inputs
+    from workloads.generator import widen
+
+    cfg = get_config("C2").with_(heads=2, latent=(4, 16, 16), generator=generator)  # N = 1024, d = 64, r = 16
+    x = {nm: widen(a) for nm, a in make_inputs(cfg, with_grad=False).items()}
+    ps = 1.0 / math.sqrt(cfg.head_dim)
+    bq, bk = cfg.q_block, cfg.kv_block
+    s, qt, kl = O.predict(x["q"], x["k"], x["wq"], x["wk"], bq, bk, ps, "bf16")
+    u = 2.0 ** -8
+    n = cfg.seq_len
+    blocks = lambda m: m.reshape(n // bq, bq, n // bk, bk).sum(axis=(1, 3))
+    for h in range(cfg.heads):
+        a, b = x["q"][0, h] @ x["wq"][h], x["k"][0, h] @ x["wk"][h]
+        exact = torch.softmax(torch.from_numpy(ps * a @ b.T), dim=-1).numpy()     # P*, float64
+        e = ps * (np.abs(a) @ np.abs(b).T) * (2 * u + u * u) * (1 + 1e-12)     # E_ij (+ fp64 slack)
+        zlo = (exact * np.exp(-e)).sum(axis=1, keepdims=True)
+        zhi = (exact * np.exp(e)).sum(axis=1, keepdims=True)
+        lo, hi = blocks(exact * np.exp(-e) / zhi), blocks(exact * np.exp(e) / zlo)
+        within = lambda sc: bool(np.all((sc >= lo - 1e-12) & (sc <= hi + 1e-12)))
+        assert within(s[0, h]), (s[0, h] - hi).max()
+        err, slack = np.abs(s[0, h] - blocks(exact)), np.maximum(hi - blocks(exact), blocks(exact) - lo)
+        print(f"{generator} h={h}: max |score - exact| {err.max():.3e}, max half-width {slack.max():.3e}")
+        assert err.max() > 0  # the operands are rounded: the scores move
+        # the operands are bf16 values within u of the exact scaled projections
+        y = ps / math.log(2.0) * a
+        np.testing.assert_array_equal(qt[0, h], O.round_bf16(qt[0, h]))
+        np.testing.assert_array_equal(kl[0, h], O.round_bf16(kl[0, h]))
+        assert np.all(np.abs(qt[0, h] - y) <= u * np.abs(y)) and np.all(np.abs(kl[0, h] - b) <= u * np.abs(b))
+        # planted slips (in the oracle's score step, on the CPU) fall outside the bound: logits left
+        # in base-2 units, the log scale applied twice, the key operand never projected by Wk's scale
+        # (a factor 2 on K_lr)
+        ql, kk = qt[0, h], kl[0, h]
+        assert not within(O.block_scores_head(ql, kk, bq, bk, 1.0))
+        assert not within(O.block_scores_head(ql, kk, bq, bk, O.LN2 * O.LN2))
+        assert not within(O.block_scores_head(ql, 2 * kk, bq, bk, O.LN2))
+
+
 def test_representative_scores_are_the_one_row_softmax():
     rng = _rng(14)
     n, r, bq, bk = 256, 8, 64, 32
