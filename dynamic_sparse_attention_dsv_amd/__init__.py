@@ -33,6 +33,7 @@ STATUS = {0: "DSV_OK", 1: "DSV_ERR_INVALID_ARGUMENT", 2: "DSV_ERR_UNSUPPORTED", 
 
 EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_predict_representative", "dsv_select_topk",
             "dsv_select_mass", "dsv_head_density", "dsv_block_recall", "dsv_pack_kv_workspace_size", "dsv_pack_kv",
+            "dsv_pack_kv_noalloc",
             "dsv_sparse_attn_fwd_workspace_size",
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd_workspace_size", "dsv_sparse_attn_bwd", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_timing_begin", "dsv_timing_end", "dsv_peak_probe_workspace_size",
@@ -81,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsv_head_density": (ctypes.c_int, [P, V, ctypes.c_float, V, V, V]),
         "dsv_pack_kv_workspace_size": (S, [P]),
         "dsv_pack_kv": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, ctypes.c_int32, V, V, V, V, V, V, S, V]),
+        "dsv_pack_kv_noalloc": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, ctypes.c_int32, V, V, V, V, V, V]),
         "dsv_sparse_attn_fwd_workspace_size": (S, [P]),
         "dsv_sparse_attn_fwd": (ctypes.c_int, [P, V, V, V, V, V, V, V, V, V, S, V]),
         "dsv_sparse_attn_bwd_workspace_size": (S, [P]),
@@ -377,6 +379,33 @@ def pack_kv(k, v, block_idx, qb_begin: int, qb_end: int, *, q_block: int, kv_blo
     _check(lib.dsv_pack_kv(ctypes.byref(prob), _p(k), _p(v), _p(block_idx), _p(block_counts), int(qb_begin),
                            int(qb_end), _p(kp), _p(vp), _p(blocks), _p(counts), _p(pidx) if pidx.numel() else None,
                            _p(ws), ws.numel() * ws.element_size(), _stream(dev)), "dsv_pack_kv")
+    return kp, vp, blocks, counts, pidx
+
+
+def pack_kv_noalloc(k, v, block_idx, qb_begin: int, qb_end: int, *, out, q_block: int, kv_block: int = 64,
+                    block_counts: Optional[torch.Tensor] = None):
+    """:func:`pack_kv` with no allocation at all: ``out`` = (k_packed, v_packed, packed_blocks,
+    packed_counts, packed_idx), shaped as pack_kv returns them, is filled in place (packed_idx may
+    be None when qb_end == qb_begin).  The scratch is the library's own device array (B*H*N/Bk <=
+    262144); calls that overlap in time on one GPU race."""
+    lib = load_library()
+    kp, vp, blocks, counts, pidx = out
+    dev = _dev(k, v, block_idx, kp, vp, blocks, counts)
+    _contig(k, v, block_idx, kp, vp, blocks, counts, pidx)
+    b, h, n, d = k.shape
+    nsh = max(qb_end - qb_begin, 0)
+    want = {"k_packed": (kp, k.shape, k.dtype), "v_packed": (vp, k.shape, k.dtype),
+            "packed_blocks": (blocks, (b, h, n // kv_block), torch.int32), "packed_counts": (counts, (b, h), torch.int32)}
+    if nsh:
+        want["packed_idx"] = (pidx, (b, h, nsh, block_idx.shape[-1]), torch.int32)
+    for name, (t, shape, dt) in want.items():
+        if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dt or t.device != dev:
+            raise ValueError(f"{name} must be {dt} {tuple(shape)} on {dev}")
+    prob = make_problem(k, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1])
+    _check_counts(block_counts, block_idx)
+    _check(lib.dsv_pack_kv_noalloc(ctypes.byref(prob), _p(k), _p(v), _p(block_idx), _p(block_counts), int(qb_begin),
+                                   int(qb_end), _p(kp), _p(vp), _p(blocks), _p(counts), _p(pidx) if nsh else None,
+                                   _stream(dev)), "dsv_pack_kv_noalloc")
     return kp, vp, blocks, counts, pidx
 
 

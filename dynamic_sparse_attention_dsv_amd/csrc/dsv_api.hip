@@ -429,12 +429,12 @@ size_t dsv_pack_kv_workspace_size(const dsv_problem* p) {
   return 2 * align_up((size_t)o.bh() * o.nkb() * 4);
 }
 
-dsv_status dsv_pack_kv(const dsv_problem* p, const void* k, const void* v, const int32_t* block_idx,
-                       const int32_t* block_counts, int32_t qb_begin, int32_t qb_end, void* k_packed, void* v_packed,
-                       int32_t* packed_blocks, int32_t* packed_counts, int32_t* packed_idx, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  Prob o;
+namespace {
+// the checks shared by dsv_pack_kv and dsv_pack_kv_noalloc (everything but the scratch)
+dsv_status check_pack(const dsv_problem* p, Prob& o, const void* k, const void* v, const int32_t* block_idx,
+                      const int32_t* block_counts, int32_t qb_begin, int32_t qb_end, const void* k_packed,
+                      const void* v_packed, const int32_t* packed_blocks, const int32_t* packed_counts,
+                      const int32_t* packed_idx) {
   TRY(to_prob(p, o, false));
   if (qb_begin < 0 || qb_end > o.nqb() || qb_begin > qb_end)
     return fail(DSV_ERR_INVALID_ARGUMENT, "need 0 <= qb_begin <= qb_end <= N/Bq");
@@ -446,15 +446,50 @@ dsv_status dsv_pack_kv(const dsv_problem* p, const void* k, const void* v, const
   TRY(check_ptr(packed_blocks, "packed_blocks", 4));
   TRY(check_ptr(packed_counts, "packed_counts", 4));
   if (qb_end > qb_begin) TRY(check_ptr(packed_idx, "packed_idx", 4));
+  if (o.bk != 64) return fail(DSV_ERR_UNSUPPORTED, "packing needs Bk = 64");
+  return DSV_OK;
+}
+}  // namespace
+
+dsv_status dsv_pack_kv(const dsv_problem* p, const void* k, const void* v, const int32_t* block_idx,
+                       const int32_t* block_counts, int32_t qb_begin, int32_t qb_end, void* k_packed, void* v_packed,
+                       int32_t* packed_blocks, int32_t* packed_counts, int32_t* packed_idx, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(check_pack(p, o, k, v, block_idx, block_counts, qb_begin, qb_end, k_packed, v_packed, packed_blocks,
+                 packed_counts, packed_idx));
   TRY(check_ptr(workspace, "workspace", kWsAlign));
   const size_t half = align_up((size_t)o.bh() * o.nkb() * 4);
   if (workspace_bytes < 2 * half)
     return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "pack workspace needs " + std::to_string(2 * half) + " bytes");
-  if (o.bk != 64) return fail(DSV_ERR_UNSUPPORTED, "packing needs Bk = 64");
   hipStream_t st = static_cast<hipStream_t>(stream);
   TRY_HIP(dsv::launch_pack_kv(k, v, block_idx, block_counts, k_packed, v_packed, packed_blocks, packed_counts,
                               packed_idx, at<int32_t>(workspace, 0), at<int32_t>(workspace, half), o.bh(), o.n,
                               (int)(o.d * o.esize()), o.nqb(), o.nkb(), o.k, qb_begin, qb_end, st),
+          "pack_kernels");
+  return DSV_OK;
+}
+
+dsv_status dsv_pack_kv_noalloc(const dsv_problem* p, const void* k, const void* v, const int32_t* block_idx,
+                               const int32_t* block_counts, int32_t qb_begin, int32_t qb_end, void* k_packed,
+                               void* v_packed, int32_t* packed_blocks, int32_t* packed_counts, int32_t* packed_idx,
+                               void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, false));
+  const size_t need = (size_t)o.bh() * o.nkb();
+  if (need > dsv::kPackScratchEntries)
+    return fail(DSV_ERR_UNSUPPORTED, "B*H*N/Bk = " + std::to_string(need) + " exceeds the allocation-free limit of " +
+                                         std::to_string(dsv::kPackScratchEntries) + " (use dsv_pack_kv)");
+  TRY(check_pack(p, o, k, v, block_idx, block_counts, qb_begin, qb_end, k_packed, v_packed, packed_blocks,
+                 packed_counts, packed_idx));
+  int32_t *flags = nullptr, *pos = nullptr;
+  TRY(hip_status(dsv::pack_scratch(&flags, &pos), "pack scratch lookup"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY_HIP(dsv::launch_pack_kv(k, v, block_idx, block_counts, k_packed, v_packed, packed_blocks, packed_counts,
+                              packed_idx, flags, pos, o.bh(), o.n, (int)(o.d * o.esize()), o.nqb(), o.nkb(), o.k,
+                              qb_begin, qb_end, st),
           "pack_kernels");
   return DSV_OK;
 }

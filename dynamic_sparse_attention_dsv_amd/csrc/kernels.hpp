@@ -86,6 +86,10 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
 hipError_t launch_pack_kv(const void* k, const void* v, const int32_t* idx, const int32_t* cnts, void* kp, void* vp,
                           int32_t* blocks, int32_t* count, int32_t* packed_idx, int32_t* flags, int32_t* pos, int bh,
                           int n, int row_bytes, int nqb, int nkb, int topk, int qb0, int qb1, hipStream_t st);
+// the allocation-free variant's flags and positions (kPackScratchEntries int32 each) in the library's
+// own device array: the current device's address of it, looked up once per device
+constexpr size_t kPackScratchEntries = (size_t)1 << 18;  // B * H * N/Bk at most (1 MiB per array)
+hipError_t pack_scratch(int32_t** flags, int32_t** pos);
 
 // peak-rate probes (probe.hip): kind 0/1 MFMA 32x32x16 bf16/fp16 (flop), 2 v_exp_f32 (results),
 // 3 HBM copy (bytes read + written), 4 HBM read (bytes).  *work is the launch's amount of that work.

@@ -15,6 +15,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <mutex>
 
 namespace dsv {
 
@@ -141,6 +142,40 @@ hipError_t launch_pack_kv(const void* k, const void* v, const int32_t* idx, cons
     e = hipGetLastError();
   }
   return e;
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+//
+// For callers that cannot allocate device memory (graph capture, tight serving loops): the
+// flags and positions live in this file-scope device array instead of a caller workspace.
+// Every GPU the library runs on holds its own copy until the process ends.  In host code the
+// array's name is only a stand-in for the symbol: its device address, which differs per
+// device, comes from hipGetSymbolAddress and is cached per device ordinal below; only that
+// address is ever handed to a kernel.
+static __device__ __align__(256) int32_t scratch[2 * kPackScratchEntries];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t pack_scratch(int32_t** flags, int32_t** pos) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy (the device is current)
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *flags = g_scratch_ptr[dev];
+  *pos = g_scratch_ptr[dev] + kPackScratchEntries;
+  return hipSuccess;
 }
 
 }  // namespace dsv

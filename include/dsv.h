@@ -236,6 +236,24 @@ dsv_status dsv_pack_kv(const dsv_problem* p, const void* k, const void* v, const
                        void* v_packed, int32_t* packed_blocks, int32_t* packed_counts, int32_t* packed_idx,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * dsv_pack_kv_noalloc -- dsv_pack_kv without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, outputs and results as dsv_pack_kv, minus `workspace`.  The
+ * union flags and positions live instead in a device array inside the library: one copy per
+ * GPU, allocated with the code object and held until the process ends, sized for
+ * B * H * N/Bk <= 262144 (2 MiB in all).  The call allocates and frees nothing; it clears
+ * what must start at zero with a kernel of its own on `stream`.
+ * Limits and races: a larger problem returns DSV_ERR_UNSUPPORTED (use dsv_pack_kv).  Every
+ * call on one GPU shares that GPU's array, so calls that may overlap in time on one GPU
+ * (different streams, or different host threads) race and must be serialised by the caller;
+ * calls queued on one stream are ordered and safe.
+ */
+dsv_status dsv_pack_kv_noalloc(const dsv_problem* p, const void* k, const void* v, const int32_t* block_idx,
+                               const int32_t* block_counts, int32_t qb_begin, int32_t qb_end, void* k_packed,
+                               void* v_packed, int32_t* packed_blocks, int32_t* packed_counts, int32_t* packed_idx,
+                               void* stream);
+
 /* Workspace bytes dsv_sparse_attn_fwd needs when o_lo is requested (DSV_BF16: an fp16 copy
    of V plus a few bytes per head); 0 for DSV_F32 or an invalid problem.  A forward without
    o_lo needs no workspace (`workspace` may then be NULL). */

@@ -232,3 +232,15 @@ def test_peak_probe_validates_before_any_launch(lib):
     assert lib.dsv_peak_probe(3, 1, FAKE, (1 << 30) - 1, ctypes.byref(rate), None) == 3  # workspace too small
     assert "workspace" in lib.dsv_last_error().decode()
     assert rate.value == 0.0
+
+
+def test_noalloc_pack_rejects_problems_beyond_its_scratch(lib):
+    # B*H*N/Bk = 65 * 4096 entries exceeds the library's 262144-entry device array: refused on the
+    # host before any launch, with the limit named
+    p = _prob(heads=65, seq_len=262144, head_dim=128, q_block=128, topk=8)
+    st = lib.dsv_pack_kv_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, None, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == 2 and "allocation-free limit" in lib.dsv_last_error().decode()
+    # exactly at the limit the size passes and the pointer checks run
+    p = _prob(heads=64, seq_len=262144, head_dim=128, q_block=128, topk=8)
+    st = lib.dsv_pack_kv_noalloc(ctypes.byref(p), FAKE, FAKE, None, None, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == 1 and "block_idx" in lib.dsv_last_error().decode()
