@@ -350,7 +350,18 @@ def main():
             evr[2].synchronize()
         rep = {"rep_row": 0, "predict_ms": evr[0].elapsed_time(evr[1]), "select_ms": evr[1].elapsed_time(evr[2]),
                "logits": float(B * H * cfg.nqb) * N}
-        log(f"[bench] representative leg: predict {rep['predict_ms']:.2f} ms, select {rep['select_ms']:.2f} ms")
+        # the fused predictor + top-k (indices straight from the projections, no score matrix)
+        idx_f = torch.empty_like(idx)
+        for _ in range(2):  # the first pass warms up
+            evr[0].record(stream)
+            dsv.predict_select_representative(t["q"], t["k"], t["wq"], t["wk"], cfg.topk, 0, workspace=wsp,
+                                              out=idx_f, **kw)
+            evr[1].record(stream)
+            evr[1].synchronize()
+        rep["fused_ms"] = evr[0].elapsed_time(evr[1])
+        rep["fused_equal_to_unfused"] = float((idx_f == idx).all(dim=-1).float().mean())
+        log(f"[bench] representative leg: predict {rep['predict_ms']:.2f} ms, select {rep['select_ms']:.2f} ms; "
+            f"fused {rep['fused_ms']:.2f} ms (rows equal to the unfused pair: {rep['fused_equal_to_unfused']:.4f})")
 
     pack = None
     if not a.no_pack:

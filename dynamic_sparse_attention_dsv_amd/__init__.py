@@ -8,6 +8,7 @@ tensors are not on a GPU, the calls raise.
 
 Entry points (same names as the C ABI):
   predict(q, k, wq, wk, ...)          -> block_scores [B, H, N/Bq, N/Bk] float32 (rep_row=...: one-row masses)
+  predict_select_representative(q, k, wq, wk, topk, rep_row, ...) -> block_idx (fused predict + top-k)
   select_topk(block_scores, topk)     -> block_idx    [B, H, N/Bq, k]    int32
   select_mass(block_scores, tau, kmax) -> (block_idx [B, H, N/Bq, kmax] padded with -1, block_counts)
   sparse_attn_fwd(q, k, v, idx, ...)  -> (o, lse), or (o, lse, o_lo) with residual=True
@@ -31,7 +32,8 @@ DSV_F32, DSV_BF16 = 0, 1
 STATUS = {0: "DSV_OK", 1: "DSV_ERR_INVALID_ARGUMENT", 2: "DSV_ERR_UNSUPPORTED", 3: "DSV_ERR_WORKSPACE_TOO_SMALL",
           4: "DSV_ERR_HIP"}
 
-EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_predict_representative", "dsv_select_topk",
+EXPORTED = ("dsv_predict_workspace_size", "dsv_predict", "dsv_predict_representative",
+            "dsv_predict_select_representative", "dsv_select_topk",
             "dsv_select_mass", "dsv_head_density", "dsv_block_recall", "dsv_pack_kv_workspace_size", "dsv_pack_kv",
             "dsv_pack_kv_noalloc",
             "dsv_sparse_attn_fwd_workspace_size",
@@ -76,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsv_predict_workspace_size": (S, [P]),
         "dsv_predict": (ctypes.c_int, [P, V, V, V, V, V, S, V, V]),
         "dsv_predict_representative": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, V, S, V, V]),
+        "dsv_predict_select_representative": (ctypes.c_int, [P, V, V, V, V, ctypes.c_int32, V, S, V, V]),
         "dsv_select_topk": (ctypes.c_int, [P, V, V, V]),
         "dsv_select_mass": (ctypes.c_int, [P, V, ctypes.c_float, V, V, V]),
         "dsv_block_recall": (ctypes.c_int, [P, V, V, V, V]),
@@ -116,6 +119,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _dev(*ts: torch.Tensor) -> torch.device:
+    ts = [t for t in ts if t is not None]
     dev = ts[0].device
     if dev.type != "cuda":
         raise RuntimeError("dsv kernels need GPU tensors (no CPU path exists)")
@@ -129,12 +133,20 @@ def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype) -> None:
+    """Shape and dtype of a tensor the kernels will read or write: a mismatch would make them
+    touch memory outside the allocation, so it is refused here, before any device work."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def _check_counts(cnt: Optional[torch.Tensor], idx: torch.Tensor) -> None:
-    if cnt is None:
-        return
-    _contig(cnt)
-    if cnt.dtype != torch.int32 or tuple(cnt.shape) != tuple(idx.shape[:-1]) or cnt.device != idx.device:
-        raise ValueError("block_counts must be int32 [B, H, N/Bq] on the block_idx device")
+    if cnt is not None:
+        _expect(cnt, "block_counts", idx.shape[:-1], torch.int32)
 
 
 def _stream(dev: torch.device):
@@ -156,6 +168,12 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _blocks(n: int, q_block: int, kv_block: int) -> Tuple[int, int]:
+    if q_block < 1 or kv_block < 1 or n % q_block or n % kv_block:
+        raise ValueError(f"N={n} must be a multiple of q_block={q_block} and kv_block={kv_block}")
+    return n // q_block, n // kv_block
+
+
 def _workspace(nbytes: int, dev: torch.device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return None
@@ -170,6 +188,27 @@ def predict_workspace_size(prob: Problem) -> int:
     return int(load_library().dsv_predict_workspace_size(ctypes.byref(prob)))
 
 
+def _predict_inputs(q, k, wq, wk):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    b, h, n, d = q.shape
+    _expect(k, "k", q.shape, q.dtype)
+    if wq.dim() != 3:
+        raise ValueError("wq must be [H, d, r]")
+    _expect(wq, "wq", (h, d, wq.shape[2]), q.dtype)
+    _expect(wk, "wk", wq.shape, q.dtype)
+    _contig(q)
+    return b, h, n, d, wq.shape[2]
+
+
+def _projections(ws, q, b, h, n, r):
+    esz = q.element_size()
+    lr = b * h * n * r * esz
+    off_k = (lr + 255) // 256 * 256
+    flat = ws.view(torch.uint8)
+    return flat[:lr].view(q.dtype).view(b, h, n, r), flat[off_k:off_k + lr].view(q.dtype).view(b, h, n, r)
+
+
 def predict(q, k, wq, wk, *, q_block: int, kv_block: int = 64, pred_scale: Optional[float] = None,
             rep_row: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
             return_projections: bool = False, out: Optional[torch.Tensor] = None):
@@ -180,18 +219,14 @@ def predict(q, k, wq, wk, *, q_block: int, kv_block: int = 64, pred_scale: Optio
     returns the two operands of the logit product: Q~ = round(pred_scale * log2(e) * q @ wq) (the
     scale applied before the one rounding) and K_lr = round(k @ wk); logit = ln(2) * <Q~_i, K_lr_j>."""
     lib = load_library()
-    dev = _dev(q, k, wq, wk)
-    _contig(q, k, wq, wk)
-    b, h, n, d = q.shape
-    if k.shape != q.shape or wq.shape != wk.shape or wq.shape[:2] != (h, d):
-        raise ValueError("shape mismatch: q, k [B,H,N,d]; wq, wk [H,d,r]")
-    if not (q.dtype == k.dtype == wq.dtype == wk.dtype):
-        raise TypeError("q, k, wq, wk must share one dtype")
-    r = wq.shape[2]
+    b, h, n, d, r = _predict_inputs(q, k, wq, wk)
+    nqb, nkb = _blocks(n, q_block, kv_block)
+    if out is not None:
+        _expect(out, "out", (b, h, nqb, nkb), torch.float32)
+    dev = _dev(q, k, wq, wk, out)
     prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=1, rank=r, pred_scale=pred_scale)
     ws = _workspace(int(lib.dsv_predict_workspace_size(ctypes.byref(prob))), dev, workspace)
-    scores = out if out is not None else torch.empty((b, h, n // q_block, n // kv_block), dtype=torch.float32,
-                                                     device=dev)
+    scores = out if out is not None else torch.empty((b, h, nqb, nkb), dtype=torch.float32, device=dev)
     nbytes = ws.numel() * ws.element_size()
     if rep_row is None:
         _check(lib.dsv_predict(ctypes.byref(prob), _p(q), _p(k), _p(wq), _p(wk), _p(ws), nbytes, _p(scores),
@@ -200,28 +235,53 @@ def predict(q, k, wq, wk, *, q_block: int, kv_block: int = 64, pred_scale: Optio
         _check(lib.dsv_predict_representative(ctypes.byref(prob), _p(q), _p(k), _p(wq), _p(wk), int(rep_row), _p(ws),
                                               nbytes, _p(scores), _stream(dev)), "dsv_predict_representative")
     if return_projections:
-        esz = q.element_size()
-        lr = b * h * n * r * esz
-        off_k = (lr + 255) // 256 * 256
-        flat = ws.view(torch.uint8)
-        qlr = flat[:lr].view(q.dtype).view(b, h, n, r)
-        klr = flat[off_k:off_k + lr].view(q.dtype).view(b, h, n, r)
-        return scores, qlr, klr
+        return (scores, *_projections(ws, q, b, h, n, r))
     return scores
+
+
+def predict_select_representative(q, k, wq, wk, topk: int, rep_row: int, *, q_block: int, kv_block: int = 64,
+                                  pred_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                                  return_projections: bool = False, out: Optional[torch.Tensor] = None):
+    """The fused representative-row predictor and top-k: for every query block, the ``topk`` KV
+    blocks with the largest predicted mass of its row qb * q_block + rep_row, ascending ->
+    block_idx [B, H, N/Bq, k] int32 (no score matrix is formed).  ``return_projections`` also
+    returns Q~ and K_lr as :func:`predict` does."""
+    lib = load_library()
+    b, h, n, d, r = _predict_inputs(q, k, wq, wk)
+    nqb, nkb = _blocks(n, q_block, kv_block)
+    if out is not None:
+        _expect(out, "out", (b, h, nqb, topk), torch.int32)
+    dev = _dev(q, k, wq, wk, out)
+    prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=topk, rank=r, pred_scale=pred_scale)
+    ws = _workspace(int(lib.dsv_predict_workspace_size(ctypes.byref(prob))), dev, workspace)
+    idx = out if out is not None else torch.empty((b, h, nqb, topk), dtype=torch.int32, device=dev)
+    _check(lib.dsv_predict_select_representative(ctypes.byref(prob), _p(q), _p(k), _p(wq), _p(wk), int(rep_row),
+                                                 _p(ws), ws.numel() * ws.element_size(), _p(idx), _stream(dev)),
+           "dsv_predict_select_representative")
+    if return_projections:
+        return (idx, *_projections(ws, q, b, h, n, r))
+    return idx
+
+
+def _scores_shape(scores: torch.Tensor, q_block: int, kv_block: int):
+    if scores.dtype != torch.float32 or scores.dim() != 4:
+        raise TypeError("scores must be float32 [B, H, N/Bq, N/Bk]")
+    _contig(scores)
+    b, h, nqb, nkb = scores.shape
+    n = nkb * kv_block
+    if nqb * q_block != n:
+        raise ValueError("scores shape does not match the block sizes")
+    return b, h, nqb, nkb, n
 
 
 def select_topk(scores: torch.Tensor, topk: int, *, q_block: int, kv_block: int = 64,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The top-k KV blocks of every query block, ascending, ties to the smaller index."""
     lib = load_library()
-    dev = _dev(scores)
-    _contig(scores)
-    if scores.dtype != torch.float32 or scores.dim() != 4:
-        raise TypeError("scores must be float32 [B, H, N/Bq, N/Bk]")
-    b, h, nqb, nkb = scores.shape
-    n = nkb * kv_block
-    if nqb * q_block != n:
-        raise ValueError("scores shape does not match the block sizes")
+    b, h, nqb, nkb, n = _scores_shape(scores, q_block, kv_block)
+    if out is not None:
+        _expect(out, "out", (b, h, nqb, topk), torch.int32)
+    dev = _dev(scores, out)
     prob = Problem(b, h, n, 64, q_block, kv_block, topk, 1, DSV_F32, 0.0, 0.0)
     idx = out if out is not None else torch.empty((b, h, nqb, topk), dtype=torch.int32, device=dev)
     _check(lib.dsv_select_topk(ctypes.byref(prob), _p(scores), _p(idx), _stream(dev)), "dsv_select_topk")
@@ -233,23 +293,35 @@ def select_mass(scores: torch.Tensor, tau: float, kmax: int, *, q_block: int, kv
     """The fewest KV blocks (by descending score) carrying a fraction tau of each query block's
     score, at most kmax -> (block_idx ascending then -1 padding, block_counts)."""
     lib = load_library()
-    dev = _dev(scores)
-    _contig(scores)
-    if scores.dtype != torch.float32 or scores.dim() != 4:
-        raise TypeError("scores must be float32 [B, H, N/Bq, N/Bk]")
-    b, h, nqb, nkb = scores.shape
-    n = nkb * kv_block
-    if nqb * q_block != n:
-        raise ValueError("scores shape does not match the block sizes")
-    prob = Problem(b, h, n, 64, q_block, kv_block, kmax, 1, DSV_F32, 0.0, 0.0)
+    b, h, nqb, nkb, n = _scores_shape(scores, q_block, kv_block)
     if out is not None:
         idx, cnt = out
+        _expect(idx, "out[0] (block_idx)", (b, h, nqb, kmax), torch.int32)
+        _expect(cnt, "out[1] (block_counts)", (b, h, nqb), torch.int32)
+        dev = _dev(scores, idx, cnt)
     else:
+        dev = _dev(scores)
         idx = torch.empty((b, h, nqb, kmax), dtype=torch.int32, device=dev)
         cnt = torch.empty((b, h, nqb), dtype=torch.int32, device=dev)
+    prob = Problem(b, h, n, 64, q_block, kv_block, kmax, 1, DSV_F32, 0.0, 0.0)
     _check(lib.dsv_select_mass(ctypes.byref(prob), _p(scores), ctypes.c_float(tau), _p(idx), _p(cnt), _stream(dev)),
            "dsv_select_mass")
     return idx, cnt
+
+
+def _attn_inputs(q, k, v, block_idx, q_block, kv_block):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    b, h, n, d = q.shape
+    _dtype_code(q)
+    _contig(q)
+    _expect(k, "k", q.shape, q.dtype)
+    _expect(v, "v", q.shape, q.dtype)
+    nqb, _ = _blocks(n, q_block, kv_block)
+    if block_idx.dim() != 4:
+        raise ValueError("block_idx must be [B, H, N/Bq, k]")
+    _expect(block_idx, "block_idx", (b, h, nqb, block_idx.shape[-1]), torch.int32)
+    return b, h, n, d
 
 
 def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_scale: Optional[float] = None,
@@ -264,32 +336,31 @@ def sparse_attn_fwd(q, k, v, block_idx, *, q_block: int, kv_block: int = 64, sm_
     :func:`select_mass`) limits each query block to the first entries of its list.
     """
     lib = load_library()
-    dev = _dev(q, k, v, block_idx)
-    _contig(q, k, v, block_idx)
-    if not (q.shape == k.shape == v.shape) or block_idx.dtype != torch.int32:
-        raise ValueError("q, k, v must share a shape; block_idx must be int32")
-    b, h, n, d = q.shape
-    prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1], sm_scale=sm_scale)
-    if tuple(block_idx.shape) != (b, h, n // q_block, prob.topk):
-        raise ValueError("block_idx must be [B, H, N/Bq, k]")
+    b, h, n, d = _attn_inputs(q, k, v, block_idx, q_block, kv_block)
     if residual and q.dtype != torch.bfloat16:
         raise ValueError("the O residual exists for bf16 problems only")
-    ws = _workspace(int(lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(prob))) if residual else 0, dev,
-                    workspace)
+    _check_counts(block_counts, block_idx)
     o_lo = None
     if out is not None:
+        if len(out) < (3 if residual else 2):
+            raise ValueError("out must hold (o, lse) or, with residual=True, (o, lse, o_lo)")
         o, lse = out[0], out[1]
+        _expect(o, "out[0] (o)", q.shape, q.dtype)
+        _expect(lse, "out[1] (lse)", (b, h, n), torch.float32)
         if residual:
-            if len(out) < 3:
-                raise ValueError("out must hold (o, lse, o_lo) when residual=True")
             o_lo = out[2]
+            _expect(o_lo, "out[2] (o_lo)", q.shape, torch.bfloat16)
+        dev = _dev(q, k, v, block_idx, block_counts, o, lse, o_lo)
     else:
+        dev = _dev(q, k, v, block_idx, block_counts)
         o = torch.empty_like(q)
         lse = torch.empty((b, h, n), dtype=torch.float32, device=dev)
-    if residual and o_lo is None:
-        o_lo = torch.empty_like(q)
+        if residual:
+            o_lo = torch.empty_like(q)
+    prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1], sm_scale=sm_scale)
+    ws = _workspace(int(lib.dsv_sparse_attn_fwd_workspace_size(ctypes.byref(prob))) if residual else 0, dev,
+                    workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check_counts(block_counts, block_idx)
     _check(lib.dsv_sparse_attn_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(block_idx), _p(block_counts), _p(o),
                                    _p(lse), _p(o_lo), _p(ws), nbytes, _stream(dev)), "dsv_sparse_attn_fwd")
     return (o, lse, o_lo) if residual else (o, lse)
@@ -301,17 +372,22 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, block_idx, *, q_block: int, kv_block:
                     out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """Gradients (dq, dk, dv) of the sparse attention; ``o_lo`` is the forward's residual (or None)."""
     lib = load_library()
-    dev = _dev(q, k, v, o, dout, lse, block_idx)
-    _contig(q, k, v, o, dout, lse, block_idx)
+    b, h, n, d = _attn_inputs(q, k, v, block_idx, q_block, kv_block)
+    _expect(o, "o", q.shape, q.dtype)
+    _expect(dout, "dout", q.shape, q.dtype)
+    _expect(lse, "lse", (b, h, n), torch.float32)
     if o_lo is not None:
-        _contig(o_lo)
-        if o_lo.shape != o.shape or o_lo.dtype != torch.bfloat16:
-            raise ValueError("o_lo must be a bf16 tensor shaped like o")
-    b, h, n, d = q.shape
+        _expect(o_lo, "o_lo", q.shape, torch.bfloat16)
+    _check_counts(block_counts, block_idx)
+    if out is not None:
+        dq, dk, dv = out
+        for nm, t in (("out[0] (dq)", dq), ("out[1] (dk)", dk), ("out[2] (dv)", dv)):
+            _expect(t, nm, q.shape, q.dtype)
+    dev = _dev(q, k, v, o, dout, lse, block_idx, o_lo, block_counts, *(out or ()))
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     prob = make_problem(q, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1], sm_scale=sm_scale)
     ws = _workspace(int(lib.dsv_sparse_attn_bwd_workspace_size(ctypes.byref(prob))), dev, workspace)
-    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    _check_counts(block_counts, block_idx)
     _check(lib.dsv_sparse_attn_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(o), _p(o_lo), _p(dout), _p(lse),
                                    _p(block_idx), _p(block_counts), _p(dq), _p(dk), _p(dv), _p(ws),
                                    ws.numel() * ws.element_size(), _stream(dev)), "dsv_sparse_attn_bwd")
@@ -326,11 +402,11 @@ def head_density(block_counts: Optional[torch.Tensor], *, topk: int, seq_len: in
     given (every list full).  Returns (density float32 [B, H], dense int32 [B, H])."""
     lib = load_library()
     if block_counts is not None:
-        _contig(block_counts)
-        if block_counts.dtype != torch.int32 or block_counts.dim() != 3:
+        if block_counts.dim() != 3:
             raise ValueError("block_counts must be int32 [B, H, N/Bq]")
         batch, heads = block_counts.shape[0], block_counts.shape[1]
-        dev = block_counts.device
+        _expect(block_counts, "block_counts", (batch, heads, seq_len // q_block), torch.int32)
+        dev = _dev(block_counts)
     else:
         if batch is None or heads is None:
             raise ValueError("without block_counts, pass batch and heads")
@@ -348,11 +424,16 @@ def block_recall(lse_selected: torch.Tensor, lse_all: torch.Tensor, *, q_block: 
     """Mean over each query block's rows of exp(lse_selected - lse_all): the true attention mass
     the selection captures (lse_all from the forward with every block selected)."""
     lib = load_library()
-    dev = _dev(lse_selected, lse_all)
-    _contig(lse_selected, lse_all)
-    if lse_selected.shape != lse_all.shape or lse_selected.dim() != 3 or lse_selected.dtype != torch.float32:
-        raise ValueError("lse tensors must be float32 [B, H, N] of one shape")
+    if lse_selected.dim() != 3:
+        raise ValueError("lse tensors must be float32 [B, H, N]")
     b, h, n = lse_selected.shape
+    _expect(lse_selected, "lse_selected", (b, h, n), torch.float32)
+    _expect(lse_all, "lse_all", (b, h, n), torch.float32)
+    if n % q_block:
+        raise ValueError("N must be a multiple of q_block")
+    if out is not None:
+        _expect(out, "out", (b, h, n // q_block), torch.float32)
+    dev = _dev(lse_selected, lse_all, out)
     prob = Problem(b, h, n, 64, q_block, q_block, 1, 1, DSV_F32, 0.0, 0.0)
     rec = out if out is not None else torch.empty((b, h, n // q_block), dtype=torch.float32, device=dev)
     _check(lib.dsv_block_recall(ctypes.byref(prob), _p(lse_selected), _p(lse_all), _p(rec), _stream(dev)),
@@ -366,11 +447,10 @@ def pack_kv(k, v, block_idx, qb_begin: int, qb_end: int, *, q_block: int, kv_blo
     (k_packed, v_packed [B,H,N,d], packed_blocks [B,H,N/Bk], packed_counts [B,H],
     packed_idx [B,H,qb_end-qb_begin,k])."""
     lib = load_library()
-    dev = _dev(k, v, block_idx)
-    _contig(k, v, block_idx)
-    b, h, n, d = k.shape
-    prob = make_problem(k, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1])
+    b, h, n, d = _attn_inputs(k, k, v, block_idx, q_block, kv_block)
     _check_counts(block_counts, block_idx)
+    dev = _dev(k, v, block_idx, block_counts)
+    prob = make_problem(k, q_block=q_block, kv_block=kv_block, topk=block_idx.shape[-1])
     ws = _workspace(int(lib.dsv_pack_kv_workspace_size(ctypes.byref(prob))), dev, workspace)
     kp, vp = torch.empty_like(k), torch.empty_like(v)
     blocks = torch.empty((b, h, n // kv_block), dtype=torch.int32, device=dev)

@@ -138,7 +138,7 @@ dsv_status timed(const char* name, hipStream_t st, F&& launch) {
 // ---------------------------------------------------------------- workspace layouts
 
 struct PredictWs {
-  size_t qlr, klr, scratch, lse, total;
+  size_t qlr, klr, scratch, lse, scores, total;
 };
 PredictWs predict_ws(const Prob& o) {
   PredictWs w{};
@@ -152,6 +152,8 @@ PredictWs predict_ws(const Prob& o) {
   } else {
     w.lse = off;
     off += align_up((size_t)o.bh() * o.n * sizeof(float));
+    w.scores = off;  // the fused representative call's scores before its selection (fp32 path)
+    off += align_up((size_t)o.bh() * o.nqb() * o.nkb() * sizeof(float));
   }
   w.total = off;
   return w;
@@ -364,6 +366,55 @@ dsv_status dsv_predict_representative(const dsv_problem* p, const void* q, const
   g_err.clear();
   if (rep_row < 0) return fail(DSV_ERR_INVALID_ARGUMENT, "rep_row must lie in [0, q_block)");
   return predict_impl(p, q, k, wq, wk, workspace, workspace_bytes, block_scores, rep_row, stream);
+}
+
+dsv_status dsv_predict_select_representative(const dsv_problem* p, const void* q, const void* k, const void* wq,
+                                             const void* wk, int32_t rep_row, void* workspace, size_t workspace_bytes,
+                                             int32_t* block_idx, void* stream) {
+  g_err.clear();
+  Prob o;
+  TRY(to_prob(p, o, true));
+  if (rep_row < 0 || rep_row >= o.bq) return fail(DSV_ERR_INVALID_ARGUMENT, "rep_row must lie in [0, q_block)");
+  if (o.dtype == DSV_BF16) {
+    if ((o.d != 64 && o.d != 128) || (o.r != 16 && o.r != 32) || (o.bq != 64 && o.bq != 128) || o.bk != 64 ||
+        o.n % 256)
+      return fail(DSV_ERR_UNSUPPORTED, "bf16 predictor needs d in {64,128}, r in {16,32}, Bq in {64,128}, Bk = 64, N % 256 == 0");
+  } else if (o.r > 64) {
+    return fail(DSV_ERR_UNSUPPORTED, "f32 predictor needs r <= 64");
+  }
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(wq, "wq", o.dtype == DSV_BF16 ? 2 : 4));
+  TRY(check_ptr(wk, "wk", o.dtype == DSV_BF16 ? 2 : 4));
+  TRY(check_ptr(block_idx, "block_idx", 4));
+  TRY(check_ptr(workspace, "workspace", kWsAlign));
+  const PredictWs w = predict_ws(o);
+  if (workspace_bytes < w.total)
+    return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "predict workspace needs " + std::to_string(w.total) + " bytes");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float q_scale = o.ps * 1.4426950408889634f;  // log2(e): Q~ carries the logit scale (as dsv_predict)
+  if (o.dtype == DSV_BF16) {
+    uint16_t* qlr = at<uint16_t>(workspace, w.qlr);
+    uint16_t* klr = at<uint16_t>(workspace, w.klr);
+    TRY_HIP(dsv::launch_proj_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(wq), qlr, o.bh(), o.n,
+                                  o.h, o.d, o.r, q_scale, st), "proj_kernel(q)");
+    TRY_HIP(dsv::launch_proj_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(wk), klr, o.bh(), o.n,
+                                  o.h, o.d, o.r, 1.f, st), "proj_kernel(k)");
+    TRY_HIP(dsv::launch_rep_select_bf16(qlr, klr, at<float>(workspace, w.scratch), block_idx, o.bh(), o.n, o.nkb(),
+                                        o.r, o.bq, rep_row, o.k, st), "rep_select_kernel");
+  } else {  // the plain VALU path for small fp32 problems: scores into the workspace, then top-k
+    float* qlr = at<float>(workspace, w.qlr);
+    float* klr = at<float>(workspace, w.klr);
+    float* sc = at<float>(workspace, w.scores);
+    TRY_HIP(dsv::launch_proj_f32(static_cast<const float*>(q), static_cast<const float*>(wq), qlr, o.bh(), o.n, o.h,
+                                 o.d, o.r, q_scale, st), "proj_kernel(q)");
+    TRY_HIP(dsv::launch_proj_f32(static_cast<const float*>(k), static_cast<const float*>(wk), klr, o.bh(), o.n, o.h,
+                                 o.d, o.r, 1.f, st), "proj_kernel(k)");
+    TRY_HIP(dsv::launch_rep_scores_f32(qlr, klr, at<float>(workspace, w.lse), sc, o.bh(), o.n, o.r, o.bq, o.bk,
+                                       0.6931471805599453f /* ln 2 */, rep_row, st), "scores_kernel");
+    TRY_HIP(dsv::launch_select_topk(sc, block_idx, o.bh() * o.nqb(), o.nkb(), o.k, st), "select_topk_kernel");
+  }
+  return DSV_OK;
 }
 
 dsv_status dsv_select_topk(const dsv_problem* p, const float* block_scores, int32_t* block_idx, void* stream) {

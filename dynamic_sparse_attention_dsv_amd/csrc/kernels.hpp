@@ -22,6 +22,11 @@ int score_items(int bh, int n, int bq, bool representative);
 // qlr is the scaled query projection: <qlr_i, klr_j> is the logit in log2 units.
 hipError_t launch_scores_bf16(const uint16_t* qlr, const uint16_t* klr, float* scratch, float* scores, int bh,
                               int n, int nkb, int r, int bq, int rep, hipStream_t st);
+// fused representative-row predictor and top-k (bf16): block_idx straight from the projections;
+// scratch = the predict workspace's slot area (rep_select_slots(bh, n, bq) * 64 * nkb floats)
+int rep_select_slots(int bh, int n, int bq);
+hipError_t launch_rep_select_bf16(const uint16_t* qlr, const uint16_t* klr, float* scratch, int32_t* idx, int bh,
+                                  int n, int nkb, int r, int bq, int rep, int k, hipStream_t st);
 hipError_t launch_rep_scores_f32(const float* qlr, const float* klr, float* lse, float* scores, int bh, int n,
                                  int r, int bq, int bk, float pred_scale, int rep, hipStream_t st);
 hipError_t launch_scores_f32(const float* qlr, const float* klr, float* lse, float* scores, int bh, int n, int r,

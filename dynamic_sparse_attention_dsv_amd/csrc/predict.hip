@@ -26,6 +26,7 @@
 //    bound by the vector ALU (one exp2 and one add per logit), not by MFMA or memory.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk_row.hpp"
 
 namespace dsv {
 
@@ -382,6 +383,107 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
                                  scores + (size_t)pbh * nqb * nkb, pqb0);
 }
 
+// ---------------------------------------------------------------- fused representative predict + top-k (bf16)
+//
+// The pages' fused matmul and top-k kernel with query grouping by one representative row per
+// group ([de] §2.B): the critical KV blocks of a query block are chosen from the logits of its
+// row qb * Bq + rep, and no score matrix is written.  For one row, ranking KV blocks by predicted
+// softmax mass equals ranking them by the in-block log-sum-exp of the row's logits (the row's
+// normaliser is common to all its blocks), so selection needs no other statistic.
+//
+// One workgroup per (head, 64 consecutive query blocks).  Wave w sweeps KV blocks
+// [w nkb/4, (w+1) nkb/4) for all 64 representative rows: one bf16 32x32x16 MFMA product of Q~ and
+// K_lr gives log2-unit logits, and each (row, block) key is m + log2 sum_j 2^(l_j - m) with m the
+// block's maximum, exact at any logit range (no fallback).  Keys go row-major into the workgroup's
+// scratch (64 x nkb floats); after one barrier each wave picks the top k of 16 rows with
+// topk_row and writes their ascending index lists.
+template <int R, int NPL>
+__global__ __launch_bounds__(256) void rep_select_bf16_kernel(const uint16_t* __restrict__ qlr,
+                                                              const uint16_t* __restrict__ klr,
+                                                              float* __restrict__ scratch,
+                                                              int32_t* __restrict__ idx, int n, int nkb, int bq,
+                                                              int rep, int k, int items) {
+  constexpr int NC = R / 16;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, c32 = lane & 31;
+  const int nqb = n / bq;
+  const int groups = (nqb + 63) / 64;  // work items per head
+  float* const keys = scratch + (size_t)blockIdx.x * 64 * nkb;
+  const int quarter = nkb / 4;  // nkb is a multiple of 4 (N % 256 == 0)
+  const int kb0 = wave * quarter, kb1 = kb0 + quarter;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int bh = item / groups;
+    const int qb0 = (item % groups) * 64;
+    const uint16_t* kh = klr + (size_t)bh * n * R;
+    // B operands = Q~^T of the two 32-row halves: lane holds the representative row of query block
+    // qb0 + h*32 + c32 (clamped past the last query block: computed, never selected)
+    bf16x8 qh[2][NC];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int qb = min(qb0 + h * 32 + c32, nqb - 1);
+      const uint16_t* qrow = qlr + ((size_t)bh * n + (size_t)qb * bq + rep) * R;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qh[h][c] = as_bf16x8(ld16(qrow + c * 16 + g * 8));
+    }
+    // A operands (K_lr rows, 8 consecutive r) of one KV block: 2 tiles x NC chunks
+    auto load_k = [&](int kb, u32x4 (&ka)[2][NC]) {
+      const uint16_t* kp = kh + (size_t)kb * 64 * R;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) ka[t][c] = ld16(kp + (size_t)(t * 32 + c32) * R + c * 16 + g * 8);
+    };
+    u32x4 ka[2][NC];
+    f32x16 acc[2][2];
+    load_k(kb0, ka);
+    for (int kb = kb0; kb < kb1; ++kb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          acc[h][t] = f32x16{};
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[h][t] = mfma32(as_bf16x8(ka[t][c]), qh[h][c], acc[h][t]);
+        }
+      if (kb + 1 < kb1) load_k(kb + 1, ka);
+      // lane holds 32 of the block's 64 logits for its row of half h; lane ^ 32 the other 32
+      float key2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float m = fmaxf(acc[h][0][0], acc[h][1][0]);
+#pragma unroll
+        for (int v = 1; v < 16; ++v) m = fmaxf(m, fmaxf(acc[h][0][v], acc[h][1][v]));
+        m = max_xor32(m);
+        float s0 = fast_exp2(acc[h][0][0] - m), s1 = fast_exp2(acc[h][1][0] - m);
+#pragma unroll
+        for (int v = 1; v < 16; ++v) {
+          s0 += fast_exp2(acc[h][0][v] - m);
+          s1 += fast_exp2(acc[h][1][v] - m);
+        }
+        key2[h] = m + fast_log2(sum_xor32(s0 + s1));
+      }
+      // lanes g = 0 write half 0's rows, lanes g = 1 half 1's
+      keys[(size_t)(g * 32 + c32) * nkb + kb] = g ? key2[1] : key2[0];
+    }
+    __threadfence_block();
+    __syncthreads();
+    // selection: wave w takes the item's rows [16w, 16w + 16)
+    for (int i = wave * 16; i < wave * 16 + 16; ++i) {
+      const int qb = qb0 + i;
+      if (qb >= nqb) break;
+      const float* row = keys + (size_t)i * nkb;
+      uint32_t key[NPL];
+#pragma unroll
+      for (int e = 0; e < NPL; ++e) {
+        const int kb = e * 64 + lane;
+        key[e] = kb < nkb ? max(order_key(row[kb]), 1u) : 0u;  // padding = 0, valid keys >= 1
+      }
+      topk_row<NPL>(key, k, idx + ((size_t)bh * nqb + qb) * k, lane);
+    }
+    __syncthreads();  // the next item's sweep refills the scratch
+  }
+}
+
 // ---------------------------------------------------------------- scores (f32, plain VALU)
 
 __global__ void row_lse_f32_kernel(const float* __restrict__ qlr, const float* __restrict__ klr,
@@ -541,6 +643,33 @@ hipError_t launch_scores_bf16(const uint16_t* qlr, const uint16_t* klr, float* s
   }
   SC(16, 64) SC(16, 128) SC(32, 64) SC(32, 128)
 #undef SC
+  return hipErrorInvalidValue;
+}
+
+int rep_select_items(int bh, int n, int bq) { return bh * ((n / bq + 63) / 64); }
+
+// Grid of the fused kernel: its per-workgroup scratch (64 x nkb floats) is 1/8 of a score slot's
+// (two halves of 256 x nkb), so eight of its workgroups fit in each slot of dsv_predict's workspace.
+int rep_select_slots(int bh, int n, int bq) {
+  const int items = rep_select_items(bh, n, bq);
+  const int cap = 8 * score_slots(score_items(bh, n, bq, false));
+  return items < cap ? items : cap;
+}
+
+hipError_t launch_rep_select_bf16(const uint16_t* qlr, const uint16_t* klr, float* scratch, int32_t* idx, int bh,
+                                  int n, int nkb, int r, int bq, int rep, int k, hipStream_t st) {
+  const int items = rep_select_items(bh, n, bq);
+  const int grid = rep_select_slots(bh, n, bq);
+  const int npl = (nkb + 63) / 64;
+#define RS(R_, N_)                                                                                             \
+  if (r == R_ && npl <= N_) {                                                                                  \
+    hipLaunchKernelGGL((rep_select_bf16_kernel<R_, N_>), dim3(grid), dim3(256), 0, st, qlr, klr, scratch, idx, n, \
+                       nkb, bq, rep, k, items);                                                                \
+    return hipGetLastError();                                                                                  \
+  }
+  RS(16, 1) RS(16, 2) RS(16, 4) RS(16, 8) RS(16, 16) RS(16, 32) RS(16, 64)
+  RS(32, 1) RS(32, 2) RS(32, 4) RS(32, 8) RS(32, 16) RS(32, 32) RS(32, 64)
+#undef RS
   return hipErrorInvalidValue;
 }
 

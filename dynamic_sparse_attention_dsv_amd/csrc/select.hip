@@ -8,23 +8,14 @@
 // ties toward the smaller block index, and written in ascending block order.
 //
 // gfx950 design: one wave64 per query block.  Lane l holds blocks e*64 + l
-// (e = 0 .. NPL-1), loaded coalesced.  Scores become order-preserving 32-bit
-// keys; the k-th largest key is found by an MSB-first bit search whose counts
-// are wave ballots + scalar popcounts.  Ties at the threshold are resolved by
-// block index through a running prefix count in ascending block order, so the
-// output positions fall out of the same ballots.  The kernel is bound by the
-// HBM read of the score rows.
+// (e = 0 .. NPL-1), loaded coalesced, as order-preserving 32-bit keys; the
+// wave-level search of topk_row.hpp picks the k largest.  The kernel is bound by
+// the HBM read of the score rows.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk_row.hpp"
 
 namespace dsv {
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
 template <int NPL>
 __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
@@ -40,35 +31,7 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
     const int kb = e * 64 + lane;
     key[e] = kb < nkb ? max(order_key(src[kb]), 1u) : 0u;  // padding = 0, valid keys >= 1
   }
-  // MSB-first search for T = the k-th largest key: the largest T with count(key >= T) >= k.
-  // Valid keys are >= 1, so padding never counts (k <= nkb valid keys exist).
-  uint32_t prefix = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = prefix | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < NPL; ++e) cnt += popc64(__ballot(key[e] >= cand));
-    if (cnt >= k) prefix = cand;
-  }
-  const uint32_t T = prefix;
-  int gt = 0;
-#pragma unroll
-  for (int e = 0; e < NPL; ++e) gt += popc64(__ballot(key[e] > T));
-  const int need = k - gt;  // number of ties at T to keep, smallest block index first
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int32_t* dst = idx + (size_t)row * k;
-  int taken = 0, ties_seen = 0;
-#pragma unroll
-  for (int e = 0; e < NPL; ++e) {
-    const bool tie = key[e] == T && key[e] != 0u;
-    const uint64_t tie_m = __ballot(tie);
-    const int tie_rank = ties_seen + popc64(tie_m & lt_mask);
-    const bool sel = key[e] > T || (tie && tie_rank < need);
-    const uint64_t sel_m = __ballot(sel);
-    if (sel) dst[taken + popc64(sel_m & lt_mask)] = e * 64 + lane;
-    taken += popc64(sel_m);
-    ties_seen += popc64(tie_m);
-  }
+  topk_row<NPL>(key, k, idx + (size_t)row * k, lane);
 }
 
 // ---------------------------------------------------------------- mass-threshold selection

@@ -13,6 +13,7 @@
  * The four compute calls, in pipeline order:
  *   dsv_predict          predicted attention mass per (query block, KV block)
  *   dsv_predict_representative  (alternative) the mass of one representative row per query block
+ *   dsv_predict_select_representative  (alternative) that predictor fused with top-k: indices only
  *   dsv_select_topk      the k most important KV blocks of each query block
  *   dsv_select_mass      (alternative) the fewest blocks carrying a fraction tau of the score
  *   dsv_sparse_attn_fwd  softmax attention restricted to the selected blocks
@@ -148,6 +149,28 @@ dsv_status dsv_predict(const dsv_problem* p, const void* q, const void* k, const
 dsv_status dsv_predict_representative(const dsv_problem* p, const void* q, const void* k, const void* wq,
                                       const void* wk, int32_t rep_row, void* workspace, size_t workspace_bytes,
                                       float* block_scores, void* stream);
+
+/*
+ * dsv_predict_select_representative -- the fused predictor and top-k selection of the pages
+ * ([de] §2.B: one kernel does the low-rank matmul and the top-k, without an O(S^2) intermediate;
+ * query grouping: the critical pairs of a group of neighbouring queries are estimated for one
+ * representative).  block_idx[b,h,qb] = the k KV blocks with the largest predicted softmax mass
+ * of the single query row i = qb * Bq + rep_row (the scores of dsv_predict_representative), ties
+ * toward the smaller block index, written ascending -- equal to dsv_predict_representative
+ * followed by dsv_select_topk up to floating-point rounding of near-equal masses.  The bf16
+ * instance ranks each row's blocks by their in-block log-sum-exp of logits (the same order as
+ * the mass, since the row's normaliser is common) inside the predictor's sweep and writes no
+ * score matrix; the fp32 instance computes the scores into the workspace and selects from them.
+ *
+ *   q, k, wq, wk  as dsv_predict;  rep_row  0 <= rep_row < Bq;  k = problem.topk
+ *   workspace     >= dsv_predict_workspace_size(p) bytes; on return it holds Q~ and K_lr as for
+ *                 dsv_predict (the rest is scratch)
+ *   block_idx     [B, H, N/Bq, k] int32 output
+ * The bf16 instance needs the same sizes as dsv_predict.
+ */
+dsv_status dsv_predict_select_representative(const dsv_problem* p, const void* q, const void* k, const void* wq,
+                                             const void* wk, int32_t rep_row, void* workspace, size_t workspace_bytes,
+                                             int32_t* block_idx, void* stream);
 
 /*
  * dsv_select_topk -- critical-KV selection ([de] §2.B, top-k selection;

@@ -37,12 +37,13 @@ def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
 
 
-def check_indices(gpu_idx: np.ndarray, oracle_scores: np.ndarray, k: int):
-    """Index criterion.  Rows whose oracle gap s_(k) - s_(k+1) > GAP must match the
+def check_indices(gpu_idx: np.ndarray, oracle_scores: np.ndarray, k: int, gap_rule: float = GAP):
+    """Index criterion.  Rows whose oracle gap s_(k) - s_(k+1) > gap_rule must match the
     oracle's selection exactly; every other row must be a valid near-tie choice:
-    each selected block scores >= s_(k) - GAP and each dropped block <= s_(k+1) + GAP.
+    each selected block scores >= s_(k) - gap_rule and each dropped block <= s_(k+1) + gap_rule.
     Also checks every row is ascending and duplicate-free.  Returns the coverage
     (fraction of rows under the exact rule)."""
+    GAP = gap_rule  # noqa: N806
     s = oracle_scores.reshape(-1, oracle_scores.shape[-1])
     g = gpu_idx.reshape(-1, gpu_idx.shape[-1]).astype(np.int64)
     assert np.all(np.diff(g, axis=1) > 0), "rows must be strictly ascending"
