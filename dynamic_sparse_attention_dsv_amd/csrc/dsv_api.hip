@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -134,6 +135,23 @@ dsv_status timed(const char* name, hipStream_t st, F&& launch) {
   return hip_status(e, name);
 }
 #define TRY_HIP(x, name) TRY(timed(name, st, [&] { return (x); }))
+
+// The opt-in device check of the block lists (DSV_DEBUG_VALIDATE=1, read at each call).
+bool debug_validate() {
+  const char* v = std::getenv("DSV_DEBUG_VALIDATE");
+  return v && std::strcmp(v, "1") == 0;
+}
+
+dsv_status check_lists(const Prob& o, const int32_t* block_idx, const int32_t* block_counts, hipStream_t st) {
+  if (!debug_validate()) return DSV_OK;
+  uint32_t bad = 0;
+  TRY(hip_status(dsv::check_block_lists(block_idx, block_counts, o.bh() * o.nqb(), o.nkb(), o.k, st, &bad),
+                 "DSV_DEBUG_VALIDATE list check"));
+  if (bad)
+    return fail(DSV_ERR_INVALID_ARGUMENT, "DSV_DEBUG_VALIDATE: " + std::to_string(bad) +
+                                              " query block(s) use block indices that are out of range or repeated");
+  return DSV_OK;
+}
 
 // ---------------------------------------------------------------- workspace layouts
 
@@ -574,6 +592,7 @@ dsv_status dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* 
       return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "forward workspace needs " + std::to_string(need) + " bytes");
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY(check_lists(o, block_idx, block_counts, st));
   if (o.dtype == DSV_BF16) {
     TRY_HIP(dsv::launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                       static_cast<const uint16_t*>(v), block_idx, block_counts,
@@ -618,6 +637,7 @@ dsv_status dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* 
   if (workspace_bytes < w.total)
     return fail(DSV_ERR_WORKSPACE_TOO_SMALL, "backward workspace needs " + std::to_string(w.total) + " bytes");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY(check_lists(o, block_idx, block_counts, st));
   int32_t* col_ptr = at<int32_t>(workspace, w.col_ptr);
   int32_t* rows = at<int32_t>(workspace, w.rows);
   int32_t* order = o.dtype == DSV_BF16 ? at<int32_t>(workspace, w.order) : nullptr;

@@ -96,6 +96,11 @@ hipError_t launch_pack_kv(const void* k, const void* v, const int32_t* idx, cons
 constexpr size_t kPackScratchEntries = (size_t)1 << 18;  // B * H * N/Bk at most (1 MiB per array)
 hipError_t pack_scratch(int32_t** flags, int32_t** pos);
 
+// debug check of block lists (validate.hip): counts the query blocks whose used entries are out of
+// range or repeated into *bad_rows.  Blocks: it synchronises `st` and copies the count to the host.
+hipError_t check_block_lists(const int32_t* idx, const int32_t* cnts, int rows, int nkb, int k, hipStream_t st,
+                             uint32_t* bad_rows);
+
 // peak-rate probes (probe.hip): kind 0/1 MFMA 32x32x16 bf16/fp16 (flop), 2 v_exp_f32 (results),
 // 3 HBM copy (bytes read + written), 4 HBM read (bytes).  *work is the launch's amount of that work.
 constexpr int kProbeMaxCus = 1024;

@@ -40,9 +40,28 @@
  *   same thread).  A failed launch returns DSV_ERR_HIP.  Non-finite inputs are
  *   not checked: they propagate into the outputs.
  * State.  The library has no global mutable state (only the optional per-thread
- *   timing record below); calls are thread-safe and may run concurrently on
+ *   timing record below, and the device arrays of dsv_pack_kv_noalloc and of the
+ *   debug check below); calls are thread-safe and may run concurrently on
  *   different streams with different buffers.  All calls are
  *   deterministic (bitwise repeatable for the same inputs and problem).
+ * Block lists.  Every call that takes block_idx uses, per query block, its first
+ *   block_counts[qb] entries (clamped to [0, k]) or all k when block_counts is
+ *   NULL.  Results are defined only when those entries are distinct indices in
+ *   [0, N/Bk) (the selection calls always emit such lists; entries past a count,
+ *   such as dsv_select_mass's -1 padding, are never read).  For any other list
+ *   every access still stays inside the tensors -- an out-of-range entry is
+ *   clamped into range by the forward and the dQ kernel and skipped by the
+ *   dK/dV kernel's transposed lists, and a repeated entry is used twice by the
+ *   forward and dQ but once by dK/dV -- but the outputs are unspecified, and the
+ *   backward is then not the forward's gradient.  (dsv_pack_kv states its own,
+ *   defined treatment of out-of-range entries.)
+ * Debug check.  With the environment variable DSV_DEBUG_VALIDATE=1 (read at each
+ *   call), dsv_sparse_attn_fwd and dsv_sparse_attn_bwd first check the lists on
+ *   the device and return DSV_ERR_INVALID_ARGUMENT, having launched nothing else,
+ *   if a query block's used entries are out of range or repeated.  The check
+ *   BLOCKS (it waits for the stream) and keeps its count in a device word of the
+ *   library, so checked calls must not overlap in time on one GPU.  It is meant
+ *   for debugging, not for timed runs.
  */
 #ifndef DSV_H_
 #define DSV_H_
@@ -284,15 +303,13 @@ size_t dsv_sparse_attn_fwd_workspace_size(const dsv_problem* p);
 
 /*
  * dsv_sparse_attn_fwd -- exact softmax attention over the selected KV blocks
- * only (the sparse attention kernels of [es] §2.B and [de] §2.B, used for
+ * only (the custom sparse attention kernels of [es] §3 and [de] §3, used for
  * sparse training, [de] §2.A stage 2).  For each query row i of block qb, with
  * J = the keys of the blocks in block_idx[b,h,qb]:
  *   s_ij = sm_scale <q_i, k_j>,  O_i = sum_{j in J} softmax_J(s_i)_j v_j,
  *   lse_i = log sum_{j in J} exp(s_ij)   (natural log)
- * block_idx rows must hold k distinct indices in [0, N/Bk); their order does not
- * matter (dsv_select_topk emits them ascending).  Indices are not validated:
- * an out-of-range index is clamped into range (the result is then meaningless
- * but no memory outside the tensors is touched); duplicates count twice.
+ * The list entries used must be distinct indices in [0, N/Bk) (see "Block lists"
+ * above); their order does not matter (dsv_select_topk emits them ascending).
  *
  *   q, k, v     [B, H, N, d] inputs;  block_idx [B, H, N/Bq, k]
  *   block_counts  optional [B, H, N/Bq] int32, or NULL: query block qb uses the first

@@ -352,11 +352,17 @@ def pack_rows(x: np.ndarray, blocks: np.ndarray, count: np.ndarray, bk: int) -> 
 # --------------------------------------------------------------------------
 
 
-def selected_keys(idx_row: np.ndarray, bk: int) -> np.ndarray:
+def selected_keys(idx_row: np.ndarray, bk: int, nkb: Optional[int] = None) -> np.ndarray:
     """Token indices of the selected KV blocks, block by block in list order (negative
-    entries pad a ragged list and select nothing, R13)."""
+    entries pad a ragged list and select nothing, R13).
+
+    R7: a list names each selected block once.  With ``nkb`` given, a list whose non-negative
+    entries repeat a block or reach past the last block (>= nkb) is rejected: the attention is
+    defined only for distinct in-range lists."""
     idx_row = np.asarray(idx_row, np.int64)
     idx_row = idx_row[idx_row >= 0]
+    if nkb is not None and (np.any(idx_row >= nkb) or np.unique(idx_row).size != idx_row.size):
+        raise ValueError(f"block list {idx_row.tolist()} repeats a block or exceeds the {nkb} KV blocks (R7)")
     return (idx_row[:, None] * bk + np.arange(bk)[None, :]).reshape(-1)
 
 
@@ -366,7 +372,7 @@ def attn_fwd_qblock(q_blk, k, v, idx_row, bk: int, sm_scale: float) -> Tuple[np.
     Returns (O [Bq, d], LSE [Bq]) with LSE_i = log sum_j exp(sm_scale <q_i, k_j>).  An empty
     list (R13) defines O = 0 and LSE = -inf.
     """
-    keys = selected_keys(idx_row, bk)
+    keys = selected_keys(idx_row, bk, np.shape(k)[0] // bk)
     if keys.size == 0:
         return np.zeros((np.shape(q_blk)[0], np.shape(v)[-1])), np.full(np.shape(q_blk)[0], -np.inf)
     s = sm_scale * (np.asarray(q_blk, np.float64) @ np.asarray(k, np.float64)[keys].T)
@@ -401,7 +407,7 @@ def attn_bwd_qblock(q_blk, k, v, do_blk, idx_row, bk: int, sm_scale: float):
       dQ = sm_scale dS K_J,   dK_J = sm_scale dS^T Q.
     Returns (dQ [Bq, d], dK_J [|J|, d], dV_J [|J|, d], J); an empty list has no gradient.
     """
-    keys = selected_keys(idx_row, bk)
+    keys = selected_keys(idx_row, bk, np.shape(k)[0] // bk)
     if keys.size == 0:
         dq = np.zeros(np.shape(q_blk))
         return dq, np.zeros((0, np.shape(k)[-1])), np.zeros((0, np.shape(v)[-1])), keys

@@ -499,6 +499,25 @@ def test_padded_block_lists_select_nothing_extra():
         assert np.array_equal(a, b)
 
 
+def test_attention_is_defined_only_for_distinct_in_range_lists():
+    # R7 and the block-list contract: a list names each selected block once, within [0, N/Bk);
+    # negative entries are padding (R13).  A repeated or out-of-range entry is refused by the
+    # forward and the backward alike (the GPU leaves such lists unspecified and can check them).
+    rng = _rng(31)
+    n, d, bq, bk = 256, 8, 64, 64
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    good = np.array([0, 3, -1], np.int32)
+    O.attn_fwd_qblock(q[:bq], k, v, good, bk, 0.5)
+    O.attn_bwd_qblock(q[:bq], k, v, do[:bq], good, bk, 0.5)
+    for bad in (np.array([1, 1], np.int32), np.array([0, 4], np.int32), np.array([2, -1, 2], np.int32)):
+        with pytest.raises(ValueError):
+            O.attn_fwd_qblock(q[:bq], k, v, bad, bk, 0.5)
+        with pytest.raises(ValueError):
+            O.attn_bwd_qblock(q[:bq], k, v, do[:bq], bad, bk, 0.5)
+        with pytest.raises(ValueError):
+            O.sparse_attn_fwd(q[None, None], k[None, None], v[None, None], np.tile(bad, (1, 1, n // bq, 1)), bq, bk, 0.5)
+
+
 def test_empty_block_list_defines_zero_output_and_gradient():
     rng = np.random.default_rng(4)
     n, d, bq, bk = 128, 8, 64, 64
