@@ -30,9 +30,10 @@ CSRC = os.path.join(HERE, "csrc")
 
 # library timing name -> (device kernel name prefix, source files it is compiled from)
 KERNELS = {
-    "proj_kernel(q)": ("proj_bf16_kernel", ["predict.hip", "common.hpp"]),
-    "scores_kernel": ("scores_bf16_kernel", ["predict.hip", "common.hpp"]),
-    "select_topk_kernel": ("select_topk_kernel", ["select.hip", "common.hpp"]),
+    "proj_kernel(q)": ("proj_bf16_kernel", ["predict.hip", "common.hpp", "topk_row.hpp"]),
+    "scores_kernel": ("scores_bf16_kernel", ["predict.hip", "common.hpp", "topk_row.hpp"]),
+    "rep_select_kernel": ("rep_select_bf16_kernel", ["predict.hip", "common.hpp", "topk_row.hpp"]),
+    "select_topk_kernel": ("select_topk_kernel", ["select.hip", "common.hpp", "topk_row.hpp"]),
     "attn_fwd_kernel": ("attn_fwd_bf16_kernel", ["attn_fwd.hip", "common.hpp"]),
     "bwd_pre_kernel": ("bwd_pre_bf16_kernel", ["attn_bwd.hip", "common.hpp"]),
     "attn_bwd_dkdv_kernel": ("attn_bwd_dkdv_bf16_kernel", ["attn_bwd.hip", "common.hpp"]),
