@@ -93,7 +93,11 @@ def measured_traffic(cfg, timing_name):
     if not os.path.exists(path):
         return None, None
     with open(path) as fh:
-        rec = json.load(fh).get("kernels", {}).get(timing_name)
+        summary = json.load(fh)
+    # counters of another input generator (another selection) do not describe this run
+    if not summary.get("workload", "").endswith(f"{cfg.generator} inputs"):
+        return None, None
+    rec = summary.get("kernels", {}).get(timing_name)
     if rec is None or rec.get("source_sha256") != source_hash(timing_name):
         return None, None
     return rec["read_bytes"] + rec["write_bytes"], os.path.relpath(path, ROOT)
@@ -125,10 +129,15 @@ def cpu_baseline(cfg, inp, target_s):
                 break
         dt = time.perf_counter() - t0
     flops = 14.0 * done * cfg.q_block * cfg.topk * cfg.kv_block * cfg.head_dim
+    # heads and query blocks are independent, so the whole layer scales linearly from the sample
+    layer_s = dt / done * cfg.nqb * cfg.heads * cfg.batch
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"head 0 of {cfg.name}, {done} of {cfg.nqb} query blocks: projections, full-key predictor "
                       f"sweep, top-k, sparse forward and backward in float64 NumPy ({dt:.1f} s)",
-            "seconds": dt, "query_blocks": done}
+            "seconds": dt, "query_blocks": done,
+            "extrapolated_layer_s": layer_s,
+            "extrapolated_layer_note": f"one full layer ({cfg.batch * cfg.heads} heads x {cfg.nqb} query blocks) "
+                                       "at the sample's rate, extrapolated (linear in heads and query blocks)"}
 
 
 def main():
