@@ -43,7 +43,8 @@ def test_summary_scales_counters_by_the_calibration_copy(tmp_path):
 def test_bench_reports_traffic_only_for_an_unchanged_kernel(tmp_path, monkeypatch):
     cfg = get_config("C5")
     (tmp_path / "profiles").mkdir()
-    rec = {"kernels": {"attn_fwd_kernel": {"read_bytes": 5.0, "write_bytes": 1.0,
+    rec = {"workload": f"C5: ..., {cfg.generator} inputs",
+           "kernels": {"attn_fwd_kernel": {"read_bytes": 5.0, "write_bytes": 1.0,
                                            "source_sha256": ps.source_hash("attn_fwd_kernel")},
                        "attn_bwd_dq_kernel": {"read_bytes": 5.0, "write_bytes": 1.0, "source_sha256": "0" * 64}}}
     (tmp_path / "profiles" / "c5_kernel_traffic.json").write_text(json.dumps(rec))
@@ -51,6 +52,10 @@ def test_bench_reports_traffic_only_for_an_unchanged_kernel(tmp_path, monkeypatc
     assert bench.measured_traffic(cfg, "attn_fwd_kernel")[0] == 6.0
     assert bench.measured_traffic(cfg, "attn_bwd_dq_kernel") == (None, None)   # sources changed since
     assert bench.measured_traffic(cfg, "scores_kernel") == (None, None)        # never measured
+    other = "g2" if cfg.generator == "g1" else "g1"
+    rec["workload"] = f"C5: ..., {other} inputs"
+    (tmp_path / "profiles" / "c5_kernel_traffic.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic(cfg, "attn_fwd_kernel") == (None, None)      # counters of other inputs
 
 
 def test_counter_summary_ratios(tmp_path):
