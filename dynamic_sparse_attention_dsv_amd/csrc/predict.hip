@@ -127,29 +127,21 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
   const int nqb = n / BQ;
   const int items_per_head = REP ? (nqb + kScoreRows - 1) / kScoreRows : n / kScoreRows;
 
-  // finalize: score[qb, kb] = sum_{i in qb} mass[kb][i] / T_i (log domain on the exact path), all
-  // at once after a sweep.  chunks of 64 KV blocks: lane <-> kb, wave w sums its rows [64w, 64w+64).
-  auto finalize_now = [&](const float* sl, const float* rs_all, bool exact, float* sc_head, int qb0) {
+  // Exact-path finalisation, at once after the item's sweep: score[qb, kb] = sum_{i in qb}
+  // 2^(t[kb][i] - log2 T_i) over the log-domain block masses t.  Chunks of 64 KV blocks: lane <-> kb,
+  // wave w sums its rows [64w, 64w+64).
+  auto finalize_exact = [&](const float* sl, const float* rs_all, float* sc_head, int qb0) {
     for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
       const int kb = kb0 + lane;
       float acc0 = 0.f, acc1 = 0.f;
       if (kb < nkb) {
         const float* src = sl + (size_t)kb * kScoreRows + wave * 64;
         const float* rs = rs_all + wave * 64;
-        if (!exact) {
 #pragma unroll
-          for (int i = 0; i < 64; i += 4) {
-            const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
-            acc0 = fmaf(tv[0], rs[i], fmaf(tv[1], rs[i + 1], acc0));
-            acc1 = fmaf(tv[2], rs[i + 2], fmaf(tv[3], rs[i + 3], acc1));
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 64; i += 4) {
-            const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
-            acc0 += fast_exp2(tv[0] - rs[i]) + fast_exp2(tv[1] - rs[i + 1]);
-            acc1 += fast_exp2(tv[2] - rs[i + 2]) + fast_exp2(tv[3] - rs[i + 3]);
-          }
+        for (int i = 0; i < 64; i += 4) {
+          const f32x4 tv = *reinterpret_cast<const f32x4*>(src + i);
+          acc0 += fast_exp2(tv[0] - rs[i]) + fast_exp2(tv[1] - rs[i + 1]);
+          acc1 += fast_exp2(tv[2] - rs[i + 2]) + fast_exp2(tv[3] - rs[i + 3]);
         }
       }
       part_s[wave][lane] = acc0 + acc1;
@@ -370,7 +362,7 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
       continue;
     }
     if (exact) {  // finalised at once (its masses are log-domain); nothing stays pending
-      finalize_now(slot, row_s[buf], true, scores + (size_t)bh * nqb * nkb, row0 / BQ);
+      finalize_exact(slot, row_s[buf], scores + (size_t)bh * nqb * nkb, row0 / BQ);
       pend = false;
     } else {
       pend = true;
@@ -379,8 +371,31 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
       buf ^= 1;
     }
   }
-  if (!REP && pend) finalize_now(slots + (size_t)(buf ^ 1) * slot_elems, row_s[buf ^ 1], false,
-                                 scores + (size_t)pbh * nqb * nkb, pqb0);
+  if (!REP && pend) {
+    // The slot's last fast item: the same steps as the deferred finalisation, in the same order, so
+    // that no score depends on which item of a slot came last (nor on the grid, the head count of
+    // the call or the device's compute units).
+    const float* const pslot = slots + (size_t)(buf ^ 1) * slot_elems;
+    const float* const prs = row_s[buf ^ 1];
+    float* const psc = scores + (size_t)pbh * nqb * nkb;
+    const int P = nchw * (kScoreRows / 16);
+    float fa = 0.f;
+#pragma unroll 4
+    for (int p = 0; p < P; ++p) {  // P is a multiple of 16: four steps' loads are issued together
+      const int kbs = (wave + 4 * (p >> 4)) * 64 + lane, r0 = (p & 15) * 16;
+      const float* src = pslot + (size_t)min(kbs, nkb - 1) * kScoreRows + r0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * u);
+        const f32x4 w = *reinterpret_cast<const f32x4*>(prs + r0 + 4 * u);
+        fa = fmaf(v[3], w[3], fmaf(v[2], w[2], fmaf(v[1], w[1], fmaf(v[0], w[0], fa))));
+      }
+      if (((p + 1) & (BQ / 16 - 1)) == 0) {  // the query block's last sixteen rows
+        if (kbs < nkb) psc[(size_t)(pqb0 + r0 / BQ) * nkb + kbs] = fa;
+        fa = 0.f;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- fused representative predict + top-k (bf16)

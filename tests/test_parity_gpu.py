@@ -439,6 +439,40 @@ def test_predictor_extreme_logits_use_the_exact_fallback(case):
     assert np.all(sg[:, 5] > 0.99 * bq)  # block 5 takes essentially all the mass
 
 
+@pytest.mark.parametrize("r,bq", [(32, 128), (16, 64)])
+def test_predictor_scores_do_not_depend_on_the_heads_sharing_a_call(r, bq):
+    # The score sweep's persistent workgroups take items (256 query rows of one head) in turn.  A
+    # workgroup finalises an item during its next item's sweep, or after its loop when the item was
+    # its last; which items come last depends on the grid, the call's head count and the device.
+    # Both finalisations must take the same arithmetic in the same order, so that a head's scores,
+    # and with them its selection, are bit-identical whether it is predicted with all heads (2304
+    # items: on a 256-CU device every workgroup runs two or three), in groups of 8 heads (128
+    # items, each the last of its workgroup) or alone.
+    heads, n, d, bk, topk = 144, 4096, 64, 64, 7
+    rng = np.random.default_rng(53)
+    from workloads.generator import bf16_bits_from_f32
+    q = bf16_bits_from_f32(rng.standard_normal((1, heads, n, d)).astype(np.float32))
+    k = bf16_bits_from_f32(rng.standard_normal((1, heads, n, d)).astype(np.float32))
+    w = bf16_bits_from_f32((rng.standard_normal((2, heads, d, r)) / np.sqrt(d)).astype(np.float32))
+    t = {nm: to_dev(a) for nm, a in (("q", q), ("k", k), ("wq", w[0]), ("wk", w[1]))}
+    kw = dict(q_block=bq, kv_block=bk)
+    full = dsv.predict(t["q"], t["k"], t["wq"], t["wk"], **kw)
+    grouped = torch.empty_like(full)
+    for h0 in range(0, heads, 8):
+        sl = slice(h0, h0 + 8)
+        dsv.predict(t["q"][:, sl], t["k"][:, sl], t["wq"][sl], t["wk"][sl], out=grouped[:, sl], **kw)
+    alone = [dsv.predict(t["q"][:, h:h + 1], t["k"][:, h:h + 1], t["wq"][h:h + 1], t["wk"][h:h + 1], **kw)
+             for h in (0, heads - 1)]
+    idx_full = dsv.select_topk(full, topk, **kw)
+    idx_grouped = dsv.select_topk(grouped, topk, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(full, grouped)
+    assert torch.equal(full[:, :1], alone[0]) and torch.equal(full[:, -1:], alone[1])
+    assert torch.equal(idx_full, idx_grouped)
+    np.testing.assert_allclose(to_f64(full).sum(axis=-1), bq, rtol=1e-5)
+    log(f"[parity] predictor r={r} bq={bq}: {heads} heads bit-equal alone, in groups of 8 and all at once")
+
+
 def test_autograd_function_gradients_match_the_oracle():
     # DSVAttention.apply: predict -> select -> training forward, and the sparse backward through
     # autograd.  The q, k, v gradients must match the oracle's backward on the GPU-chosen indices
