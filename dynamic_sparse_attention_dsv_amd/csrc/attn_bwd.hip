@@ -456,7 +456,7 @@ __global__ __launch_bounds__(BQ * 2, (kMinWavesPerSimd<D, BQ>)) void attn_bwd_dq
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dvec,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ dq,
     const uint32_t* __restrict__ absmax /* per head max |.| bits: [0,bh) K, [bh,2bh) Q, [2bh,3bh) V */, int bh_total,
-    int n, int topk, int nwg, float c, float sm_scale) {
+    int n, int topk, float c, float sm_scale) {
   constexpr int WAVES = BQ / 32;
   constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
   // one array per buffer, so the compiler can see that the asynchronous copy into
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(BQ * 2, (kMinWavesPerSimd<D, BQ>)) void attn_bwd_dq
   __shared__ __attribute__((aligned(16))) uint16_t V0[64 * D], V1[64 * D];
 
   const int nqb = n / BQ;
-  const int id = xcd_remap(blockIdx.x, nwg);
+  const int id = blockIdx.x;  // plain dispatch order, as the forward (measured faster than the remap)
   const int bh = id / nqb, qb = id % nqb;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
@@ -787,7 +787,7 @@ hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* v, const uint16
 #define DQ(D_, BQ_)                                                                                          \
   if (d == D_ && bq == BQ_) {                                                                                \
     hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D_, BQ_>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, f.k16, v, dout,  \
-                       lse2, dvec, idx, cnts, dq, f.absmax, bh, n, topk, nwg, c, sm_scale);                  \
+                       lse2, dvec, idx, cnts, dq, f.absmax, bh, n, topk, c, sm_scale);                       \
     return hipGetLastError();                                                                                \
   }
   DQ(64, 64) DQ(64, 128) DQ(128, 64) DQ(128, 128)

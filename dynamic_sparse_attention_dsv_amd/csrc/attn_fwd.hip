@@ -10,7 +10,8 @@
 //  * one workgroup per (b, h, qb), Bq/32 waves, each wave owns 32 query rows;
 //    registers are capped so that two waves share each SIMD (one's softmax
 //    VALU work overlaps the other's MFMAs);
-//    workgroup ids are remapped so that one XCD works on one head at a time;
+//    workgroups run in plain dispatch order, so that the eight XCDs work on one head
+//    at a time (its gathered K/V tiles then stay within the Infinity Cache);
 //  * Q stays in registers as the B operand of S^T = K Q^T (v_mfma 32x32x16);
 //  * each selected KV block is gathered into swizzled LDS tiles (K and V both
 //    row-major, as stored) by direct global->LDS loads, double-buffered: the
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(BQ * 2, (kMinWavesPerSimd<D, BQ>)) void attn_fwd_bf
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnts, uint16_t* __restrict__ o,
     float* __restrict__ lse, uint16_t* __restrict__ o_lo /* rounding residual of O (PV16) */,
-    const uint32_t* __restrict__ vmax /* PV16: per-head max |V| (float bits) */, int n, int topk, int nwg,
+    const uint32_t* __restrict__ vmax /* PV16: per-head max |V| (float bits) */, int n, int topk,
     float c /* sm_scale * log2(e) */) {
   constexpr int WAVES = BQ / 32;
   constexpr int NI = 2 * 64 * D / 512;  // global->LDS instructions per KV block (K and V tiles)
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(BQ * 2, (kMinWavesPerSimd<D, BQ>)) void attn_fwd_bf
   __shared__ __attribute__((aligned(16))) uint16_t V0[64 * D], V1[64 * D];
 
   const int nqb = n / BQ;
-  const int id = xcd_remap(blockIdx.x, nwg);
+  const int id = blockIdx.x;  // measured faster here than the per-XCD remap of dK/dV
   const int bh = id / nqb, qb = id % nqb;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
@@ -333,10 +334,10 @@ hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint
   if (d == D_ && bq == BQ_) {                                                                             \
     if (o_lo)                                                                                             \
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, true>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v16, idx, \
-                         cnts, o, lse, o_lo, vmax, n, topk, nwg, c);                                      \
+                         cnts, o, lse, o_lo, vmax, n, topk, c);                                           \
     else                                                                                                  \
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, BQ_, false>), dim3(nwg), dim3(BQ_ * 2), 0, st, q, k, v, \
-                         idx, cnts, o, lse, o_lo, vmax, n, topk, nwg, c);                                 \
+                         idx, cnts, o, lse, o_lo, vmax, n, topk, c);                                      \
     return hipGetLastError();                                                                             \
   }
   FWD(64, 64) FWD(64, 128) FWD(128, 64) FWD(128, 128)

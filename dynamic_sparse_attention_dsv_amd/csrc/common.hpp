@@ -306,8 +306,10 @@ __device__ __forceinline__ int list_len(const int32_t* cnts, size_t row, int k) 
 
 // Map a workgroup id so that consecutive logical ids run on the same XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); with this
-// remap XCD x processes the contiguous logical range [x*per, (x+1)*per), so the
-// work sharing one head's K/V tiles shares that XCD's L2.
+// remap XCD x processes the contiguous logical range [x*per, (x+1)*per).  The
+// dK/dV kernel uses it: the ~64 KV-block columns an XCD runs together are then
+// neighbours in the heaviest-first order of one head and share its Q/dO tiles in
+// that XCD's L2.
 __device__ __forceinline__ int xcd_remap(int id, int n) {
   const int per = n / 8;
   if (per == 0 || id >= per * 8) return id;
