@@ -10,7 +10,7 @@
 
 namespace dsv {
 
-static __device__ __align__(256) uint32_t bad_lists[64];  // [0] counts; one word used per device
+static __device__ __align__(256) uint32_t bad_lists[1];  // the count of bad query blocks (each GPU has its own copy)
 
 __global__ void clear_count_kernel(uint32_t* __restrict__ c) {
   if (threadIdx.x == 0) c[0] = 0u;

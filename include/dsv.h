@@ -43,7 +43,10 @@
  *   timing record below, and the device arrays of dsv_pack_kv_noalloc and of the
  *   debug check below); calls are thread-safe and may run concurrently on
  *   different streams with different buffers.  All calls are
- *   deterministic (bitwise repeatable for the same inputs and problem).
+ *   deterministic (bitwise repeatable for the same inputs and problem), and a
+ *   head's results do not depend on the other heads of the call or on the
+ *   device's compute-unit count: predicting heads one call at a time or all at
+ *   once gives the same bits.
  * Block lists.  Every call that takes block_idx uses, per query block, its first
  *   block_counts[qb] entries (clamped to [0, k]) or all k when block_counts is
  *   NULL.  Results are defined only when those entries are distinct indices in
