@@ -473,6 +473,31 @@ def test_predictor_scores_do_not_depend_on_the_heads_sharing_a_call(r, bq):
     log(f"[parity] predictor r={r} bq={bq}: {heads} heads bit-equal alone, in groups of 8 and all at once")
 
 
+def test_attention_results_do_not_depend_on_the_heads_sharing_a_call():
+    # Forward and backward on all heads at once, and head group by head group (4 calls of 3
+    # heads), on the same lists: every output bit-equal.  Each head's fp16 scales come from that
+    # head's own maxima, and no workgroup mixes heads.
+    cfg = get_config("C2")
+    inp = make_inputs(cfg, with_grad=True)
+    t = {k: to_dev(v) for k, v in inp.items()}
+    kw = dict(q_block=cfg.q_block, kv_block=cfg.kv_block)
+    idx_d = to_dev(seeded_idx(11, (cfg.batch, cfg.heads), cfg.nqb, cfg.nkb, cfg.topk))
+    o, lse, o_lo = dsv.sparse_attn_fwd(t["q"], t["k"], t["v"], idx_d, residual=True, **kw)
+    full = (o, lse) + tuple(dsv.sparse_attn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, idx_d, o_lo=o_lo, **kw))
+    parts = [torch.empty_like(x) for x in full]
+    for h0 in range(0, cfg.heads, 3):
+        sl = slice(h0, h0 + 3)
+        q, k, v, do = (t[n][:, sl] for n in ("q", "k", "v", "do"))
+        og, lg, olg = dsv.sparse_attn_fwd(q, k, v, idx_d[:, sl], residual=True, **kw)
+        grads = dsv.sparse_attn_bwd(q, k, v, og, do, lg, idx_d[:, sl], o_lo=olg, **kw)
+        for dst, src in zip(parts, (og, lg) + tuple(grads)):
+            dst[:, sl] = src
+    torch.cuda.synchronize()
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), full, parts):
+        assert torch.equal(a, b), name
+    log(f"[parity] C2 attention: {cfg.heads} heads bit-equal at once and in groups of 3")
+
+
 def test_autograd_function_gradients_match_the_oracle():
     # DSVAttention.apply: predict -> select -> training forward, and the sparse backward through
     # autograd.  The q, k, v gradients must match the oracle's backward on the GPU-chosen indices
