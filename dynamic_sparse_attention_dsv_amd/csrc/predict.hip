@@ -409,7 +409,9 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t* __rest
 // One workgroup per (head, 64 consecutive query blocks).  Its waves take the chunks of 32 KV blocks
 // round-robin (wave w: chunks w, w + 4, ...) and sweep them for all 64 representative rows: one
 // bf16 32x32x16 MFMA product of Q~ and K_lr gives log2-unit logits, and each (row, block) key is
-// m + log2 sum_j 2^(l_j - m) with m the block's maximum, exact at any logit range (no fallback).
+// the block's mass sum_j 2^l_j (one exp and one add per logit).  An item holding a row whose
+// largest block mass leaves [2^-100, fp32 max] is swept again with keys m + log2 sum_j 2^(l_j - m),
+// m the block's maximum, exact at any logit range.
 // A chunk's keys are transposed through LDS so that each row's 32 keys leave as one 128-byte line
 // into the workgroup's row-major scratch (64 x nkb floats); after one barrier each wave picks the
 // top k of 16 rows with topk_row and writes their ascending index lists.
@@ -422,7 +424,9 @@ __global__ __launch_bounds__(256) void rep_select_bf16_kernel(const uint16_t* __
   constexpr int NC = R / 16;
   constexpr int CH = 32;           // KV blocks per chunk
   constexpr int TP = 65;           // padded row pitch of the transpose tile (conflict-free writes)
+  constexpr float kTinyMass = 7.888609052210118e-31f;  // 2^-100
   __shared__ float tile_s[4][CH * TP];
+  __shared__ float rmax_s[4][64];  // per wave: the largest fast-sweep block mass of each row
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c32 = lane & 31;
   const int nqb = n / bq;
@@ -452,58 +456,96 @@ __global__ __launch_bounds__(256) void rep_select_bf16_kernel(const uint16_t* __
 #pragma unroll
         for (int c = 0; c < NC; ++c) ka[t][c] = ld16(kp + (size_t)(t * 32 + c32) * R + c * 16 + g * 8);
     };
-    for (int ch = wave; ch < nchunks; ch += 4) {
-      const int cb0 = ch * CH, cnt = min(CH, nkb - cb0);  // cnt is a multiple of 4 (nkb is)
-      u32x4 ka[2][NC];
-      f32x16 acc[2][2];
-      load_k(cb0, ka);
-      for (int j = 0; j < cnt; ++j) {
+    // One sweep over the item's KV blocks.  Fast (exact = false): the key of (row, block) is the
+    // block's mass sum_j 2^l_j, one exp and one add per logit, as in the score sweep; returned is
+    // the largest mass of this lane's row (row = lane) over the wave's chunks.  Exact: the key is
+    // the in-block log-sum-exp m + log2 sum_j 2^(l_j - m), m the block's maximum, valid at any
+    // logit range.  Either key orders a row's blocks as their predicted softmax mass does.
+    auto sweep = [&](bool exact) {
+      float rmax = 0.f;
+      for (int ch = wave; ch < nchunks; ch += 4) {
+        const int cb0 = ch * CH, cnt = min(CH, nkb - cb0);  // cnt is a multiple of 4 (nkb is)
+        u32x4 ka[2][NC];
+        f32x16 acc[2][2];
+        load_k(cb0, ka);
+        for (int j = 0; j < cnt; ++j) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            acc[h][t] = f32x16{};
+            for (int t = 0; t < 2; ++t) {
+              acc[h][t] = f32x16{};
 #pragma unroll
-            for (int c = 0; c < NC; ++c) acc[h][t] = mfma32(as_bf16x8(ka[t][c]), qh[h][c], acc[h][t]);
+              for (int c = 0; c < NC; ++c) acc[h][t] = mfma32(as_bf16x8(ka[t][c]), qh[h][c], acc[h][t]);
+            }
+          if (j + 1 < cnt) load_k(cb0 + j + 1, ka);
+          // lane holds 32 of the block's 64 logits for its row of half h; lane ^ 32 the other 32
+          float key2[2];
+          if (!exact) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              float sp[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sp[e] = fast_exp2(acc[h][e >> 1][e & 1]);
+#pragma unroll
+              for (int v = 2; v < 16; v += 2)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sp[e] += fast_exp2(acc[h][e >> 1][v + (e & 1)]);
+              key2[h] = sum_xor32((sp[0] + sp[1]) + (sp[2] + sp[3]));
+            }
+          } else {
+            // a tree maximum and four partial sums: short dependency chains, since few waves share
+            // a SIMD
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              float mx[16];
+#pragma unroll
+              for (int v = 0; v < 16; ++v) mx[v] = fmaxf(acc[h][0][v], acc[h][1][v]);
+#pragma unroll
+              for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+                for (int v = 0; v < w; ++v) mx[v] = fmaxf(mx[v], mx[v + w]);
+              const float m = max_xor32(mx[0]);
+              float sp[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sp[e] = fast_exp2(acc[h][e >> 1][e & 1] - m);
+#pragma unroll
+              for (int v = 2; v < 16; v += 2)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sp[e] += fast_exp2(acc[h][e >> 1][v + (e & 1)] - m);
+              key2[h] = m + fast_log2(sum_xor32((sp[0] + sp[1]) + (sp[2] + sp[3])));
+            }
           }
-        if (j + 1 < cnt) load_k(cb0 + j + 1, ka);
-        // lane holds 32 of the block's 64 logits for its row of half h; lane ^ 32 the other 32
-        // (a tree maximum and four partial sums: short dependency chains, since few waves share a SIMD)
-        float key2[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float mx[16];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx[v] = fmaxf(acc[h][0][v], acc[h][1][v]);
-#pragma unroll
-          for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-            for (int v = 0; v < w; ++v) mx[v] = fmaxf(mx[v], mx[v + w]);
-          const float m = max_xor32(mx[0]);
-          float sp[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sp[e] = fast_exp2(acc[h][e >> 1][e & 1] - m);
-#pragma unroll
-          for (int v = 2; v < 16; v += 2)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sp[e] += fast_exp2(acc[h][e >> 1][v + (e & 1)] - m);
-          key2[h] = m + fast_log2(sum_xor32((sp[0] + sp[1]) + (sp[2] + sp[3])));
+          // lanes g = 0 hold half 0's rows, lanes g = 1 half 1's: tile[block][row], row = lane
+          const float mine = g ? key2[1] : key2[0];
+          rmax = fmaxf(rmax, mine);
+          tile[j * TP + g * 32 + c32] = mine;
         }
-        // lanes g = 0 hold half 0's rows, lanes g = 1 half 1's: tile[block][row]
-        tile[j * TP + g * 32 + c32] = g ? key2[1] : key2[0];
-      }
-      // the chunk's keys, row by row: lane L writes 4 keys (one 16-byte segment) of row
-      // (u * 64 + L) / 8, so that eight lanes fill one row's 128-byte line
+        // the chunk's keys, row by row: lane L writes 4 keys (one 16-byte segment) of row
+        // (u * 64 + L) / 8, so that eight lanes fill one row's 128-byte line
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, row = f >> 3, seg = (f & 7) * 4;
-        if (seg < cnt) {
-          const f32x4 v4 = {tile[(seg + 0) * TP + row], tile[(seg + 1) * TP + row], tile[(seg + 2) * TP + row],
-                            tile[(seg + 3) * TP + row]};
-          *reinterpret_cast<f32x4*>(keys + (size_t)row * nkb + cb0 + seg) = v4;
+        for (int u = 0; u < 8; ++u) {
+          const int f = u * 64 + lane, row = f >> 3, seg = (f & 7) * 4;
+          if (seg < cnt) {
+            const f32x4 v4 = {tile[(seg + 0) * TP + row], tile[(seg + 1) * TP + row], tile[(seg + 2) * TP + row],
+                              tile[(seg + 3) * TP + row]};
+            *reinterpret_cast<f32x4*>(keys + (size_t)row * nkb + cb0 + seg) = v4;
+          }
         }
       }
+      return rmax;
+    };
+    // The fast keys hold (up to rounding) for rows whose largest block mass is finite and at least
+    // 2^-100 (the top blocks then keep full precision); an item with any other valid row is swept
+    // again in the log domain.
+    rmax_s[wave][lane] = sweep(false);
+    __syncthreads();
+    bool off_range = false;
+    if (threadIdx.x < 64 && qb0 + (int)threadIdx.x < nqb) {
+      const float m = fmaxf(fmaxf(rmax_s[0][threadIdx.x], rmax_s[1][threadIdx.x]),
+                            fmaxf(rmax_s[2][threadIdx.x], rmax_s[3][threadIdx.x]));
+      off_range = !(m >= kTinyMass && m < INFINITY);
     }
+    if (__syncthreads_or(off_range)) sweep(true);
     __threadfence_block();
     __syncthreads();
     // selection: wave w takes the item's rows [16w, 16w + 16)

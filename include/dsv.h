@@ -180,9 +180,10 @@ dsv_status dsv_predict_representative(const dsv_problem* p, const void* q, const
  * of the single query row i = qb * Bq + rep_row (the scores of dsv_predict_representative), ties
  * toward the smaller block index, written ascending -- equal to dsv_predict_representative
  * followed by dsv_select_topk up to floating-point rounding of near-equal masses.  The bf16
- * instance ranks each row's blocks by their in-block log-sum-exp of logits (the same order as
- * the mass, since the row's normaliser is common) inside the predictor's sweep and writes no
- * score matrix; the fp32 instance computes the scores into the workspace and selects from them.
+ * instance ranks each row's blocks by their unnormalised mass (the same order as the score,
+ * since the row's normaliser is common; by their in-block log-sum-exp of logits where the masses
+ * leave fp32's range) inside the predictor's sweep and writes no score matrix; the fp32 instance
+ * computes the scores into the workspace and selects from them.
  *
  *   q, k, wq, wk  as dsv_predict;  rep_row  0 <= rep_row < Bq;  k = problem.topk
  *   workspace     >= dsv_predict_workspace_size(p) bytes; on return it holds Q~ and K_lr as for

@@ -76,7 +76,7 @@ def _fused_vs_oracle(cfg, inp, rep, heads_checked):
 @pytest.mark.parametrize("name,rep", [("C2", 0), ("C2", 63), ("C3", 17), ("C5", 64), ("C1", 5)])
 def test_fused_representative_selection(name, rep):
     # dsv_predict_select_representative: the top-k of each query block's representative row straight
-    # from the projections (the bf16 kernel ranks blocks by their in-block log-sum-exp inside the
+    # from the projections (the bf16 kernel ranks blocks by their unnormalised mass inside the
     # sweep), against the oracle's representative scores and top-k: bit-exact wherever the oracle's
     # k-th/(k+1)-th gap exceeds 1e-5, valid near-tie choices elsewhere.  C5: 2 heads at full size
     # (2048 KV blocks, 1024 query blocks).
@@ -102,8 +102,9 @@ def test_fused_representative_edge_sizes(n, heads, topk):
 
 @pytest.mark.parametrize("case", ["overflow", "tiny"])
 def test_fused_representative_extreme_logits(case):
-    # Logits far beyond fp32's exponent range (2^+-138 per key): the in-block log-sum-exp keys stay
-    # exact, so block 5 -- the only block with the largest logits -- leads every selection.
+    # Logits far beyond fp32's exponent range (2^+-138 per key): the block masses overflow or
+    # vanish, the item is swept again with in-block log-sum-exp keys, which stay exact, so block 5
+    # -- the only block with the largest logits -- leads every selection.
     n, d, r, bq, bk, k = 1024, 64, 16, 64, 64, 3
     rng = np.random.default_rng(23)
     q = rng.standard_normal((1, 1, n, d)).astype(np.float32) * 0.1
