@@ -127,3 +127,34 @@ def test_fused_representative_extreme_logits(case):
     ig = idx.cpu().numpy()[0, 0]
     check_indices(ig, ref, k, gap_rule=REP_GAP)
     assert np.all(np.any(ig == 5, axis=1))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_representative_paths_over_random_shapes(seed):
+    # Seeded shapes over the bf16 instances: d, Bq and r drawn from the compiled ones, N a multiple
+    # of 256 up to 4096, one to three heads, a random representative row and k.  Both paths --
+    # scores then top-k, and the fused selection -- against the oracle on the GPU's projections.
+    rng = np.random.default_rng(5100 + seed)
+    d, bq, r = int(rng.choice([64, 128])), int(rng.choice([64, 128])), int(rng.choice([16, 32]))
+    n, heads = 256 * int(rng.integers(1, 17)), int(rng.integers(1, 4))
+    nkb = n // 64
+    k, rep = int(rng.integers(1, nkb + 1)), int(rng.integers(0, bq))
+    log(f"[parity] representative sweep seed={seed}: H={heads} N={n} d={d} r={r} Bq={bq} k={k} rep={rep}")
+    from workloads.generator import bf16_bits_from_f32
+    bf = lambda shape, s=1.0: bf16_bits_from_f32((rng.standard_normal(shape) * s).astype(np.float32))  # noqa: E731
+    t = {"q": to_dev(bf((1, heads, n, d))), "k": to_dev(bf((1, heads, n, d))),
+         "wq": to_dev(bf((heads, d, r), 1 / np.sqrt(d))), "wk": to_dev(bf((heads, d, r), 1 / np.sqrt(d)))}
+    kw = dict(q_block=bq, kv_block=64)
+    sc, qlr, klr = dsv.predict(t["q"], t["k"], t["wq"], t["wk"], rep_row=rep, return_projections=True, **kw)
+    iu = dsv.select_topk(sc, k, **kw)
+    ig = dsv.predict_select_representative(t["q"], t["k"], t["wq"], t["wk"], k, rep, **kw)
+    torch.cuda.synchronize()
+    sg, ql, kl = to_f64(sc), to_f64(qlr), to_f64(klr)
+    iu, ig = iu.cpu().numpy(), ig.cpu().numpy()
+    for h in range(heads):
+        ref = O.representative_scores_head(ql[0, h], kl[0, h], bq, 64, O.LN2, rep=rep)
+        np.testing.assert_allclose(sg[0, h], ref, rtol=2e-4, atol=1e-6, err_msg=f"head {h}")
+        check_indices(iu[0, h], ref, k, gap_rule=REP_GAP)
+        check_indices(ig[0, h], ref, k, gap_rule=REP_GAP)
+        exact = O.topk_gap(ref, k) > REP_GAP
+        assert np.array_equal(ig[0, h][exact], iu[0, h][exact])
