@@ -16,6 +16,9 @@ Entry points (same names as the C ABI):
   block_recall(lse_selected, lse_all, q_block) -> recall [B, H, N/Bq] (true mass captured)
   head_density(block_counts, topk, ...) -> (density [B, H], dense flag [B, H])
   pack_kv(k, v, idx, qb_begin, qb_end, ...) -> (k_packed, v_packed, packed_blocks, packed_counts, packed_idx)
+  pack_kv_noalloc(...)                 the same without a workspace (the library's own device array)
+  peak_probe(kind)                     the rate this device sustains for one bounding operation
+  DSVAttention.apply(q, k, v, wq, wk, q_block, kv_block, topk) -> (o, block_idx), differentiable in q, k, v
 """
 from __future__ import annotations
 
